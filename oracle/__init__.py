@@ -1,0 +1,23 @@
+"""fp64 CPU oracle for exact attention, forward and backward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, calls or links
+anything in this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+library (no kernels, headers, helpers, tables or pre/post-processing).
+
+Every function follows the page titled "把 FlashAttention 搬上昇腾：Triton-Ascend
+CV Pipeline 优化实战" ("Porting FlashAttention to Ascend: CV-pipeline
+optimisation with Triton-Ascend", BiumBiu, 2026-08-30), cited below as
+[FA-Ascend] with the section it comes from.
+
+Pinning: every function here is pinned by tests marked ``not gpu`` to facts
+other than itself (finite differences, closed forms, invariants, a library
+routine, brute force on tiny inputs); see ``tests/test_oracle.py``.  No function
+is "parity unpinned".
+"""
+from .attention import (  # noqa: F401
+    attention_forward,
+    attention_forward_full,
+    attention_backward,
+    loss_sum_o_do,
+)

@@ -1,0 +1,110 @@
+"""Plain fp64 attention, written out from its definition.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  [FA-Ascend] is the page
+"把 FlashAttention 搬上昇腾：Triton-Ascend CV Pipeline 优化实战" (BiumBiu).
+
+The method on that page (tiles, online softmax, recomputation) reaches exactly
+this result up to rounding order, so the oracle is the definition itself: it
+materialises the full N x N score and probability matrices, which is precisely
+what the tiled method avoids.  The only library primitives used are matrix
+products, exp, log and reductions.
+
+Readings of points the page leaves open (each is listed in the design doc):
+
+* layout: q, k, v, do are (..., N, D) arrays; leading axes are independent heads;
+* self-attention with one key/value head per query head, N_q = N_k = N;
+* causal means key j is visible to query i iff j <= i (the lower triangle
+  including the diagonal, [FA-Ascend] §八);
+* the saved row statistic is the natural-log log-sum-exp lse = m + ln(l)
+  (the page's backward "recomputes" the softmax, [FA-Ascend] §二, which needs a
+  saved row statistic; the page never names it);
+* Delta uses the oracle's own fp64 O.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = ["attention_forward", "attention_forward_full", "attention_backward", "loss_sum_o_do"]
+
+
+def _as_f64(x):
+    x = np.asarray(x)
+    if x.dtype != np.float64:
+        x = x.astype(np.float64)
+    return x
+
+
+def _scores(q, k, scale, causal):
+    """S = Q @ K^T * scale, with the causal upper triangle set to -inf.
+
+    [FA-Ascend] §一 (first forward equation) and §八 (causal: the upper
+    triangle takes no part).
+    """
+    s = np.matmul(q, np.swapaxes(k, -1, -2)) * scale
+    if causal:
+        n_q, n_k = s.shape[-2], s.shape[-1]
+        i = np.arange(n_q)[:, None]
+        j = np.arange(n_k)[None, :]
+        s = np.where(j <= i, s, -np.inf)
+    return s
+
+
+def attention_forward_full(q, k, v, scale, causal=False):
+    """Forward pass returning every intermediate: dict(S, P, O, lse, m, l).
+
+    [FA-Ascend] §一: S = Q @ K^T * scale; P = softmax(S) row-wise; O = P @ V.
+    The softmax is the textbook one: subtract the row max m, exponentiate,
+    divide by the row sum l.  lse = m + ln(l).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    scale = float(scale)
+    S = _scores(q, k, scale, causal)
+    m = np.max(S, axis=-1, keepdims=True)
+    E = np.exp(S - m)
+    l = np.sum(E, axis=-1, keepdims=True)
+    P = E / l
+    O = np.matmul(P, v)
+    lse = (m + np.log(l))[..., 0]
+    return {"S": S, "P": P, "O": O, "lse": lse, "m": m[..., 0], "l": l[..., 0]}
+
+
+def attention_forward(q, k, v, scale, causal=False):
+    """(O, lse) of the forward pass; see ``attention_forward_full``."""
+    r = attention_forward_full(q, k, v, scale, causal)
+    return r["O"], r["lse"]
+
+
+def attention_backward(q, k, v, do, scale, causal=False):
+    """Backward pass, taken literally from [FA-Ascend] §二:
+
+        Delta = rowsum(O * dO)
+        P     = softmax(Q @ K^T * scale)          (recomputed)
+        dP    = dO @ V^T
+        dS    = scale * P * (dP - Delta)
+        dQ    = dS @ K
+        dK    = dS^T @ Q
+        dV    = P^T @ dO
+
+    The page writes the three gradients as accumulations ("+=") over tiles;
+    over the whole matrix they are the plain products above.  Returns a dict
+    with dq, dk, dv and the intermediates O, lse, P, dP, dS, Delta.
+    """
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    scale = float(scale)
+    fwd = attention_forward_full(q, k, v, scale, causal)
+    O, P = fwd["O"], fwd["P"]
+    Delta = np.sum(O * do, axis=-1)
+    dP = np.matmul(do, np.swapaxes(v, -1, -2))
+    dS = scale * P * (dP - Delta[..., None])
+    dq = np.matmul(dS, k)
+    dk = np.matmul(np.swapaxes(dS, -1, -2), q)
+    dv = np.matmul(np.swapaxes(P, -1, -2), do)
+    return {"dq": dq, "dk": dk, "dv": dv, "O": O, "lse": fwd["lse"], "P": P,
+            "dP": dP, "dS": dS, "Delta": Delta}
+
+
+def loss_sum_o_do(q, k, v, do, scale, causal=False):
+    """L = sum(O * dO) with dO held fixed: its gradient w.r.t. (Q, K, V) is the
+    backward pass above, which the finite-difference pin uses."""
+    O, _ = attention_forward(q, k, v, scale, causal)
+    return float(np.sum(O * _as_f64(do)))

@@ -1,0 +1,104 @@
+"""Seeded synthetic workloads shared by the tests, the bench and the oracle checks.
+
+This module holds shapes, seeds and random draws only.  It contains none of the
+attention arithmetic, so both the HIP path and the fp64 oracle can take their
+inputs from here without sharing any of the method.
+
+Recipe (one generator per workload, PCG64 through ``numpy.random.default_rng``):
+
+* seed = the workload's index (1..5);
+* draw, in this order, ``q, k, v, do`` as ``standard_normal(shape, float32)``
+  with shape (Z, H, N, D);
+* for the long-sequence workload only, multiply q and k by 2 in float32 (exact),
+  which sharpens the softmax and exercises the running-max rescaling;
+* cast to the workload's dtype with round-to-nearest-even.
+
+``scale`` is a float32 value; the oracle receives the same float32 value upcast
+to float64, so both sides see the identical number.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+__all__ = ["Workload", "WORKLOADS", "by_name", "draw_f32", "make_inputs", "f32_scale"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    Z: int
+    H: int
+    N: int
+    D: int
+    dtype: str          # "f16" or "bf16"
+    causal: bool
+    qk_gain: float = 1.0  # multiplier applied to q and k in float32
+
+    @property
+    def scale(self) -> float:
+        return f32_scale(self.D)
+
+    @property
+    def shape(self):
+        return (self.Z, self.H, self.N, self.D)
+
+    @property
+    def heads(self) -> int:
+        return self.Z * self.H
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+def f32_scale(D: int) -> float:
+    """1/sqrt(D) rounded to float32, returned as a Python float holding that value."""
+    return float(np.float32(1.0 / math.sqrt(D)))
+
+
+# The five workloads: a tiny parity case, three Z=128 x H=8 x N=1024 cases at
+# head dims 64/128/256, and a long-sequence causal case with a peaked softmax.
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 1, 1, 128, 64, "f16", False),
+    "d64": Workload("d64", 2, 128, 8, 1024, 64, "f16", False),
+    "d128_causal": Workload("d128_causal", 3, 128, 8, 1024, 128, "f16", True),
+    "d256_bf16": Workload("d256_bf16", 4, 128, 8, 1024, 256, "bf16", False),
+    "long_causal_bf16": Workload("long_causal_bf16", 5, 16, 16, 8192, 128, "bf16", True, 2.0),
+}
+
+
+def by_name(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def draw_f32(w: Workload, heads: slice | None = None):
+    """Return float32 (q, k, v, do) of shape (Z, H, N, D) drawn from the workload's seed.
+
+    ``heads`` is ignored for the draw itself (the stream must stay identical); it
+    exists so that callers can document that they slice afterwards.
+    """
+    rng = np.random.default_rng(w.seed)
+    out = []
+    for name in ("q", "k", "v", "do"):
+        x = rng.standard_normal(size=w.shape, dtype=np.float32)
+        if name in ("q", "k") and w.qk_gain != 1.0:
+            x *= np.float32(w.qk_gain)
+        out.append(x)
+    return tuple(out)
+
+
+def make_inputs(w: Workload):
+    """Return torch CPU tensors (q, k, v, do) in the workload's dtype (RNE cast)."""
+    import torch
+
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    return tuple(torch.from_numpy(x).to(tdt) for x in draw_f32(w))
+
+
+def random_inputs(shape, dtype: str, seed: int, qk_gain: float = 1.0):
+    """Seeded (q, k, v, do) torch CPU tensors of an arbitrary shape, same recipe."""
+    w = Workload("adhoc", seed, *shape, dtype, False, qk_gain)
+    return make_inputs(w)
