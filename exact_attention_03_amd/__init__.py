@@ -1,0 +1,178 @@
+"""Exact attention (FlashAttention) forward and backward on AMD MI355X.
+
+Thin binding over the C ABI of ``libfa.so`` (see ``include/fa.h``): it checks
+tensors, allocates outputs with torch and passes raw device pointers plus the
+current HIP stream.  Every step of the computation runs in the library's HIP
+kernels; nothing here computes attention.
+
+The operations follow the page "把 FlashAttention 搬上昇腾：Triton-Ascend CV
+Pipeline 优化实战" (BiumBiu): §一 for the forward, §二 for the backward.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32, FAError, check, last_error, lib,  # noqa: F401
+                   status_name)
+
+__all__ = ["forward", "backward", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "workspace_bytes",
+           "device_info", "dkdv_schedule", "fwd_tile_pairs", "FAError", "lib"]
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    codes = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16, torch.float32: FA_DTYPE_F32}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _check_qkv(*ts, names):
+    ref = ts[0]
+    for t, n in zip(ts, names):
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be a GPU tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{n} must be (Z, H, N, D), got shape {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+        if t.shape != ref.shape:
+            raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {tuple(ref.shape)}")
+        if t.device != ref.device:
+            raise ValueError(f"{n} is on {t.device}, expected {ref.device}")
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _scale(scale, D):
+    return float(1.0 / math.sqrt(D)) if scale is None else float(scale)
+
+
+def forward(q, k, v, causal=False, scale=None, out_dtype=None):
+    """O, lse = attention(q, k, v).  q, k, v: (Z, H, N, D) fp16/bf16 GPU tensors.
+
+    out_dtype: dtype of O, either q.dtype (default) or torch.float32.
+    Returns O (Z, H, N, D) and lse (Z, H, N) float32 (natural log).
+    """
+    torch = _torch()
+    _check_qkv(q, k, v, names=("q", "k", "v"))
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    Z, H, N, D = q.shape
+    odt = q.dtype if out_dtype is None else out_dtype
+    with torch.cuda.device(q.device):
+        o = torch.empty((Z, H, N, D), dtype=odt, device=q.device)
+        lse = torch.empty((Z, H, N), dtype=torch.float32, device=q.device)
+        st = lib().fa_fwd(Z, H, N, D, _dtype_code(q), _dtype_code(o), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                          _ptr(lse), _scale(scale, D), int(bool(causal)), _stream(q))
+    check(st, "fa_fwd")
+    return o, lse
+
+
+def workspace_bytes(Z, H, N, D):
+    return int(lib().fa_bwd_workspace_bytes(Z, H, N, D))
+
+
+def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None):
+    """dq, dk, dv of attention given dO; o and lse from ``forward``.
+
+    workspace: optional float32 GPU tensor of >= Z*H*N elements (Delta); one
+    is allocated when omitted.
+    """
+    torch = _torch()
+    _check_qkv(q, k, v, do, names=("q", "k", "v", "do"))
+    _check_qkv(q, o, names=("q", "o"))
+    Z, H, N, D = q.shape
+    if lse.shape != (Z, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (Z, H, N) tensor")
+    with torch.cuda.device(q.device):
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+        if workspace is None:
+            workspace = torch.empty((max(1, Z * H * N),), dtype=torch.float32, device=q.device)
+        st = lib().fa_bwd(Z, H, N, D, _dtype_code(q), _dtype_code(o), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                          _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _scale(scale, D),
+                          int(bool(causal)), _ptr(workspace), workspace.numel() * 4, _stream(q))
+    check(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def bwd_preprocess(o, do):
+    """Delta = rowsum(O * dO) in float32, shape (Z, H, N)."""
+    torch = _torch()
+    _check_qkv(do, o, names=("do", "o"))
+    Z, H, N, D = do.shape
+    with torch.cuda.device(do.device):
+        delta = torch.empty((Z, H, N), dtype=torch.float32, device=do.device)
+        st = lib().fa_bwd_preprocess(Z, H, N, D, _dtype_code(do), _dtype_code(o), _ptr(o), _ptr(do),
+                                     _ptr(delta), _stream(do))
+    check(st, "fa_bwd_preprocess")
+    return delta
+
+
+def bwd_dkdv(q, k, v, do, lse, delta, causal=False, scale=None, num_programs=0):
+    """dK, dV from the persistent key-tile pass (num_programs 0 = device default)."""
+    torch = _torch()
+    _check_qkv(q, k, v, do, names=("q", "k", "v", "do"))
+    Z, H, N, D = q.shape
+    with torch.cuda.device(q.device):
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+        st = lib().fa_bwd_dkdv(Z, H, N, D, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
+                               _ptr(delta), _ptr(dk), _ptr(dv), _scale(scale, D), int(bool(causal)),
+                               int(num_programs), _stream(q))
+    check(st, "fa_bwd_dkdv")
+    return dk, dv
+
+
+def bwd_dq(q, k, v, do, lse, delta, causal=False, scale=None):
+    """dQ from the query-tile pass."""
+    torch = _torch()
+    _check_qkv(q, k, v, do, names=("q", "k", "v", "do"))
+    Z, H, N, D = q.shape
+    with torch.cuda.device(q.device):
+        dq = torch.empty_like(q)
+        st = lib().fa_bwd_dq(Z, H, N, D, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
+                             _ptr(delta), _ptr(dq), _scale(scale, D), int(bool(causal)), _stream(q))
+    check(st, "fa_bwd_dq")
+    return dq
+
+
+def device_info(D=128, dtype_code=FA_DTYPE_F16):
+    """(compute units, default dK/dV persistent grid) of the current device."""
+    cus, progs = ctypes.c_int(0), ctypes.c_int(0)
+    check(lib().fa_device_info(D, dtype_code, ctypes.byref(cus), ctypes.byref(progs)), "fa_device_info")
+    return cus.value, progs.value
+
+
+def dkdv_schedule(Z, H, N, D, causal, num_programs):
+    """Host-only replay of the dK/dV schedule: (units per program, query tiles per program, unit count)."""
+    units = (ctypes.c_int64 * num_programs)()
+    work = (ctypes.c_int64 * num_programs)()
+    n = ctypes.c_int64(0)
+    check(lib().fa_dkdv_schedule(Z, H, N, D, int(bool(causal)), num_programs, units, work, ctypes.byref(n)),
+          "fa_dkdv_schedule")
+    return list(units), list(work), n.value
+
+
+def fwd_tile_pairs(N, D, causal):
+    """Host-only: (query tile, key tile) pairs the forward visits, and the total."""
+    vis, tot = ctypes.c_int64(0), ctypes.c_int64(0)
+    check(lib().fa_fwd_tile_pairs(N, D, int(bool(causal)), ctypes.byref(vis), ctypes.byref(tot)),
+          "fa_fwd_tile_pairs")
+    return vis.value, tot.value

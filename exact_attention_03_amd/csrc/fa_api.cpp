@@ -1,0 +1,340 @@
+// fa_api.cpp - the C ABI declared in include/fa.h.
+//
+// Argument validation (pure host code, no HIP call), dispatch to the kernel
+// launchers, per-device launch facts cached once, and error reporting.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "fa_kernels.h"
+#include "fa_schedule.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* s = std::getenv("FA_DEBUG_SYNC");
+    return s != nullptr && s[0] != '\0' && s[0] != '0';
+  }();
+  return on;
+}
+
+constexpr int64_t kMaxI32 = 2147483647;
+
+struct Shape {
+  int64_t Z, H, N, D;
+  int64_t heads() const { return Z * H; }
+  bool empty() const { return Z == 0 || H == 0 || N == 0; }
+};
+
+int check_shape(const Shape& s) {
+  if (s.Z < 0 || s.H < 0 || s.N < 0 || s.D < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "negative size (Z=%lld H=%lld N=%lld D=%lld)", (long long)s.Z,
+                (long long)s.H, (long long)s.N, (long long)s.D);
+  if (s.D != 64 && s.D != 128 && s.D != 256)
+    return fail(FA_ERR_UNSUPPORTED, "head dim D=%lld not supported (64, 128 or 256)", (long long)s.D);
+  if (s.empty()) return FA_OK;
+  // Kernels index one head with 32-bit byte offsets (fp32 O included, plus a
+  // tile of padding rows) and launch up to heads * tiles workgroups.
+  if (s.Z > kMaxI32 || s.H > kMaxI32 || s.N > kMaxI32 || s.heads() > kMaxI32 ||
+      (s.N + 256) * s.D * 4 > kMaxI32)
+    return fail(FA_ERR_UNSUPPORTED, "problem too large (Z=%lld H=%lld N=%lld D=%lld)", (long long)s.Z,
+                (long long)s.H, (long long)s.N, (long long)s.D);
+  if (s.heads() * ((s.N + 63) / 64) > kMaxI32)
+    return fail(FA_ERR_UNSUPPORTED, "grid too large (Z*H=%lld N=%lld)", (long long)s.heads(), (long long)s.N);
+  return FA_OK;
+}
+
+int check_dtypes(int dtype, int o_dtype, bool need_o) {
+  if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
+    return fail(FA_ERR_INVALID_ARGUMENT, "dtype %d must be FA_DTYPE_F16 or FA_DTYPE_BF16", dtype);
+  if (need_o && o_dtype != dtype && o_dtype != FA_DTYPE_F32)
+    return fail(FA_ERR_INVALID_ARGUMENT, "o_dtype %d must equal dtype (%d) or be FA_DTYPE_F32", o_dtype, dtype);
+  return FA_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(FA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+  return FA_OK;
+}
+
+int check_scale(float scale, int causal) {
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(FA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0 (got %g)", (double)scale);
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", causal);
+  return FA_OK;
+}
+
+#define FA_TRY(x)            \
+  do {                       \
+    const int st_ = (x);     \
+    if (st_ != FA_OK) return st_; \
+  } while (0)
+
+// Per-device launch facts, filled once per device.
+struct DeviceFacts {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  int cus = 0;
+  int dkdv_per_cu[3][2] = {};  // [D index][dtype]
+};
+constexpr int kMaxDevices = 64;
+DeviceFacts g_facts[kMaxDevices];
+
+int d_index(int64_t D) { return D == 64 ? 0 : (D == 128 ? 1 : 2); }
+
+int device_facts(DeviceFacts** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FA_ERR_HIP, "device index %d out of range", dev);
+  DeviceFacts& f = g_facts[dev];
+  std::call_once(f.once, [&f, dev] {
+    int cus = 0;
+    f.err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (f.err != hipSuccess) return;
+    f.cus = cus;
+    const int Ds[3] = {64, 128, 256};
+    for (int di = 0; di < 3; ++di)
+      for (int dt = 0; dt < 2; ++dt) {
+        f.err = fa::dkdv_blocks_per_cu(Ds[di], dt, &f.dkdv_per_cu[di][dt]);
+        if (f.err != hipSuccess) return;
+      }
+  });
+  if (f.err != hipSuccess) return hip_fail(f.err, "querying device attributes");
+  *out = &f;
+  return FA_OK;
+}
+
+int finish(hipError_t launch_err, hipStream_t stream, const char* what) {
+  if (launch_err != hipSuccess) return hip_fail(launch_err, what);
+  if (debug_sync()) {
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, what);
+  }
+  return FA_OK;
+}
+
+int validate_bwd_common(const Shape& s, int dtype, const void* q, const void* k, const void* v,
+                        const void* dout, const float* lse, const float* delta, float scale, int causal) {
+  FA_TRY(check_shape(s));
+  FA_TRY(check_dtypes(dtype, dtype, false));
+  FA_TRY(check_scale(scale, causal));
+  if (s.empty()) return FA_OK;
+  FA_TRY(check_ptr(q, "q"));
+  FA_TRY(check_ptr(k, "k"));
+  FA_TRY(check_ptr(v, "v"));
+  FA_TRY(check_ptr(dout, "dout"));
+  FA_TRY(check_ptr(lse, "lse"));
+  FA_TRY(check_ptr(delta, "delta"));
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return 100; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARGUMENT: return "FA_ERR_INVALID_ARGUMENT";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    default: return "FA_UNKNOWN_STATUS";
+  }
+}
+
+const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+size_t fa_bwd_workspace_bytes(int64_t Z, int64_t H, int64_t N, int64_t D) {
+  (void)D;
+  if (Z <= 0 || H <= 0 || N <= 0) return 0;
+  return (size_t)(Z * H * N) * sizeof(float);
+}
+
+int fa_fwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, const void* q, const void* k,
+           const void* v, void* o, float* lse, float scale, int causal, hipStream_t stream) {
+  g_last_error.clear();
+  const Shape s{Z, H, N, D};
+  FA_TRY(check_shape(s));
+  FA_TRY(check_dtypes(dtype, o_dtype, true));
+  FA_TRY(check_scale(scale, causal));
+  if (s.empty()) return FA_OK;
+  FA_TRY(check_ptr(q, "q"));
+  FA_TRY(check_ptr(k, "k"));
+  FA_TRY(check_ptr(v, "v"));
+  FA_TRY(check_ptr(o, "o"));
+  FA_TRY(check_ptr(lse, "lse"));
+  fa::FwdArgs a{Z, H, N, D, dtype, o_dtype, q, k, v, o, lse, scale, causal, stream};
+  return finish(fa::launch_fwd(a), stream, "fa_fwd launch");
+}
+
+int fa_bwd_preprocess(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, const void* o,
+                      const void* dout, float* delta, hipStream_t stream) {
+  g_last_error.clear();
+  const Shape s{Z, H, N, D};
+  FA_TRY(check_shape(s));
+  FA_TRY(check_dtypes(dtype, o_dtype, true));
+  if (s.empty()) return FA_OK;
+  FA_TRY(check_ptr(o, "o"));
+  FA_TRY(check_ptr(dout, "dout"));
+  FA_TRY(check_ptr(delta, "delta"));
+  fa::BwdArgs a{};
+  a.Z = Z; a.H = H; a.N = N; a.D = D; a.dtype = dtype; a.o_dtype = o_dtype;
+  a.o = o; a.dout = dout; a.delta = delta; a.stream = stream;
+  return finish(fa::launch_bwd_pre(a), stream, "fa_bwd_preprocess launch");
+}
+
+int fa_bwd_dkdv(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, const void* q, const void* k,
+                const void* v, const void* dout, const float* lse, const float* delta, void* dk, void* dv,
+                float scale, int causal, int num_programs, hipStream_t stream) {
+  g_last_error.clear();
+  const Shape s{Z, H, N, D};
+  FA_TRY(validate_bwd_common(s, dtype, q, k, v, dout, lse, delta, scale, causal));
+  if (num_programs < 0) return fail(FA_ERR_INVALID_ARGUMENT, "num_programs must be >= 0 (got %d)", num_programs);
+  if (s.empty()) return FA_OK;
+  FA_TRY(check_ptr(dk, "dk"));
+  FA_TRY(check_ptr(dv, "dv"));
+  if (num_programs == 0) {
+    DeviceFacts* f = nullptr;
+    FA_TRY(device_facts(&f));
+    num_programs = f->cus * f->dkdv_per_cu[d_index(D)][dtype];
+  }
+  fa::BwdArgs a{};
+  a.Z = Z; a.H = H; a.N = N; a.D = D; a.dtype = dtype;
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.lse = lse; a.delta = const_cast<float*>(delta);
+  a.dk = dk; a.dv = dv; a.scale = scale; a.causal = causal; a.num_programs = num_programs; a.stream = stream;
+  return finish(fa::launch_bwd_dkdv(a), stream, "fa_bwd_dkdv launch");
+}
+
+int fa_bwd_dq(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, const void* q, const void* k,
+              const void* v, const void* dout, const float* lse, const float* delta, void* dq, float scale,
+              int causal, hipStream_t stream) {
+  g_last_error.clear();
+  const Shape s{Z, H, N, D};
+  FA_TRY(validate_bwd_common(s, dtype, q, k, v, dout, lse, delta, scale, causal));
+  if (s.empty()) return FA_OK;
+  FA_TRY(check_ptr(dq, "dq"));
+  fa::BwdArgs a{};
+  a.Z = Z; a.H = H; a.N = N; a.D = D; a.dtype = dtype;
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.lse = lse; a.delta = const_cast<float*>(delta);
+  a.dq = dq; a.scale = scale; a.causal = causal; a.stream = stream;
+  return finish(fa::launch_bwd_dq(a), stream, "fa_bwd_dq launch");
+}
+
+int fa_bwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, const void* q, const void* k,
+           const void* v, const void* o, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  const Shape s{Z, H, N, D};
+  FA_TRY(check_shape(s));
+  FA_TRY(check_dtypes(dtype, o_dtype, true));
+  FA_TRY(check_scale(scale, causal));
+  if (s.empty()) return FA_OK;
+  FA_TRY(check_ptr(q, "q"));
+  FA_TRY(check_ptr(k, "k"));
+  FA_TRY(check_ptr(v, "v"));
+  FA_TRY(check_ptr(o, "o"));
+  FA_TRY(check_ptr(dout, "dout"));
+  FA_TRY(check_ptr(lse, "lse"));
+  FA_TRY(check_ptr(dq, "dq"));
+  FA_TRY(check_ptr(dk, "dk"));
+  FA_TRY(check_ptr(dv, "dv"));
+  FA_TRY(check_ptr(workspace, "workspace"));
+  const size_t need = fa_bwd_workspace_bytes(Z, H, N, D);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                workspace_bytes, need);
+  float* delta = static_cast<float*>(workspace);
+  FA_TRY(fa_bwd_preprocess(Z, H, N, D, dtype, o_dtype, o, dout, delta, stream));
+  FA_TRY(fa_bwd_dkdv(Z, H, N, D, dtype, q, k, v, dout, lse, delta, dk, dv, scale, causal, 0, stream));
+  FA_TRY(fa_bwd_dq(Z, H, N, D, dtype, q, k, v, dout, lse, delta, dq, scale, causal, stream));
+  return FA_OK;
+}
+
+int fa_device_info(int64_t D, int dtype, int* compute_units, int* dkdv_programs) {
+  g_last_error.clear();
+  FA_TRY(check_shape(Shape{1, 1, 1, D}));
+  FA_TRY(check_dtypes(dtype, dtype, false));
+  DeviceFacts* f = nullptr;
+  FA_TRY(device_facts(&f));
+  if (compute_units) *compute_units = f->cus;
+  if (dkdv_programs) *dkdv_programs = f->cus * f->dkdv_per_cu[d_index(D)][dtype];
+  return FA_OK;
+}
+
+int fa_dkdv_schedule(int64_t Z, int64_t H, int64_t N, int64_t D, int causal, int num_programs,
+                     int64_t* units_per_program, int64_t* qtiles_per_program, int64_t* n_units) {
+  g_last_error.clear();
+  const Shape s{Z, H, N, D};
+  FA_TRY(check_shape(s));
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  if (num_programs <= 0) return fail(FA_ERR_INVALID_ARGUMENT, "num_programs must be > 0");
+  const int64_t bk = fa::kDkdvKeys, bq = fa::dkdv_queries((int)D);
+  const int64_t ZH = s.heads();
+  const int64_t n_kt = (N + bk - 1) / bk, n_qt = (N + bq - 1) / bq;
+  const int64_t U = ZH * n_kt;
+  if (n_units) *n_units = U;
+  for (int64_t p = 0; p < num_programs; ++p) {
+    int64_t units = 0, work = 0;
+    for (int64_t r = 0;; ++r) {
+      const int64_t u = fa::sched_unit(r, p, num_programs);
+      if (u >= U) break;
+      int64_t kt, head;
+      fa::sched_decode(u, ZH, &kt, &head);
+      ++units;
+      work += n_qt - fa::sched_first_qtile(kt, bk, bq, causal);
+    }
+    if (units_per_program) units_per_program[p] = units;
+    if (qtiles_per_program) qtiles_per_program[p] = work;
+  }
+  return FA_OK;
+}
+
+int fa_fwd_tile_pairs(int64_t N, int64_t D, int causal, int64_t* visited, int64_t* total) {
+  g_last_error.clear();
+  FA_TRY(check_shape(Shape{1, 1, N, D}));
+  if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
+  const int64_t bm = fa::kFwdQueries, bn = fa::fwd_keys((int)D);
+  const int64_t nq = (N + bm - 1) / bm, nk = (N + bn - 1) / bn;
+  int64_t vis = 0;
+  for (int64_t i = 0; i < nq; ++i) {
+    const int64_t end = causal ? std::min(N, (i + 1) * bm) : N;
+    vis += (end + bn - 1) / bn;
+  }
+  if (visited) *visited = vis;
+  if (total) *total = nq * nk;
+  return FA_OK;
+}
+
+}  // extern "C"

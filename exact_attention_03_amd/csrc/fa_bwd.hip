@@ -1,0 +1,515 @@
+// fa_bwd.hip - exact attention backward for gfx950: Delta pass, dK/dV pass
+// and dQ pass.
+//
+// [FA-Ascend] = the page "把 FlashAttention 搬上昇腾：Triton-Ascend CV Pipeline
+// 优化实战" (BiumBiu).  §二 gives the backward:
+//     Delta = rowsum(O * dO)
+//     P     = recompute_softmax(Q K^T * scale)
+//     dP    = dO V^T
+//     dS    = scale * P * (dP - Delta)
+//     dQ   += dS K ;  dK += dS^T Q ;  dV += P^T dO
+// and the rules the page keeps: P is recomputed, never stored; each gradient
+// tile has a single writer; scratch does not grow with N^2.  §二 also notes
+// that dQ can be finished by the query tile itself while a dK/dV tile gathers
+// contributions from every query tile; hence two passes with different owners:
+// a persistent pass that owns key tiles (dK, dV) and a pass that owns query
+// tiles (dQ).  The scale of dS is applied once to the finished dK and dQ
+// accumulators, which is the same product.
+//
+// P is recomputed from the saved lse: P = exp2(S * scale * log2e - lse * log2e).
+#include "fa_device.h"
+#include "fa_kernels.h"
+#include "fa_schedule.h"
+
+namespace fa {
+
+// ============================================================ Delta pass
+// delta[row] = sum_d O[row, d] * dO[row, d] in fp32.  HBM-bound: each thread
+// reads one 16-byte chunk of dO (8 elements) and the matching O elements; the
+// D/8 threads of a row combine their partial sums with lane shuffles.
+template <int D, typename T, bool O32>
+__global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const void* __restrict__ o,
+                                                         const uint16_t* __restrict__ dout,
+                                                         float* __restrict__ delta, int64_t rows) {
+  constexpr int TPR = D / 8;             // threads per row
+  constexpr int RPB = 256 / TPR;         // rows per block
+  const int tid = threadIdx.x;
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;
+  const int c = tid % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 g = *reinterpret_cast<const u32x4*>(dout + row * D + 8 * c);
+    float ov[8];
+    if constexpr (O32) {
+      const f32x4* op = reinterpret_cast<const f32x4*>((const float*)o + row * D + 8 * c);
+      const f32x4 a = op[0], b = op[1];
+      ov[0] = a.x; ov[1] = a.y; ov[2] = a.z; ov[3] = a.w;
+      ov[4] = b.x; ov[5] = b.y; ov[6] = b.z; ov[7] = b.w;
+    } else {
+      const u32x4 ow = *reinterpret_cast<const u32x4*>((const uint16_t*)o + row * D + 8 * c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ov[2 * i] = lo16_to_f32<T>(ow[i]);
+        ov[2 * i + 1] = hi16_to_f32<T>(ow[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = __builtin_fmaf(ov[2 * i], lo16_to_f32<T>(g[i]), acc);
+      acc = __builtin_fmaf(ov[2 * i + 1], hi16_to_f32<T>(g[i]), acc);
+    }
+  }
+#pragma unroll
+  for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s, 64);
+  if (row < rows && c == 0) delta[row] = acc;
+}
+
+// ============================================================ dK / dV pass
+// A persistent workgroup of 4 waves owns a unit = (head, 128-key tile); wave w
+// owns keys kt0 + 32w .. +31 and keeps their K and V rows in registers, with
+// its dK and dV tiles as fp32 accumulators.  Query tiles of 64 rows (Q, dO and
+// their lse/Delta values) stream through a two-stage LDS ring.  Per 32-query
+// block the wave computes
+//     S  = Q K^T        (A = Q rows from LDS, B = K from registers)
+//     dP = dO V^T       (A = dO rows from LDS, B = V from registers)
+//     P  = exp2(S c - lse2),  dS = P (dP - Delta)
+//     dV^T += dO^T P    (A = dO^T by transposing LDS reads, B = P)
+//     dK^T += Q^T dS    (A = Q^T by transposing LDS reads, B = dS)
+// with queries as the MFMA rows and keys as the lanes, so that P and dS come
+// out of the first two products already in the operand layout of the last two.
+template <int D>
+struct DkdvTile {
+  static constexpr int NW = 4;
+  static constexpr int BK = kDkdvKeys;          // keys per unit (32 per wave)
+  static constexpr int BQ = dkdv_queries(D);     // queries per staged tile
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE_BYTES = BQ * D * 2;
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES + 2 * BQ * 4;  // Q, dO, lse2, Delta
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int CPT = BQ * CPR / (NW * 64);  // chunks per thread per tile
+  static_assert(CPT * NW * 64 == BQ * CPR, "tile must split evenly over the threads");
+  static_assert(BK == NW * 32, "one 32-key block per wave");
+};
+
+template <int D, typename T, bool CAUSAL>
+__global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int N, int ZH, int n_ktiles, int n_qtiles,
+    float c2, float scale, int P) {
+  using C = DkdvTile<D>;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+  const int64_t n_units = (int64_t)ZH * n_ktiles;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+
+  for (int64_t round = 0;; ++round) {
+    const int64_t u = sched_unit(round, blockIdx.x, P);
+    if (u >= n_units) break;  // uniform across the workgroup
+    int64_t kt64, head64;
+    sched_decode(u, ZH, &kt64, &head64);
+    const int kt = (int)kt64, head = (int)head64;
+    const int k0 = kt * C::BK;
+    const int kw0 = k0 + 32 * w;  // first key of this wave
+    const size_t hoff = (size_t)head * (size_t)N * D;
+    const auto rq = make_rsrc(q + hoff, head_bytes);
+    const auto rk = make_rsrc(k + hoff, head_bytes);
+    const auto rv = make_rsrc(v + hoff, head_bytes);
+    const auto rdo = make_rsrc(dout + hoff, head_bytes);
+    const auto rl = make_rsrc(lse + (size_t)head * N, (uint32_t)N * 4);
+    const auto rd = make_rsrc(delta + (size_t)head * N, (uint32_t)N * 4);
+
+    // K and V rows of this wave's keys, B-operand layout (lane = key, k = d).
+    u32x4 kf[C::KSTEPS], vf[C::KSTEPS];
+#pragma unroll
+    for (int t = 0; t < C::KSTEPS; ++t) {
+      const uint32_t off = (uint32_t)(((kw0 + l32) * D + 16 * t + 8 * h) * 2);
+      kf[t] = gload16(rk, off);
+      vf[t] = gload16(rv, off);
+    }
+    f32x16 dka[C::DB], dva[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      dka[db] = f32x16{};
+      dva[db] = f32x16{};
+    }
+
+    const int i0 = (int)sched_first_qtile(kt, C::BK, C::BQ, CAUSAL);
+    u32x4 qst[C::CPT], dost[C::CPT];
+    float lst = 0.f, dst = 0.f;
+    auto gload_tile = [&](int i) {
+      const int qq0 = i * C::BQ;
+#pragma unroll
+      for (int x = 0; x < C::CPT; ++x) {
+        const int uu = tid + 256 * x;
+        const int row = uu / C::CPR, c = uu % C::CPR;
+        const uint32_t off = (uint32_t)(((qq0 + row) * D + 8 * c) * 2);
+        qst[x] = gload16(rq, off);
+        dost[x] = gload16(rdo, off);
+      }
+      if (tid < C::BQ) {
+        lst = gload_f32(rl, (uint32_t)(qq0 + tid) * 4) * kLog2e;
+        dst = gload_f32(rd, (uint32_t)(qq0 + tid) * 4);
+      }
+    };
+    auto lds_store_tile = [&](int stage) {
+      char* base = smem + stage * C::STAGE_BYTES;
+#pragma unroll
+      for (int x = 0; x < C::CPT; ++x) {
+        const int uu = tid + 256 * x;
+        const int row = uu / C::CPR, c = uu % C::CPR;
+        const int off = tile_off<C::CPR>(row, 8 * c);
+        lds_write16(base, off, qst[x]);
+        lds_write16(base + C::TILE_BYTES, off, dost[x]);
+      }
+      if (tid < C::BQ) {
+        float* st = reinterpret_cast<float*>(base + 2 * C::TILE_BYTES);
+        st[tid] = lst;
+        st[C::BQ + tid] = dst;
+      }
+    };
+
+    gload_tile(i0);
+    lds_store_tile(0);
+    __syncthreads();
+    for (int i = i0; i < n_qtiles; ++i) {
+      const int stage = (i - i0) & 1;
+      const bool more = i + 1 < n_qtiles;
+      if (more) gload_tile(i + 1);
+      const char* qt = smem + stage * C::STAGE_BYTES;
+      const char* dot = qt + C::TILE_BYTES;
+      const float* lst_l = reinterpret_cast<const float*>(qt + 2 * C::TILE_BYTES);
+      const float* dst_l = lst_l + C::BQ;
+      const int qq0 = i * C::BQ;
+#pragma unroll
+      for (int qb = 0; qb < C::BQ / 32; ++qb) {
+        const int qb0 = qq0 + 32 * qb;  // first query of the block
+        // Causal: a block whose last query precedes the wave's first key is empty.
+        if (CAUSAL && qb0 + 31 < kw0) continue;
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int t = 0; t < C::KSTEPS; ++t) {
+          const int off = tile_off<C::CPR>(32 * qb + sigma32(l32), 16 * t + 8 * h);
+          s = mfma32<T>(lds_read16(qt, off), kf[t], s);
+          dp = mfma32<T>(lds_read16(dot, off), vf[t], dp);
+        }
+        // Register jj holds query qb0 + 16(jj/8) + 8h + jj%8 for key kw0 + l32.
+        f32x4 lv[4], dv4[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int qi = 32 * qb + 16 * (x >> 1) + 8 * h + 4 * (x & 1);
+          lv[x] = *reinterpret_cast<const f32x4*>(lst_l + qi);
+          dv4[x] = *reinterpret_cast<const f32x4*>(dst_l + qi);
+        }
+        const int key = kw0 + l32;
+        const bool need_mask = (CAUSAL && qb0 < kw0 + 31) || (qb0 + 32 > N);
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const float l2 = lv[jj >> 2][jj & 3];
+          const float dl = dv4[jj >> 2][jj & 3];
+          float p = fast_exp2(__builtin_fmaf(s[jj], c2, -l2));
+          if (need_mask) {
+            const int query = qb0 + 16 * (jj >> 3) + 8 * h + (jj & 7);
+            if ((CAUSAL && key > query) || query >= N) p = 0.f;
+          }
+          s[jj] = p;
+          dp[jj] = p * (dp[jj] - dl);
+        }
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const u32x4 pf = pack8<T>(s, 8 * t2);
+          const u32x4 dsf = pack8<T>(dp, 8 * t2);
+          const int krow0 = 32 * qb + 16 * t2 + 8 * h;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            dva[db] = mfma32<T>(lds_read_tr_operand<C::CPR>(dot, krow0, 32 * db, lane), pf, dva[db]);
+            dka[db] = mfma32<T>(lds_read_tr_operand<C::CPR>(qt, krow0, 32 * db, lane), dsf, dka[db]);
+          }
+        }
+      }
+      if (more) lds_store_tile(stage ^ 1);
+      __syncthreads();
+    }
+
+    // Single write of this wave's dK and dV rows.  Register jj of block db
+    // holds d = 32db + 16(jj/8) + 8h + jj%8 of key kw0 + l32.
+    const auto rdk = make_rsrc(dk + hoff, head_bytes);
+    const auto rdv = make_rsrc(dv + hoff, head_bytes);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const f32x16 ks = dka[db] * scale;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const uint32_t off = (uint32_t)(((kw0 + l32) * D + 32 * db + 16 * half + 8 * h) * 2);
+        gstore16(rdk, off, pack8<T>(ks, 8 * half));
+        gstore16(rdv, off, pack8<T>(dva[db], 8 * half));
+      }
+    }
+  }
+}
+
+// ============================================================ dQ pass
+// One workgroup of 4 waves owns 128 queries of one head (32 per wave, kept in
+// registers together with their dO rows, lse and Delta) and streams K/V tiles
+// through a two-stage LDS ring.  Per key tile the wave computes, transposed so
+// that each lane owns one query,
+//     S^T  = K Q^T,  dP^T = V dO^T          (A = K/V rows from LDS)
+//     P^T  = exp2(S^T c - lse2),  dS^T = P^T (dP^T - Delta)
+//     dQ^T += K^T dS^T                      (A = K^T by transposing LDS reads)
+template <int D>
+struct DqTile {
+  static constexpr int NW = 4;
+  static constexpr int BM = NW * 32;
+  static constexpr int KB = D == 256 ? 1 : 2;
+  static constexpr int BN = 32 * KB;
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE_BYTES = BN * D * 2;
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int CPT = BN * CPR / (NW * 64);
+  static_assert(CPT * NW * 64 == BN * CPR, "tile must split evenly over the threads");
+};
+
+template <int D, typename T, bool CAUSAL>
+__global__ __launch_bounds__(256) void fa_bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    uint16_t* __restrict__ dq, int N, int ZH, int n_qtiles, float c2, float scale) {
+  using C = DqTile<D>;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+  const int bid = blockIdx.x;
+  const int tq = bid / ZH;
+  const int head = bid - tq * ZH;
+  const int qt = CAUSAL ? (n_qtiles - 1 - tq) : tq;
+  const int q0 = qt * C::BM;
+  const int wq0 = q0 + 32 * w;
+  const int query = wq0 + l32;
+  const size_t hoff = (size_t)head * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto rq = make_rsrc(q + hoff, head_bytes);
+  const auto rk = make_rsrc(k + hoff, head_bytes);
+  const auto rv = make_rsrc(v + hoff, head_bytes);
+  const auto rdo = make_rsrc(dout + hoff, head_bytes);
+
+  u32x4 qf[C::KSTEPS], dof[C::KSTEPS];
+#pragma unroll
+  for (int t = 0; t < C::KSTEPS; ++t) {
+    const uint32_t off = (uint32_t)((query * D + 16 * t + 8 * h) * 2);
+    qf[t] = gload16(rq, off);
+    dof[t] = gload16(rdo, off);
+  }
+  const float l2 = gload_f32(make_rsrc(lse + (size_t)head * N, (uint32_t)N * 4), (uint32_t)query * 4) * kLog2e;
+  const float dl = gload_f32(make_rsrc(delta + (size_t)head * N, (uint32_t)N * 4), (uint32_t)query * 4);
+
+  const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
+  const int nt = (kv_end + C::BN - 1) / C::BN;
+
+  u32x4 kst[C::CPT], vst[C::CPT];
+  auto gload_tile = [&](int j) {
+    const int kv0 = j * C::BN;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int u = tid + 256 * i;
+      const int row = u / C::CPR, c = u % C::CPR;
+      const uint32_t off = (uint32_t)(((kv0 + row) * D + 8 * c) * 2);
+      kst[i] = gload16(rk, off);
+      vst[i] = gload16(rv, off);
+    }
+  };
+  auto lds_store_tile = [&](int stage) {
+    char* kt = smem + stage * C::STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int u = tid + 256 * i;
+      const int row = u / C::CPR, c = u % C::CPR;
+      const int off = tile_off<C::CPR>(row, 8 * c);
+      lds_write16(kt, off, kst[i]);
+      lds_write16(kt + C::TILE_BYTES, off, vst[i]);
+    }
+  };
+
+  f32x16 dqa[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) dqa[db] = f32x16{};
+
+  gload_tile(0);
+  lds_store_tile(0);
+  __syncthreads();
+  for (int j = 0; j < nt; ++j) {
+    const int stage = j & 1;
+    const bool more = j + 1 < nt;
+    if (more) gload_tile(j + 1);
+    const int kv0 = j * C::BN;
+    const bool active = !CAUSAL || kv0 <= wq0 + 31;
+    if (active) {
+      const char* kt = smem + stage * C::STAGE_BYTES;
+      const char* vt = kt + C::TILE_BYTES;
+      f32x16 s[C::KB], dp[C::KB];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
+      }
+#pragma unroll
+      for (int t = 0; t < C::KSTEPS; ++t)
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+          const int off = tile_off<C::CPR>(32 * kb + sigma32(l32), 16 * t + 8 * h);
+          s[kb] = mfma32<T>(lds_read16(kt, off), qf[t], s[kb]);
+          dp[kb] = mfma32<T>(lds_read16(vt, off), dof[t], dp[kb]);
+        }
+      const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > wq0) || (kv0 + C::BN > N);
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          float p = fast_exp2(__builtin_fmaf(s[kb][jj], c2, -l2));
+          if (need_mask) {
+            const int key = kv0 + 32 * kb + 16 * (jj >> 3) + 8 * h + (jj & 7);
+            if ((CAUSAL && key > query) || key >= N) p = 0.f;
+          }
+          dp[kb][jj] = p * (dp[kb][jj] - dl);
+        }
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const u32x4 dsf = pack8<T>(dp[kb], 8 * t2);
+          const int krow0 = 32 * kb + 16 * t2 + 8 * h;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db)
+            dqa[db] = mfma32<T>(lds_read_tr_operand<C::CPR>(kt, krow0, 32 * db, lane), dsf, dqa[db]);
+        }
+    }
+    if (more) lds_store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  const auto rdq = make_rsrc(dq + hoff, head_bytes);
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) {
+    const f32x16 y = dqa[db] * scale;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+      gstore16(rdq, (uint32_t)((query * D + 32 * db + 16 * half + 8 * h) * 2), pack8<T>(y, 8 * half));
+  }
+}
+
+// ============================================================ launchers
+template <int D, typename T, bool O32>
+static hipError_t launch_pre_t(const BwdArgs& a) {
+  constexpr int RPB = 256 / (D / 8);
+  const int64_t rows = a.Z * a.H * a.N;
+  const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
+  hipLaunchKernelGGL((fa_bwd_pre_kernel<D, T, O32>), grid, dim3(256), 0, a.stream, a.o,
+                     (const uint16_t*)a.dout, a.delta, rows);
+  return hipGetLastError();
+}
+template <int D, typename T>
+static hipError_t launch_pre_d(const BwdArgs& a) {
+  return a.o_dtype == F32::code ? launch_pre_t<D, T, true>(a) : launch_pre_t<D, T, false>(a);
+}
+template <typename T>
+static hipError_t launch_pre_dt(const BwdArgs& a) {
+  switch (a.D) {
+    case 64: return launch_pre_d<64, T>(a);
+    case 128: return launch_pre_d<128, T>(a);
+    default: return launch_pre_d<256, T>(a);
+  }
+}
+hipError_t launch_bwd_pre(const BwdArgs& a) {
+  return a.dtype == BF16::code ? launch_pre_dt<BF16>(a) : launch_pre_dt<F16>(a);
+}
+
+template <int D, typename T, bool CAUSAL>
+static hipError_t launch_dkdv_t(const BwdArgs& a) {
+  using C = DkdvTile<D>;
+  const int ZH = (int)(a.Z * a.H);
+  const int n_kt = (int)((a.N + C::BK - 1) / C::BK);
+  const int n_qt = (int)((a.N + C::BQ - 1) / C::BQ);
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, T, CAUSAL>), dim3((unsigned)a.num_programs), dim3(256), 0,
+                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, (int)a.N,
+                     ZH, n_kt, n_qt, a.scale * kLog2e, a.scale, a.num_programs);
+  return hipGetLastError();
+}
+template <int D, typename T>
+static hipError_t launch_dkdv_d(const BwdArgs& a) {
+  return a.causal ? launch_dkdv_t<D, T, true>(a) : launch_dkdv_t<D, T, false>(a);
+}
+template <typename T>
+static hipError_t launch_dkdv_dt(const BwdArgs& a) {
+  switch (a.D) {
+    case 64: return launch_dkdv_d<64, T>(a);
+    case 128: return launch_dkdv_d<128, T>(a);
+    default: return launch_dkdv_d<256, T>(a);
+  }
+}
+hipError_t launch_bwd_dkdv(const BwdArgs& a) {
+  return a.dtype == BF16::code ? launch_dkdv_dt<BF16>(a) : launch_dkdv_dt<F16>(a);
+}
+
+template <int D, typename T>
+static hipError_t occ_dkdv(int* out) {
+  int n = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fa_bwd_dkdv_kernel<D, T, true>, 256, 0);
+  if (e != hipSuccess) return e;
+  int n2 = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n2, fa_bwd_dkdv_kernel<D, T, false>, 256, 0);
+  if (e != hipSuccess) return e;
+  *out = n < n2 ? n : n2;
+  if (*out < 1) *out = 1;
+  return hipSuccess;
+}
+hipError_t dkdv_blocks_per_cu(int D, int dtype, int* out) {
+  const bool bf = dtype == BF16::code;
+  switch (D) {
+    case 64: return bf ? occ_dkdv<64, BF16>(out) : occ_dkdv<64, F16>(out);
+    case 128: return bf ? occ_dkdv<128, BF16>(out) : occ_dkdv<128, F16>(out);
+    default: return bf ? occ_dkdv<256, BF16>(out) : occ_dkdv<256, F16>(out);
+  }
+}
+
+template <int D, typename T, bool CAUSAL>
+static hipError_t launch_dq_t(const BwdArgs& a) {
+  using C = DqTile<D>;
+  const int ZH = (int)(a.Z * a.H);
+  const int n_qt = (int)((a.N + C::BM - 1) / C::BM);
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, T, CAUSAL>), dim3((unsigned)(n_qt * ZH)), dim3(256), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, (int)a.N, ZH, n_qt,
+                     a.scale * kLog2e, a.scale);
+  return hipGetLastError();
+}
+template <int D, typename T>
+static hipError_t launch_dq_d(const BwdArgs& a) {
+  return a.causal ? launch_dq_t<D, T, true>(a) : launch_dq_t<D, T, false>(a);
+}
+template <typename T>
+static hipError_t launch_dq_dt(const BwdArgs& a) {
+  switch (a.D) {
+    case 64: return launch_dq_d<64, T>(a);
+    case 128: return launch_dq_d<128, T>(a);
+    default: return launch_dq_d<256, T>(a);
+  }
+}
+hipError_t launch_bwd_dq(const BwdArgs& a) {
+  return a.dtype == BF16::code ? launch_dq_dt<BF16>(a) : launch_dq_dt<F16>(a);
+}
+
+}  // namespace fa

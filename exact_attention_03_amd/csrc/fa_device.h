@@ -1,0 +1,217 @@
+// fa_device.h - gfx950 device primitives shared by the attention kernels.
+//
+// MFMA tiles, bounds-checked buffer loads/stores, swizzled LDS tile layout,
+// transposed LDS reads and the cross-half lane exchange.  The lane layouts
+// below are those of the CDNA4 matrix instructions:
+//
+//   v_mfma_f32_32x32x16_{f16,bf16}:  A is 32(m) x 16(k), B is 16(k) x 32(n).
+//   Lane l (h = l/32) supplies A[m = l%32][k in K_h] and B[k in K_h][n = l%32],
+//   eight k values per lane, the same set K_h for A and B.  Because the k index
+//   is summed, which eight k's a half supplies is a free choice as long as A and
+//   B agree; this library always feeds k = 8h + i (i = 0..7) of each 16-wide k
+//   step.  The 32x32 fp32 result lands in 16 registers per lane:
+//   register j of lane l holds C[m = 8(j/4) + 4h + j%4][n = l%32].
+//
+// Row permutation sigma.  When the A rows of a 32-row block are loaded in the
+// order sigma(m) (bits 2 and 3 of m swapped), register j of the result holds
+// row 16(j/8) + 8h + (j%8): the first eight registers are eight consecutive
+// rows and so are the last eight.  That makes a score tile directly usable as
+// the k-operand of the next MFMA (eight consecutive keys per lane half) and
+// lets results be stored as 16-byte vectors.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+#define FA_DEV __device__ __forceinline__
+#define FA_HD __host__ __device__ __forceinline__
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Element-type tags.
+struct F16 {
+  static constexpr int code = 0;
+};
+struct BF16 {
+  static constexpr int code = 1;
+};
+struct F32 {
+  static constexpr int code = 2;
+};
+
+template <typename T>
+inline constexpr bool kIsBF16 = false;
+template <>
+inline constexpr bool kIsBF16<BF16> = true;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ----------------------------------------------------------------- MFMA
+template <typename T>
+FA_DEV f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
+
+template <>
+FA_DEV f32x16 mfma32<F16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+template <>
+FA_DEV f32x16 mfma32<BF16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Two fp32 values to one dword of two 16-bit values, round to nearest even.
+template <typename T>
+FA_DEV uint32_t pack2(float a, float b);
+template <>
+FA_DEV uint32_t pack2<F16>(float a, float b) {
+  f16x2 v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+template <>
+FA_DEV uint32_t pack2<BF16>(float a, float b) {
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Registers [j0, j0+8) of an accumulator tile packed into an MFMA operand.
+template <typename T>
+FA_DEV u32x4 pack8(const f32x16& s, int j0) {
+  u32x4 r;
+  r.x = pack2<T>(s[j0 + 0], s[j0 + 1]);
+  r.y = pack2<T>(s[j0 + 2], s[j0 + 3]);
+  r.z = pack2<T>(s[j0 + 4], s[j0 + 5]);
+  r.w = pack2<T>(s[j0 + 6], s[j0 + 7]);
+  return r;
+}
+
+// 16-bit storage value back to fp32 (for the preprocess pass).
+template <typename T>
+FA_DEV float lo16_to_f32(uint32_t w);
+template <typename T>
+FA_DEV float hi16_to_f32(uint32_t w);
+template <>
+FA_DEV float lo16_to_f32<F16>(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+template <>
+FA_DEV float hi16_to_f32<F16>(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+template <>
+FA_DEV float lo16_to_f32<BF16>(uint32_t w) {
+  return __uint_as_float(w << 16);
+}
+template <>
+FA_DEV float hi16_to_f32<BF16>(uint32_t w) {
+  return __uint_as_float(w & 0xffff0000u);
+}
+
+// ----------------------------------------------------------------- lanes
+FA_HD int sigma32(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+// Swap bits 0 and 1: sigma restricted to the 4-element chunk index of a 16-lane group.
+FA_HD int swap01(int c) { return (c & ~3) | ((c & 1) << 1) | ((c & 2) >> 1); }
+
+// {x of this lane, x of lane l^32}: max / sum across the two lane halves.
+FA_DEV float half_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+FA_DEV float half_swap_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+FA_DEV bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+FA_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ----------------------------------------------------------------- global memory
+// Buffer resources give hardware bounds checks: loads past num_records return
+// zero and stores past it are dropped.  Every kernel builds its resources over
+// one head (N*D elements), so a ragged last tile needs no extra guards.
+constexpr int kBufferFlags = 0x00020000;  // gfx9 raw-buffer data format word
+
+FA_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferFlags);
+}
+FA_DEV u32x4 gload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+FA_DEV void gstore16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+FA_DEV float gload_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+FA_DEV void gstore_f32(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
+// ----------------------------------------------------------------- LDS tiles
+// A tile is `rows` x D 16-bit elements stored row-major in LDS, in 16-byte
+// chunks (CPR = D/8 chunks per row).  Chunk c of row r sits at chunk position
+// c ^ swz(r).  The XOR keeps both access patterns free of bank conflicts:
+//  * plain 16-byte reads of one chunk column by 16 lanes whose rows are a
+//    permutation of 16 consecutive rows, and
+//  * transposed reads, where 16 lanes read 4 consecutive rows x 32 bytes.
+template <int CPR>
+FA_HD int swz(int row) {
+  if constexpr (CPR >= 16) {
+    return ((row & 7) << 1) | ((row >> 3) & 1);
+  } else {
+    static_assert(CPR == 8, "rows of 64 or more elements");
+    return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+  }
+}
+
+// Byte offset of element (row, col) in a swizzled tile; col % 4 == 0 keeps an
+// 8-byte access inside one chunk.
+template <int CPR>
+FA_HD int tile_off(int row, int col) {
+  const int c = col >> 3;
+  return row * (CPR * 16) + ((c ^ swz<CPR>(row)) << 4) + ((col & 7) << 1);
+}
+
+FA_DEV u32x4 lds_read16(const char* base, int off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+FA_DEV void lds_write16(char* base, int off, u32x4 v) { *reinterpret_cast<u32x4*>(base + off) = v; }
+
+// Transposed 8-byte LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives element (i%4) of the 8-byte chunks fetched by lanes
+// 4r + i/4 of its group, r = 0..3, as its elements r = 0..3.
+FA_DEV u32x2 lds_read_tr(const char* base, int off) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// MFMA operand of 8 consecutive k (rows krow0..krow0+7 of the tile) for column
+// n of a 32-column block starting at col0, where the 32 operand lanes take the
+// tile columns in sigma order:  lane l receives T[krow0 + i][col0 + sigma(l%32)]
+// for i = 0..7.  `krow0` may differ between the two lane halves.
+template <int CPR>
+FA_DEV u32x4 lds_read_tr_operand(const char* tile, int krow0, int col0, int lane) {
+  const int g = lane >> 4;     // group of 16 lanes
+  const int r = (lane & 15) >> 2;
+  const int c = lane & 3;
+  const int col = col0 + 16 * (g & 1) + 4 * swap01(c);
+  const u32x2 lo = lds_read_tr(tile, tile_off<CPR>(krow0 + r, col));
+  const u32x2 hi = lds_read_tr(tile, tile_off<CPR>(krow0 + 4 + r, col));
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
+}  // namespace fa

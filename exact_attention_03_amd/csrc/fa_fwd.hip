@@ -1,0 +1,290 @@
+// fa_fwd.hip - exact attention forward for gfx950.
+//
+// [FA-Ascend] = the page "把 FlashAttention 搬上昇腾：Triton-Ascend CV Pipeline
+// 优化实战" (BiumBiu).  §一 of that page defines the pass: S = Q K^T * scale,
+// P = softmax(S), O = P V, computed tile by tile with a Q tile kept on chip,
+// K/V tiles streamed past it, an online softmax (running row max m, running
+// denominator l, unnormalised accumulator), exp2 with log2(e) folded into the
+// scale, fp32 statistics and accumulator, P cast to the 16-bit input type
+// before the matrix unit, a shortened causal loop with masking only where a
+// tile straddles the diagonal, and a single write of O.
+//
+// Work decomposition on gfx950
+//   * one workgroup = 4 waves = one Q tile of BM = 128 queries of one head;
+//     wave w owns 32 consecutive queries and keeps them in registers as the
+//     B operand of the score MFMA for the whole kernel;
+//   * K/V tiles of BN keys are staged through a two-stage LDS ring (global ->
+//     registers -> LDS, the next tile's global loads issued before the current
+//     tile's math);
+//   * scores are computed transposed, S^T = K Q^T, so that each lane owns one
+//     query (a column of the MFMA result) and its softmax statistics are
+//     per-lane values; a row max needs one exchange between lane halves;
+//   * the output is accumulated transposed as well, O^T = V^T P^T, with V^T
+//     read straight from the row-major V tile by transposing LDS reads.
+// Refinement over the page's rescale-on-every-new-max (fp16 only): the running
+// max used for the exponentials is only raised when some row's max grew by more
+// than 8 in exp2 units, so most tiles skip rescaling the accumulator; the
+// normalisation by the matching denominator makes the result the same.  P then
+// reaches up to 2^8, harmless in fp16 (relative rounding 2^-11).  With bf16 P
+// the row's largest weight must stay exactly 1: a weight of up to 2^8 rounded
+// to bf16 is off by up to 2^-9 of itself, which in a near-one-hot row moves O by
+// 2^-9 |v|.  So bf16 rescales whenever a row max grows, as on the page.
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+template <int D>
+struct FwdTile {
+  static constexpr int NW = 4;                               // waves per workgroup
+  static constexpr int BM = kFwdQueries;                     // queries per workgroup
+  static constexpr int BN = fwd_keys(D);                     // keys per tile
+  static constexpr int KB = BN / 32;                         // 32-key blocks per tile
+  static_assert(BM == NW * 32, "32 queries per wave");
+  static constexpr int CPR = D / 8;                          // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BN * D * 2;
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;         // K tile, then V tile
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;          // two-stage ring
+  static constexpr int KSTEPS = D / 16;                      // k steps of the score MFMA
+  static constexpr int DB = D / 32;                          // 32-wide d blocks of O
+  static constexpr int CPT = BN * CPR / (NW * 64);           // chunks per thread per tile
+  static_assert(CPT * NW * 64 == BN * CPR, "tile must split evenly over the threads");
+};
+
+// Rescale threshold in exp2 units (see file comment).
+template <typename T>
+inline constexpr float kRescaleSlack = kIsBF16<T> ? 0.0f : 8.0f;
+
+template <int D, typename T, bool CAUSAL, typename OT>
+__global__ __launch_bounds__(256) void fa_fwd_kernel(const uint16_t* __restrict__ q,
+                                                     const uint16_t* __restrict__ k,
+                                                     const uint16_t* __restrict__ v,
+                                                     void* __restrict__ o, float* __restrict__ lse,
+                                                     int N, int ZH, int n_qtiles, float c2) {
+  using C = FwdTile<D>;
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int h = lane >> 5;
+  const int l32 = lane & 31;
+
+  // Block -> (head, query tile).  Heads vary fastest so that the tiles of one
+  // head land on the same XCD (blocks are dealt round-robin over the 8 XCDs);
+  // with the causal mask the longest tiles go first.
+  const int bid = blockIdx.x;
+  const int tq = bid / ZH;
+  const int head = bid - tq * ZH;
+  const int qt = CAUSAL ? (n_qtiles - 1 - tq) : tq;
+  const int q0 = qt * C::BM;
+  const int wq0 = q0 + 32 * w;  // first query of this wave
+  const size_t hoff = (size_t)head * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto rq = make_rsrc(q + hoff, head_bytes);
+  const auto rk = make_rsrc(k + hoff, head_bytes);
+  const auto rv = make_rsrc(v + hoff, head_bytes);
+
+  // Q tile -> registers, B-operand layout: lane owns query wq0 + l32, k = d.
+  u32x4 qf[C::KSTEPS];
+#pragma unroll
+  for (int t = 0; t < C::KSTEPS; ++t)
+    qf[t] = gload16(rq, (uint32_t)(((wq0 + l32) * D + 16 * t + 8 * h) * 2));
+
+  const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
+  const int nt = (kv_end + C::BN - 1) / C::BN;
+
+  u32x4 kst[C::CPT], vst[C::CPT];
+  auto gload_tile = [&](int j) {
+    const int kv0 = j * C::BN;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int u = tid + 256 * i;
+      const int row = u / C::CPR, c = u % C::CPR;
+      const uint32_t off = (uint32_t)(((kv0 + row) * D + 8 * c) * 2);
+      kst[i] = gload16(rk, off);
+      vst[i] = gload16(rv, off);
+    }
+  };
+  auto lds_store_tile = [&](int stage) {
+    char* kt = smem + stage * C::STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int u = tid + 256 * i;
+      const int row = u / C::CPR, c = u % C::CPR;
+      const int off = tile_off<C::CPR>(row, 8 * c);
+      lds_write16(kt, off, kst[i]);
+      lds_write16(kt + C::TILE_BYTES, off, vst[i]);
+    }
+  };
+
+  float m_run = -1e30f;  // running max, exp2 units
+  float l_run = 0.f;     // running denominator (this lane half's keys)
+  f32x16 acc[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+
+  gload_tile(0);
+  lds_store_tile(0);
+  __syncthreads();
+
+  for (int j = 0; j < nt; ++j) {
+    const int stage = j & 1;
+    const bool more = j + 1 < nt;
+    if (more) gload_tile(j + 1);
+    const int kv0 = j * C::BN;
+    // With the causal mask a wave whose last query precedes the tile skips it.
+    const bool active = !CAUSAL || kv0 <= wq0 + 31;
+    if (active) {
+      const char* kt = smem + stage * C::STAGE_BYTES;
+      const char* vt = kt + C::TILE_BYTES;
+      // ---- S^T = K Q^T : rows = keys (sigma order), columns = this wave's queries
+      f32x16 s[C::KB];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < C::KSTEPS; ++t) {
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb) {
+          const u32x4 a = lds_read16(kt, tile_off<C::CPR>(32 * kb + sigma32(l32), 16 * t + 8 * h));
+          s[kb] = mfma32<T>(a, qf[t], s[kb]);
+        }
+      }
+      // ---- masks: causal diagonal tile and ragged last tile only
+      const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > wq0) || (kv0 + C::BN > N);
+      if (need_mask) {
+        const int query = wq0 + l32;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) {
+            const int key = kv0 + 32 * kb + 16 * (jj >> 3) + 8 * h + (jj & 7);
+            if ((CAUSAL && key > query) || key >= N) s[kb][jj] = -INFINITY;
+          }
+      }
+      // ---- online softmax, exp2 units
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s[kb][jj]);
+      mx = half_swap_max(mx);
+      const float m_new = fmaxf(m_run, mx * c2);
+      if (wave_any(m_new > m_run + kRescaleSlack<T>)) {
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+        m_run = m_new;
+      }
+      // p = exp2(s c - m), packed to the 16-bit type for the PV product; l_run
+      // sums the fp32 p.
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+          const float p = fast_exp2(__builtin_fmaf(s[kb][jj], c2, -m_run));
+          s[kb][jj] = p;
+          rs += p;
+        }
+      u32x4 pk[C::KB][2];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) pk[kb][t2] = pack8<T>(s[kb], 8 * t2);
+      l_run += rs;
+      // ---- O^T += V^T P^T : A = V^T from the V tile (transposing reads), B = P
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const int krow0 = 32 * kb + 16 * t2 + 8 * h;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            const u32x4 a = lds_read_tr_operand<C::CPR>(vt, krow0, 32 * db, lane);
+            acc[db] = mfma32<T>(a, pk[kb][t2], acc[db]);
+          }
+        }
+      }
+    }
+    if (more) lds_store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l written once; lse = ln(sum exp(S)) per query
+  const float lsum = half_swap_sum(l_run);
+  const float inv = 1.0f / lsum;
+  const int query = wq0 + l32;
+  if constexpr (sizeof(OT) == 4) {
+    const auto ro = make_rsrc((float*)o + hoff, (uint32_t)N * D * 4);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int d = 32 * db + 16 * half + 8 * h;
+        const int j0 = 8 * half;
+        u32x4 lo, hi;
+        lo.x = __float_as_uint(acc[db][j0 + 0] * inv);
+        lo.y = __float_as_uint(acc[db][j0 + 1] * inv);
+        lo.z = __float_as_uint(acc[db][j0 + 2] * inv);
+        lo.w = __float_as_uint(acc[db][j0 + 3] * inv);
+        hi.x = __float_as_uint(acc[db][j0 + 4] * inv);
+        hi.y = __float_as_uint(acc[db][j0 + 5] * inv);
+        hi.z = __float_as_uint(acc[db][j0 + 6] * inv);
+        hi.w = __float_as_uint(acc[db][j0 + 7] * inv);
+        const uint32_t off = (uint32_t)((query * D + d) * 4);
+        gstore16(ro, off, lo);
+        gstore16(ro, off + 16, hi);
+      }
+  } else {
+    const auto ro = make_rsrc((uint16_t*)o + hoff, (uint32_t)N * D * 2);
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      f32x16 y = acc[db] * inv;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int d = 32 * db + 16 * half + 8 * h;
+        gstore16(ro, (uint32_t)((query * D + d) * 2), pack8<T>(y, 8 * half));
+      }
+    }
+  }
+  if (h == 0) {
+    const auto rl = make_rsrc(lse + (size_t)head * N, (uint32_t)N * 4);
+    gstore_f32(rl, (uint32_t)query * 4, (m_run + __log2f(lsum)) * kLn2);
+  }
+}
+
+template <int D, typename T, bool CAUSAL, typename OT>
+hipError_t launch_fwd_t(const FwdArgs& a) {
+  using C = FwdTile<D>;
+  const int n_qtiles = (int)((a.N + C::BM - 1) / C::BM);
+  const int ZH = (int)(a.Z * a.H);
+  const dim3 grid((unsigned)(n_qtiles * ZH));
+  hipLaunchKernelGGL((fa_fwd_kernel<D, T, CAUSAL, OT>), grid, dim3(256), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.lse,
+                     (int)a.N, ZH, n_qtiles, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <int D, typename T>
+hipError_t launch_fwd_d(const FwdArgs& a) {
+  const bool of32 = a.o_dtype == F32::code;
+  if (a.causal) return of32 ? launch_fwd_t<D, T, true, float>(a) : launch_fwd_t<D, T, true, uint16_t>(a);
+  return of32 ? launch_fwd_t<D, T, false, float>(a) : launch_fwd_t<D, T, false, uint16_t>(a);
+}
+
+template <typename T>
+hipError_t launch_fwd_dt(const FwdArgs& a) {
+  switch (a.D) {
+    case 64: return launch_fwd_d<64, T>(a);
+    case 128: return launch_fwd_d<128, T>(a);
+    default: return launch_fwd_d<256, T>(a);
+  }
+}
+
+hipError_t launch_fwd(const FwdArgs& a) {
+  return a.dtype == BF16::code ? launch_fwd_dt<BF16>(a) : launch_fwd_dt<F16>(a);
+}
+
+}  // namespace fa

@@ -1,0 +1,49 @@
+// fa_kernels.h - internal launch interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  int64_t Z, H, N, D;
+  int dtype, o_dtype;
+  const void *q, *k, *v;
+  void* o;
+  float* lse;
+  float scale;
+  int causal;
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  int64_t Z, H, N, D;
+  int dtype, o_dtype;
+  const void *q, *k, *v, *o, *dout;
+  const float* lse;
+  float* delta;
+  void *dq, *dk, *dv;
+  float scale;
+  int causal;
+  int num_programs;  // persistent dK/dV grid; resolved by the caller (> 0)
+  hipStream_t stream;
+};
+
+hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_bwd_pre(const BwdArgs& a);
+hipError_t launch_bwd_dkdv(const BwdArgs& a);
+hipError_t launch_bwd_dq(const BwdArgs& a);
+
+// Resident dK/dV workgroups per CU for (D, dtype), from the occupancy API.
+hipError_t dkdv_blocks_per_cu(int D, int dtype, int* out);
+
+// Queries per forward workgroup and keys per forward K/V tile.
+constexpr int kFwdQueries = 128;
+constexpr int fwd_keys(int D) { return D == 64 ? 128 : (D == 128 ? 64 : 32); }
+
+// Keys per dK/dV work unit and queries per staged tile of the dK/dV kernel.
+constexpr int kDkdvKeys = 128;
+constexpr int dkdv_queries(int D) { return D == 256 ? 32 : 64; }
+
+}  // namespace fa

@@ -1,0 +1,176 @@
+/*
+ * fa.h - C ABI of an exact-attention (FlashAttention) forward and backward
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are those of the page "把 FlashAttention 搬上昇腾：Triton-Ascend
+ * CV Pipeline 优化实战" (BiumBiu, 2026-08-30), cited as [FA-Ascend]:
+ *
+ *   forward  ([FA-Ascend] §一):  S = Q K^T * scale,  P = softmax(S),  O = P V
+ *   backward ([FA-Ascend] §二):  Delta = rowsum(O * dO); P recomputed from the
+ *            saved row statistic; dP = dO V^T; dS = scale * P * (dP - Delta);
+ *            dQ = dS K; dK = dS^T Q; dV = P^T dO.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors Q, K, V, O, dO, dQ, dK, dV are dense, contiguous, row-major
+ *   (Z, H, N, D) arrays: Z batch, H heads, N sequence length (queries and keys
+ *   alike), D head dimension.  lse and Delta are contiguous (Z, H, N) float32.
+ * - Every tensor pointer is a DEVICE pointer owned by the caller; the library
+ *   never allocates, frees or retains device memory.  Pointers must be 16-byte
+ *   aligned.  Outputs must not alias inputs.
+ * - dtype is FA_DTYPE_F16 or FA_DTYPE_BF16 and applies to q, k, v, dout, dq,
+ *   dk, dv.  o_dtype is either dtype or FA_DTYPE_F32 and applies to o.
+ * - D must be 64, 128 or 256 ([FA-Ascend] §七 treats exactly these head dims).
+ *   N may be any value >= 1 (a ragged last tile is masked); Z*H*N == 0 is a
+ *   valid empty problem and returns FA_OK without launching anything (its
+ *   pointers are not checked and may be NULL).  (N + 256) * D * 4 must stay
+ *   below 2^31 (32-bit offsets within one head).
+ * - causal (0 or 1) selects the causal mask: key j is visible to query i iff
+ *   j <= i ([FA-Ascend] §八, lower triangle including the diagonal).
+ * - scale must be finite and > 0 (normally 1/sqrt(D)).
+ * - Every call enqueues its kernels on `stream` (0 = the default stream) and
+ *   returns without synchronising.  The return value reports argument and
+ *   launch errors only; a device fault shows at the caller's next
+ *   synchronisation.  Setting the environment variable FA_DEBUG_SYNC=1 makes
+ *   each call synchronise its stream and report errors it finds there.
+ * - Argument checks happen before any HIP call: a call that returns
+ *   FA_ERR_INVALID_ARGUMENT or FA_ERR_UNSUPPORTED has touched no GPU state.
+ * - Return values are fa_status codes.  fa_last_error() gives a
+ *   human-readable detail of the last failure on the calling thread.
+ * - No C++ exception crosses this interface and the library writes nothing to
+ *   stdout or stderr.  All entry points are thread-safe.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_dtype {
+  FA_DTYPE_F16 = 0,
+  FA_DTYPE_BF16 = 1,
+  FA_DTYPE_F32 = 2
+} fa_dtype;
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad enum, negative size, small workspace */
+  FA_ERR_UNSUPPORTED = 2,      /* valid arguments outside what the kernels implement (e.g. D=96) */
+  FA_ERR_HIP = 3               /* a HIP runtime call or kernel launch failed */
+} fa_status;
+
+/* Library version: major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+/* Static string naming a status code ("FA_OK", ...); never NULL. */
+const char* fa_status_string(int status);
+
+/* Detail of the last error on the calling thread ("" if none); valid until
+ * the next call into the library on the same thread. */
+const char* fa_last_error(void);
+
+/*
+ * Forward pass, [FA-Ascend] §一.
+ *   q, k, v : (Z,H,N,D) dtype, read only.
+ *   o       : (Z,H,N,D) o_dtype, written: O = softmax(Q K^T * scale) V.
+ *   lse     : (Z,H,N) float32, written: natural-log log-sum-exp of each score
+ *             row, lse_i = ln(sum_j exp(S_ij)), the row statistic the backward
+ *             needs to recompute P ([FA-Ascend] §二 "recompute_softmax").
+ * One kernel: the Q tile stays in registers, K/V tiles stream through LDS,
+ * the softmax is the online (running max / running sum) form of §一, and
+ * neither S nor P is ever written to memory.
+ */
+int fa_fwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype,
+           const void* q, const void* k, const void* v, void* o, float* lse,
+           float scale, int causal, hipStream_t stream);
+
+/* Bytes of device workspace fa_bwd needs: Z*H*N*sizeof(float) (Delta). */
+size_t fa_bwd_workspace_bytes(int64_t Z, int64_t H, int64_t N, int64_t D);
+
+/*
+ * Backward pass, [FA-Ascend] §二.
+ *   q, k, v, o, lse : as produced for/by fa_fwd with the same scale, causal,
+ *                     dtype and o_dtype (lse must be passed unchanged).
+ *   dout            : (Z,H,N,D) dtype, the incoming gradient dO.
+ *   dq, dk, dv      : (Z,H,N,D) dtype, written (overwritten, not accumulated).
+ *   workspace       : device buffer of at least fa_bwd_workspace_bytes();
+ *                     holds Delta between the stages; contents on return are
+ *                     Delta = rowsum(O * dO) in float32.
+ * Runs fa_bwd_preprocess, then fa_bwd_dkdv, then fa_bwd_dq on `stream`.
+ */
+int fa_bwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype,
+           const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           float scale, int causal, void* workspace, size_t workspace_bytes,
+           hipStream_t stream);
+
+/*
+ * Stage 1 of the backward: delta[z,h,i] = sum_d O[z,h,i,d] * dO[z,h,i,d]
+ * accumulated in float32 ([FA-Ascend] §二, first line).  o is o_dtype, dout
+ * is dtype, delta is (Z,H,N) float32 (written).
+ */
+int fa_bwd_preprocess(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype,
+                      int o_dtype, const void* o, const void* dout,
+                      float* delta, hipStream_t stream);
+
+/*
+ * Stage 2: dK and dV.  A persistent grid of `num_programs` workgroups (0 =
+ * one per resident slot on the device: compute units x workgroups per CU)
+ * walks a static schedule of (head, key-tile) units; each workgroup owns whole
+ * key tiles, recomputes P from lse for every query tile, and writes each dK/dV
+ * tile exactly once: no atomics and no N*N scratch ([FA-Ascend] §二 three
+ * principles, §五 persistent programs).  delta comes from fa_bwd_preprocess.
+ * The result does not depend on num_programs (bitwise).
+ */
+int fa_bwd_dkdv(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype,
+                const void* q, const void* k, const void* v, const void* dout,
+                const float* lse, const float* delta, void* dk, void* dv,
+                float scale, int causal, int num_programs, hipStream_t stream);
+
+/*
+ * Stage 3: dQ.  One workgroup per (head, query tile) owns its dQ tile and
+ * writes it exactly once ([FA-Ascend] §二: a query tile can finish dQ by
+ * itself).
+ */
+int fa_bwd_dq(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype,
+              const void* q, const void* k, const void* v, const void* dout,
+              const float* lse, const float* delta, void* dq, float scale,
+              int causal, hipStream_t stream);
+
+/*
+ * Device facts used for launch sizing, for the current device: compute
+ * units, and the persistent grid fa_bwd_dkdv uses for (D, dtype) when
+ * num_programs is 0.  Either output pointer may be NULL.
+ */
+int fa_device_info(int64_t D, int dtype, int* compute_units, int* dkdv_programs);
+
+/*
+ * Host-only planning helpers (no HIP call, no device needed).
+ *
+ * fa_dkdv_schedule: replays the static schedule of fa_bwd_dkdv with
+ * `num_programs` programs.  units_per_program[p] receives the number of
+ * (head, key tile) units program p owns and qtiles_per_program[p] the number
+ * of query tiles it visits; both arrays hold num_programs entries (either may
+ * be NULL).  *n_units receives the total unit count.  [FA-Ascend] §五 deals
+ * heads to a fixed number of programs with a fixed stride; without the causal
+ * mask and with one key tile per head this reproduces that dealing.
+ *
+ * fa_fwd_tile_pairs: number of (query tile, key tile) pairs fa_fwd visits for
+ * a sequence of N at head dim D, and the total number of pairs, so that the
+ * work saved by the shortened causal loop ([FA-Ascend] §八) can be checked.
+ */
+int fa_dkdv_schedule(int64_t Z, int64_t H, int64_t N, int64_t D, int causal, int num_programs,
+                     int64_t* units_per_program, int64_t* qtiles_per_program, int64_t* n_units);
+int fa_fwd_tile_pairs(int64_t N, int64_t D, int causal, int64_t* visited, int64_t* total);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

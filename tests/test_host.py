@@ -1,0 +1,142 @@
+"""Host-side checks that need no GPU: the C ABI loads and exports every symbol
+its header declares, argument errors come back before any HIP call, and the
+schedule/tile logic reproduces the page's worked numbers (tests/golden/)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def _golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                k, v = line.split("=")
+                out[k] = float(v) if "." in v else int(v)
+    return out
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import exact_attention_03_amd as fa
+
+    fa.lib()  # raises if libfa.so has not been built
+    return fa
+
+
+def test_library_exports_every_declared_symbol(fa):
+    from exact_attention_03_amd._lib import SIGNATURES
+
+    header = open(os.path.join(ROOT, "include", "fa.h")).read()
+    header = re.sub(r"/\*.*?\*/", "", header, flags=re.S)
+    declared = set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", header))
+    assert declared, "no declarations found"
+    lib = fa.lib()
+    for name in sorted(declared):
+        assert hasattr(lib, name), f"{name} declared in fa.h but not exported"
+    assert declared == set(SIGNATURES), "binding signatures out of step with fa.h"
+
+
+def test_status_strings(fa):
+    assert fa.status_name(0) == "FA_OK"
+    assert fa.status_name(1) == "FA_ERR_INVALID_ARGUMENT"
+    assert fa.status_name(2) == "FA_ERR_UNSUPPORTED"
+    assert fa.status_name(3) == "FA_ERR_HIP"
+    assert fa.lib().fa_version() >= 100
+
+
+P = ctypes.c_void_p(0x10000)  # aligned dummy; never dereferenced on error paths
+MIS = ctypes.c_void_p(0x10008)
+
+
+def _fwd(fa, Z=1, H=1, N=128, D=64, dtype=0, odt=0, q=P, k=P, v=P, o=P, lse=P, scale=0.125, causal=0):
+    return fa.lib().fa_fwd(Z, H, N, D, dtype, odt, q, k, v, o, lse, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), 2), (dict(D=0), 2), (dict(N=-1), 1), (dict(dtype=7), 1), (dict(odt=1), 1),
+    (dict(q=None), 1), (dict(o=MIS), 1), (dict(lse=None), 1), (dict(scale=0.0), 1),
+    (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1), (dict(causal=2), 1),
+    (dict(N=1 << 30, D=256), 2),
+])
+def test_fwd_argument_errors(fa, kw, status):
+    assert _fwd(fa, **kw) == status
+    assert fa.last_error() != ""
+
+
+def test_empty_problem_is_ok_without_pointers(fa):
+    assert _fwd(fa, Z=0, q=None, k=None, v=None, o=None, lse=None) == 0
+    assert _fwd(fa, N=0, q=None, k=None, v=None, o=None, lse=None) == 0
+    lib = fa.lib()
+    assert lib.fa_bwd(0, 1, 8, 64, 0, 0, *([None] * 9), 0.125, 0, None, 0, None) == 0
+
+
+def test_bwd_workspace_rules(fa):
+    lib = fa.lib()
+    assert lib.fa_bwd_workspace_bytes(128, 8, 1024, 128) == 128 * 8 * 1024 * 4
+    need = lib.fa_bwd_workspace_bytes(1, 2, 100, 64)
+    st = lib.fa_bwd(1, 2, 100, 64, 0, 0, *([P] * 9), 0.125, 0, P, need - 4, None)
+    assert st == 1 and "workspace" in fa.last_error()
+    st = lib.fa_bwd(1, 2, 100, 64, 0, 0, *([P] * 9), 0.125, 0, None, need, None)
+    assert st == 1
+
+
+def test_stage_argument_errors(fa):
+    lib = fa.lib()
+    assert lib.fa_bwd_preprocess(1, 1, 64, 64, 0, 1, P, P, P, None) == 1       # o_dtype bf16 with f16
+    assert lib.fa_bwd_dkdv(1, 1, 64, 64, 0, *([P] * 8), 0.125, 0, -1, None) == 1  # negative grid
+    assert lib.fa_bwd_dq(1, 1, 64, 32, 0, *([P] * 7), 0.125, 0, None) == 2      # D = 32
+    assert lib.fa_bwd_dq(1, 1, 64, 64, 0, *([P] * 6), MIS, 0.125, 0, None) == 1  # misaligned dq
+
+
+def test_causal_tile_count_matches_page(fa):
+    g = _golden("causal_tile_count.txt")
+    # At D=64 the forward uses 128 x 128 tiles, so N = 8 * 128 is the page's 8 x 8 grid.
+    vis, tot = fa.fwd_tile_pairs(8 * 128, 64, True)
+    assert (vis, tot) == (g["causal_tiles"], g["full_tiles"])
+    assert 100.0 * (1 - vis / tot) == pytest.approx(g["saved_percent"])
+    assert fa.fwd_tile_pairs(8 * 128, 64, False) == (g["full_tiles"], g["full_tiles"])
+    # other head dims use narrower key tiles; the saved fraction is the same
+    for D in (128, 256):
+        vis, tot = fa.fwd_tile_pairs(8 * 128, D, True)
+        assert 1 - vis / tot == pytest.approx(g["saved_percent"] / 100)
+
+
+def test_persistent_dealing_matches_page(fa):
+    """One key tile per head (N = 128) and no mask: the schedule deals heads to
+    20 programs exactly as the page's fixed stride does: 51 or 52 each."""
+    g = _golden("persistent_programs.txt")
+    units, work, n = fa.dkdv_schedule(g["Z"], g["H"], 128, 64, False, g["programs"])
+    assert n == g["heads"] == sum(units)
+    assert min(units) == g["min_heads_per_program"] and max(units) == g["max_heads_per_program"]
+    assert units.count(52) == g["heads"] - 51 * g["programs"]
+
+
+@pytest.mark.parametrize("Z,H,N,D,causal,Pn", [
+    (128, 8, 1024, 128, True, 256), (16, 16, 8192, 128, True, 256), (128, 8, 1024, 64, False, 256),
+    (3, 5, 1000, 64, True, 97), (1, 1, 130, 256, True, 7), (2, 2, 300, 128, False, 1000),
+])
+def test_schedule_covers_units_and_balances(fa, Z, H, N, D, causal, Pn):
+    units, work, n = fa.dkdv_schedule(Z, H, N, D, causal, Pn)
+    assert sum(units) == n == Z * H * ((N + 127) // 128)
+    bq = 32 if D == 256 else 64
+    nq = (N + bq - 1) // bq
+    total = sum(nq - ((kt * 128) // bq if causal else 0) for kt in range((N + 127) // 128)) * Z * H
+    assert sum(work) == total
+    if n >= 4 * Pn:
+        mean = total / Pn
+        assert max(work) <= 1.10 * mean, (max(work), mean)
+
+
+def test_workspace_versus_page_full_scratch(fa):
+    g = _golden("full_scratch.txt")
+    full = g["Z"] * g["H"] * g["N"] * g["N"] * g["bytes_per_element"]
+    assert full == g["one_copy_bytes"]
+    ours = fa.workspace_bytes(g["Z"], g["H"], g["N"], 128)
+    assert ours == g["Z"] * g["H"] * g["N"] * 4 and ours * 512 == full
