@@ -1,0 +1,331 @@
+"""FlashAttention forward + backward throughput on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+fa_fwd (O in the input dtype, lse), then the backward's three stages
+(fa_bwd_preprocess -> fa_bwd_dkdv -> fa_bwd_dq, exactly what fa_bwd runs),
+all through the library's C ABI on torch's current stream.
+
+Default workload: Z=128, H=8, N=1024, D=128, fp16, causal, scale=1/sqrt(128)
+(seeded i.i.d. N(0,1) Q/K/V/dO).  Prints ONE JSON line with:
+  value       fwd+bwd TFLOP/s (FlashAttention convention: fwd = 4 Z H N^2 D,
+              halved when causal; bwd = 2.5 x fwd)
+  breakdown   fwd, bwd and per-kernel times, TFLOP/s and fraction of peak
+  roofline    the kernel taking most of the step, against its own bound
+  cpu_baseline the fp64 oracle on a bounded sample of the same workload
+
+Kernel durations come from HIP events recorded between the stage calls on the
+stream the kernels run on, inside the timed region.  Inputs are resident in
+HBM before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402  (seeded inputs only; no attention arithmetic)
+
+# MI355X published dense peaks.
+PEAK_MFMA_F16_TFLOPS = 2516.6   # fp16 / bf16 dense MFMA
+PEAK_HBM_GBS = 8000.0           # HBM3E
+DEFAULT_WORKLOAD = "d128_causal"
+KERNELS = ("fa_fwd", "fa_bwd_pre", "fa_bwd_dkdv", "fa_bwd_dq")
+# Source files each kernel is built from; a stored traffic measurement is only
+# reported while these are unchanged.
+KERNEL_SOURCES = {
+    "fa_fwd": ("fa_fwd.hip", "fa_device.h", "fa_kernels.h"),
+    "fa_bwd_pre": ("fa_bwd.hip", "fa_device.h", "fa_kernels.h"),
+    "fa_bwd_dkdv": ("fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_schedule.h"),
+    "fa_bwd_dq": ("fa_bwd.hip", "fa_device.h", "fa_kernels.h"),
+}
+
+
+def fwd_flops(w) -> float:
+    f = 4.0 * w.Z * w.H * w.N * w.N * w.D
+    return f / 2 if w.causal else f
+
+
+def kernel_work(w, o_bytes: int):
+    """Algorithmic work of one launch of each kernel: (bound, amount, unit).
+
+    fa_fwd: the two forward GEMMs (QK^T, PV), 4 N^2 D per head (x 1/2 causal).
+    fa_bwd_dkdv: four of the five counted backward GEMMs (QK^T recompute,
+      dO V^T, P^T dO, dS^T Q), 8 N^2 D per head (x 1/2 causal).
+    fa_bwd_dq: the fifth (dS K), 2 N^2 D per head (x 1/2 causal); its two
+      recomputed GEMMs are not counted.
+    fa_bwd_pre: HBM bytes, read O and dO rows and write one fp32 per row.
+    """
+    hf = fwd_flops(w)  # = 4 N^2 D per head, halved when causal
+    rows = w.Z * w.H * w.N
+    return {
+        "fa_fwd": ("mfma", hf, "flop"),
+        "fa_bwd_dkdv": ("mfma", 2.0 * hf, "flop"),
+        "fa_bwd_dq": ("mfma", 0.5 * hf, "flop"),
+        "fa_bwd_pre": ("hbm", float(rows * (w.D * o_bytes + w.D * 2 + 4)), "byte"),
+    }
+
+
+def sources_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "exact_attention_03_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None.
+
+    The summary file (profiles/traffic_<kernel>_<workload>.txt) holds
+    key = value lines: fetch_bytes, write_bytes (already scaled by the
+    copy-kernel calibration) and source_hash.  A hash that no longer matches
+    the kernel's sources means the kernel changed since the counters were
+    taken, and the figure is not reported.
+    """
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if "=" in line:
+                a, b = line.split("=", 1)
+                kv[a.strip()] = b.strip()
+    if kv.get("source_hash") != sources_hash(kernel):
+        return None
+    try:
+        return float(kv["fetch_bytes"]) + float(kv["write_bytes"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ CPU baseline
+def _oracle_heads(args):
+    """Worker: fp64 oracle forward + backward over a list of heads."""
+    import numpy as np
+
+    import oracle
+
+    q, k, v, do, scale, causal = args
+    for i in range(q.shape[0]):
+        oracle.attention_backward(q[i].astype(np.float64), k[i].astype(np.float64),
+                                  v[i].astype(np.float64), do[i].astype(np.float64), scale, causal)
+    return q.shape[0]
+
+
+def cpu_baseline(w, cpu_inputs, n_heads: int, workers: int):
+    """Time the oracle (as it stands) over the first n_heads heads of the workload."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    import numpy as np
+
+    n_heads = min(n_heads, w.Z * w.H)
+    flat = [t.reshape(w.Z * w.H, w.N, w.D)[:n_heads].float().numpy() for t in cpu_inputs]
+    workers = max(1, min(workers, n_heads))
+    chunks = np.array_split(np.arange(n_heads), workers)
+    jobs = [tuple(x[c[0]:c[-1] + 1] for x in flat) + (w.scale, w.causal) for c in chunks if len(c)]
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"  # one BLAS thread per worker process
+    try:
+        with cf.ProcessPoolExecutor(max_workers=len(jobs), mp_context=mp.get_context("spawn")) as ex:
+            list(ex.map(_oracle_heads, [tuple(x[:1] for x in j[:4]) + j[4:] for j in jobs]))  # warm import
+            t0 = time.perf_counter()
+            done = sum(ex.map(_oracle_heads, jobs))
+            dt = time.perf_counter() - t0
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    flops = 3.5 * fwd_flops(w) * done / (w.Z * w.H)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": len(jobs),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle, fwd+bwd (full N x N S and P, naive backward) on {done} of "
+                   f"{w.Z * w.H} heads of the same seeded workload, {len(jobs)} processes x 1 BLAS "
+                   f"thread, wall {dt:.2f} s; FLOPs counted with the same convention"),
+    }
+
+
+# ------------------------------------------------------------------ GPU timing
+def run(args):
+    import torch
+
+    import exact_attention_03_amd as fa
+
+    w = workloads.by_name(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cpu_inputs = workloads.make_inputs(w)
+    q, k, v, do = (t.to(dev) for t in cpu_inputs)
+    Z, H, N, D = w.shape
+    tdt = q.dtype
+    o = torch.empty_like(q)
+    lse = torch.empty((Z, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((Z, H, N), dtype=torch.float32, device=dev)
+    L = fa.lib()
+    code = fa._dtype_code(q)
+    causal = int(w.causal)
+    scale = w.scale
+    P = lambda t: t.data_ptr()  # noqa: E731
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def call(st, name):
+        if st != 0:
+            raise fa.FAError(st, name, fa.last_error())
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        call(L.fa_fwd(Z, H, N, D, code, code, P(q), P(k), P(v), P(o), P(lse), scale, causal, sp), "fa_fwd")
+        if ev is not None:
+            ev[1].record(stream)
+        call(L.fa_bwd_preprocess(Z, H, N, D, code, code, P(o), P(do), P(delta), sp), "fa_bwd_preprocess")
+        if ev is not None:
+            ev[2].record(stream)
+        call(L.fa_bwd_dkdv(Z, H, N, D, code, P(q), P(k), P(v), P(do), P(lse), P(delta), P(dk), P(dv),
+                           scale, causal, 0, sp), "fa_bwd_dkdv")
+        if ev is not None:
+            ev[3].record(stream)
+        call(L.fa_bwd_dq(Z, H, N, D, code, P(q), P(k), P(v), P(do), P(lse), P(delta), P(dq), scale, causal, sp),
+             "fa_bwd_dq")
+        if ev is not None:
+            ev[4].record(stream)
+
+    if args.calib_copy_mib > 0:
+        # A plain device copy of known size, for scaling HBM counters.
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        step(evs[s])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    per = {name: [] for name in KERNELS}
+    for e in evs:
+        for i, name in enumerate(KERNELS):
+            per[name].append(e[i].elapsed_time(e[i + 1]))
+    avg = {n: sum(x) / len(x) for n, x in per.items()}
+
+    ff = fwd_flops(w)
+    fwd_ms = avg["fa_fwd"]
+    bwd_ms = avg["fa_bwd_pre"] + avg["fa_bwd_dkdv"] + avg["fa_bwd_dq"]
+    value = 3.5 * ff / (ms_step * 1e-3) / 1e12
+    work = kernel_work(w, o.element_size())
+    kern = {}
+    for name in KERNELS:
+        bound, amount, unit = work[name]
+        t = avg[name] * 1e-3
+        if bound == "mfma":
+            ach = amount / t / 1e12
+            kern[name] = {"ms": round(avg[name], 4), "bound": "mfma", "TFLOP/s": round(ach, 1),
+                          "frac": round(ach / PEAK_MFMA_F16_TFLOPS, 4)}
+        else:
+            ach = amount / t / 1e9
+            kern[name] = {"ms": round(avg[name], 4), "bound": "hbm", "GB/s": round(ach, 1),
+                          "frac": round(ach / PEAK_HBM_GBS, 4)}
+    dom = max(KERNELS, key=lambda n: avg[n])
+    bound, amount, unit = work[dom]
+    t = avg[dom] * 1e-3
+    traffic = stored_traffic(dom, w.name)
+    if bound == "mfma":
+        roof = {"bound": "mfma", "achieved": round(amount / t / 1e12, 1), "peak": PEAK_MFMA_F16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(amount / t / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = traffic
+    roof["kernel"] = dom
+    roof["algorithmic"] = {"amount": amount, "unit": unit, "per_launch": True}
+
+    out = {
+        "metric": "FlashAttention fwd+bwd TFLOP/s on 1 MI355X, % of fp16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: Z={Z} H={H} N={N} D={D} {w.dtype} causal={bool(w.causal)} "
+                               f"scale={scale:.9g}", "Z": Z, "H": H, "N": N, "D": D, "causal": bool(w.causal),
+                   "seed": w.seed},
+        "frac_of_peak": round(value / PEAK_MFMA_F16_TFLOPS, 4),
+        "breakdown": {
+            "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+            "fwd_TFLOP/s": round(ff / (fwd_ms * 1e-3) / 1e12, 1),
+            "bwd_TFLOP/s": round(2.5 * ff / (bwd_ms * 1e-3) / 1e12, 1),
+            "fwd_frac": round(ff / (fwd_ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
+            "bwd_frac": round(2.5 * ff / (bwd_ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
+            "kernels": kern,
+        },
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, cpu_inputs, args.cpu_heads, args.cpu_workers)
+    return out
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cpu-heads", type=int, default=384, help="heads in the oracle timing sample")
+    ap.add_argument("--cpu-workers", type=int, default=min(16, len(os.sched_getaffinity(0))))
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before warm-up, copy a buffer of this many MiB (for HBM counter calibration)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested). Attention heads are "
+              "independent, so a multi-GPU run would shard Z*H across GPUs with no exchange; it is not "
+              "implemented here.", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be >= 1 and --warmup >= 0")
+    out = run(args)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
