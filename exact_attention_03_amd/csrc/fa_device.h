@@ -161,6 +161,17 @@ FA_DEV void gstore_f32(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 
+// Global -> LDS copy without a register round trip (gfx950 16-byte buffer
+// load into LDS): lane l's 16 bytes at byte offset voff of the resource land
+// at lds_base + 16 l.  lds_base must be the same for the whole wave.  Bytes
+// past the resource's end arrive as zeros.  Completion is tracked by vmcnt.
+typedef __attribute__((address_space(3))) void lds_void_t;
+FA_DEV void dma16(__amdgpu_buffer_rsrc_t r, char* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, voff, 0, 0, 0);
+}
+// Wait until every global load of this wave (including LDS copies) is done.
+FA_DEV void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ----------------------------------------------------------------- LDS tiles
 // A tile is `rows` x D 16-bit elements stored row-major in LDS, in 16-byte
 // chunks (CPR = D/8 chunks per row).  Chunk c of row r sits at chunk position

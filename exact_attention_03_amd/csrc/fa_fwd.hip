@@ -13,14 +13,19 @@
 //   * one workgroup = 4 waves = one Q tile of BM = 128 queries of one head;
 //     wave w owns 32 consecutive queries and keeps them in registers as the
 //     B operand of the score MFMA for the whole kernel;
-//   * K/V tiles of BN keys are staged through a two-stage LDS ring (global ->
-//     registers -> LDS, the next tile's global loads issued before the current
-//     tile's math);
+//   * two workgroups share a compute unit (at most 256 registers per lane and
+//     64 KiB of LDS each), so one wave's softmax arithmetic overlaps the other
+//     wave's matrix instructions on the same SIMD;
+//   * K/V tiles of BN keys are copied global -> LDS by the buffer unit itself
+//     (no register staging) into a two-stage ring: the copy of tile j+1 is in
+//     flight while tile j is consumed, with one barrier per tile;
 //   * scores are computed transposed, S^T = K Q^T, so that each lane owns one
 //     query (a column of the MFMA result) and its softmax statistics are
 //     per-lane values; a row max needs one exchange between lane halves;
 //   * the output is accumulated transposed as well, O^T = V^T P^T, with V^T
-//     read straight from the row-major V tile by transposing LDS reads.
+//     read straight from the row-major V tile by transposing LDS reads;
+//   * the query tiles of one head are dispatched back to back on one XCD so
+//     that the head's K and V are read from HBM about once.
 // Refinement over the page's rescale-on-every-new-max (fp16 only): the running
 // max used for the exponentials is only raised when some row's max grew by more
 // than 8 in exp2 units, so most tiles skip rescaling the accumulator; the
@@ -31,6 +36,7 @@
 // 2^-9 |v|.  So bf16 rescales whenever a row max grows, as on the page.
 #include "fa_device.h"
 #include "fa_kernels.h"
+#include "fa_schedule.h"
 
 namespace fa {
 
@@ -47,8 +53,10 @@ struct FwdTile {
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES;          // two-stage ring
   static constexpr int KSTEPS = D / 16;                      // k steps of the score MFMA
   static constexpr int DB = D / 32;                          // 32-wide d blocks of O
-  static constexpr int CPT = BN * CPR / (NW * 64);           // chunks per thread per tile
-  static_assert(CPT * NW * 64 == BN * CPR, "tile must split evenly over the threads");
+  static constexpr int DMA = TILE_BYTES / (NW * 1024);       // 1 KiB copies per wave per tile
+  static_assert(DMA * NW * 1024 == TILE_BYTES, "tile must split into 1 KiB copies per wave");
+  // Waves per SIMD the register budget is sized for.
+  static constexpr int OCC = D == 256 ? 1 : 2;
 };
 
 // Rescale threshold in exp2 units (see file comment).
@@ -56,13 +64,12 @@ template <typename T>
 inline constexpr float kRescaleSlack = kIsBF16<T> ? 0.0f : 8.0f;
 
 template <int D, typename T, bool CAUSAL, typename OT>
-__global__ __launch_bounds__(256) void fa_fwd_kernel(const uint16_t* __restrict__ q,
-                                                     const uint16_t* __restrict__ k,
-                                                     const uint16_t* __restrict__ v,
-                                                     void* __restrict__ o, float* __restrict__ lse,
-                                                     int N, int ZH, int n_qtiles, float c2) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdTile<D>::OCC, FwdTile<D>::OCC)))
+void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                   const uint16_t* __restrict__ v, void* __restrict__ o, float* __restrict__ lse, int N,
+                   int ZH, int n_qtiles, float c2) {
   using C = FwdTile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -70,13 +77,12 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(const uint16_t* __restrict_
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  // Block -> (head, query tile).  Heads vary fastest so that the tiles of one
-  // head land on the same XCD (blocks are dealt round-robin over the 8 XCDs);
-  // with the causal mask the longest tiles go first.
-  const int bid = blockIdx.x;
-  const int tq = bid / ZH;
-  const int head = bid - tq * ZH;
-  const int qt = CAUSAL ? (n_qtiles - 1 - tq) : tq;
+  int64_t head64, slot64;
+  xcd_tile(blockIdx.x, n_qtiles, &head64, &slot64);
+  if (head64 >= ZH) return;  // padding block
+  const int head = (int)head64;
+  // With the causal mask the longest tiles of a head go first.
+  const int qt = CAUSAL ? (n_qtiles - 1 - (int)slot64) : (int)slot64;
   const int q0 = qt * C::BM;
   const int wq0 = q0 + 32 * w;  // first query of this wave
   const size_t hoff = (size_t)head * (size_t)N * D;
@@ -85,38 +91,32 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(const uint16_t* __restrict_
   const auto rk = make_rsrc(k + hoff, head_bytes);
   const auto rv = make_rsrc(v + hoff, head_bytes);
 
+  const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
+  const int nt = (kv_end + C::BN - 1) / C::BN;
+
+  // Copy K/V tile j into ring stage st.  LDS slot sl (16 bytes) of a tile holds
+  // row sl / CPR, chunk (sl % CPR) ^ swz(row): the swizzled layout of tile_off.
+  auto issue_tile = [&](int j, int st) {
+    char* kdst = smem + st * C::STAGE_BYTES;
+    char* vdst = kdst + C::TILE_BYTES;
+    const int kv0 = j * C::BN;
+#pragma unroll
+    for (int i = 0; i < C::DMA; ++i) {
+      const int blk = w * C::DMA + i;
+      const int sl = blk * 64 + lane;
+      const int row = sl / C::CPR, pos = sl % C::CPR;
+      const uint32_t off = (uint32_t)(((kv0 + row) * D + 8 * (pos ^ swz<C::CPR>(row))) * 2);
+      dma16(rk, kdst + blk * 1024, off);
+      dma16(rv, vdst + blk * 1024, off);
+    }
+  };
+  issue_tile(0, 0);
+
   // Q tile -> registers, B-operand layout: lane owns query wq0 + l32, k = d.
   u32x4 qf[C::KSTEPS];
 #pragma unroll
   for (int t = 0; t < C::KSTEPS; ++t)
     qf[t] = gload16(rq, (uint32_t)(((wq0 + l32) * D + 16 * t + 8 * h) * 2));
-
-  const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
-  const int nt = (kv_end + C::BN - 1) / C::BN;
-
-  u32x4 kst[C::CPT], vst[C::CPT];
-  auto gload_tile = [&](int j) {
-    const int kv0 = j * C::BN;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int u = tid + 256 * i;
-      const int row = u / C::CPR, c = u % C::CPR;
-      const uint32_t off = (uint32_t)(((kv0 + row) * D + 8 * c) * 2);
-      kst[i] = gload16(rk, off);
-      vst[i] = gload16(rv, off);
-    }
-  };
-  auto lds_store_tile = [&](int stage) {
-    char* kt = smem + stage * C::STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int u = tid + 256 * i;
-      const int row = u / C::CPR, c = u % C::CPR;
-      const int off = tile_off<C::CPR>(row, 8 * c);
-      lds_write16(kt, off, kst[i]);
-      lds_write16(kt + C::TILE_BYTES, off, vst[i]);
-    }
-  };
 
   float m_run = -1e30f;  // running max, exp2 units
   float l_run = 0.f;     // running denominator (this lane half's keys)
@@ -124,92 +124,83 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(const uint16_t* __restrict_
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
 
-  gload_tile(0);
-  lds_store_tile(0);
-  __syncthreads();
-
   for (int j = 0; j < nt; ++j) {
-    const int stage = j & 1;
-    const bool more = j + 1 < nt;
-    if (more) gload_tile(j + 1);
+    // Tile j has landed for every wave, and every wave is done with tile j-1,
+    // whose stage the copy of tile j+1 now overwrites.
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < nt) issue_tile(j + 1, (j + 1) & 1);
     const int kv0 = j * C::BN;
     // With the causal mask a wave whose last query precedes the tile skips it.
     const bool active = !CAUSAL || kv0 <= wq0 + 31;
-    if (active) {
-      const char* kt = smem + stage * C::STAGE_BYTES;
-      const char* vt = kt + C::TILE_BYTES;
-      // ---- S^T = K Q^T : rows = keys (sigma order), columns = this wave's queries
-      f32x16 s[C::KB];
+    if (!active) continue;
+    const char* kt = smem + (j & 1) * C::STAGE_BYTES;
+    const char* vt = kt + C::TILE_BYTES;
+    // ---- S^T = K Q^T : rows = keys (sigma order), columns = this wave's queries
+    f32x16 s[C::KB];
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) s[kb] = f32x16{};
+    for (int kb = 0; kb < C::KB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-      for (int t = 0; t < C::KSTEPS; ++t) {
+    for (int t = 0; t < C::KSTEPS; ++t) {
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-          const u32x4 a = lds_read16(kt, tile_off<C::CPR>(32 * kb + sigma32(l32), 16 * t + 8 * h));
-          s[kb] = mfma32<T>(a, qf[t], s[kb]);
-        }
+      for (int kb = 0; kb < C::KB; ++kb) {
+        const u32x4 a = lds_read16(kt, tile_off<C::CPR>(32 * kb + sigma32(l32), 16 * t + 8 * h));
+        s[kb] = mfma32<T>(a, qf[t], s[kb]);
       }
-      // ---- masks: causal diagonal tile and ragged last tile only
-      const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > wq0) || (kv0 + C::BN > N);
-      if (need_mask) {
-        const int query = wq0 + l32;
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-          for (int jj = 0; jj < 16; ++jj) {
-            const int key = kv0 + 32 * kb + 16 * (jj >> 3) + 8 * h + (jj & 7);
-            if ((CAUSAL && key > query) || key >= N) s[kb][jj] = -INFINITY;
-          }
-      }
-      // ---- online softmax, exp2 units
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s[kb][jj]);
-      mx = half_swap_max(mx);
-      const float m_new = fmaxf(m_run, mx * c2);
-      if (wave_any(m_new > m_run + kRescaleSlack<T>)) {
-        const float alpha = fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
-        m_run = m_new;
-      }
-      // p = exp2(s c - m), packed to the 16-bit type for the PV product; l_run
-      // sums the fp32 p.
-      float rs = 0.f;
+    }
+    // ---- masks: causal diagonal tile and ragged last tile only
+    const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > wq0) || (kv0 + C::BN > N);
+    if (need_mask) {
+      const int query = wq0 + l32;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
-          const float p = fast_exp2(__builtin_fmaf(s[kb][jj], c2, -m_run));
-          s[kb][jj] = p;
-          rs += p;
+          const int key = kv0 + 32 * kb + 16 * (jj >> 3) + 8 * h + (jj & 7);
+          if ((CAUSAL && key > query) || key >= N) s[kb][jj] = -INFINITY;
         }
-      u32x4 pk[C::KB][2];
+    }
+    // ---- online softmax, exp2 units
+    float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) pk[kb][t2] = pack8<T>(s[kb], 8 * t2);
-      l_run += rs;
-      // ---- O^T += V^T P^T : A = V^T from the V tile (transposing reads), B = P
+      for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s[kb][jj]);
+    mx = half_swap_max(mx);
+    const float m_new = fmaxf(m_run, mx * c2);
+    if (wave_any(m_new > m_run + kRescaleSlack<T>)) {
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
+      for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+      m_run = m_new;
+    }
+    // p = exp2(s c - m), packed to the 16-bit type for the PV product; l_run
+    // sums the fp32 p.
+    float rs = 0.f;
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const int krow0 = 32 * kb + 16 * t2 + 8 * h;
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            const u32x4 a = lds_read_tr_operand<C::CPR>(vt, krow0, 32 * db, lane);
-            acc[db] = mfma32<T>(a, pk[kb][t2], acc[db]);
-          }
+      for (int jj = 0; jj < 16; ++jj) {
+        const float p = fast_exp2(__builtin_fmaf(s[kb][jj], c2, -m_run));
+        s[kb][jj] = p;
+        rs += p;
+      }
+    l_run += rs;
+    // ---- O^T += V^T P^T : A = V^T from the V tile (transposing reads), B = P
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const u32x4 pk = pack8<T>(s[kb], 8 * t2);
+        const int krow0 = 32 * kb + 16 * t2 + 8 * h;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+          const u32x4 a = lds_read_tr_operand<C::CPR>(vt, krow0, 32 * db, lane);
+          acc[db] = mfma32<T>(a, pk, acc[db]);
         }
       }
     }
-    if (more) lds_store_tile(stage ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue: O = acc / l written once; lse = ln(sum exp(S)) per query
@@ -260,7 +251,7 @@ hipError_t launch_fwd_t(const FwdArgs& a) {
   using C = FwdTile<D>;
   const int n_qtiles = (int)((a.N + C::BM - 1) / C::BM);
   const int ZH = (int)(a.Z * a.H);
-  const dim3 grid((unsigned)(n_qtiles * ZH));
+  const dim3 grid((unsigned)xcd_grid(ZH, n_qtiles));
   hipLaunchKernelGGL((fa_fwd_kernel<D, T, CAUSAL, OT>), grid, dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.lse,
                      (int)a.N, ZH, n_qtiles, a.scale * kLog2e);

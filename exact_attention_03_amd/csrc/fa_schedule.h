@@ -45,4 +45,21 @@ FA_SCHED_HD int64_t sched_first_qtile(int64_t key_tile, int64_t keys_per_unit,
   return causal ? (key_tile * keys_per_unit) / queries_per_tile : 0;
 }
 
+// Query-tile grids (forward and dQ passes) laid out so that the tiles of one
+// head run on one XCD, back to back, and share its L2 copy of K and V.
+// Workgroups are dealt to the XCDs round-robin by block index, so block b runs
+// on XCD b % kXcds; the s-th block of XCD x (s = b / kXcds) takes head
+// x + kXcds * (s / n_qtiles) and tile slot s % n_qtiles.  The grid is padded to
+// kXcds * ceil(ZH / kXcds) * n_qtiles blocks; a block whose head is past the
+// last one has no work.
+constexpr int64_t kXcds = 8;
+FA_SCHED_HD int64_t xcd_grid(int64_t ZH, int64_t n_qtiles) {
+  return ((ZH + kXcds - 1) / kXcds) * kXcds * n_qtiles;
+}
+FA_SCHED_HD void xcd_tile(int64_t b, int64_t n_qtiles, int64_t* head, int64_t* slot) {
+  const int64_t x = b % kXcds, s = b / kXcds;
+  *head = x + kXcds * (s / n_qtiles);
+  *slot = s % n_qtiles;
+}
+
 }  // namespace fa
