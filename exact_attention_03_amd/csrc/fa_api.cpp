@@ -307,11 +307,8 @@ int fa_dkdv_schedule(int64_t Z, int64_t H, int64_t N, int64_t D, int causal, int
   if (n_units) *n_units = U;
   for (int64_t p = 0; p < num_programs; ++p) {
     int64_t units = 0, work = 0;
-    for (int64_t r = 0;; ++r) {
-      const int64_t u = fa::sched_unit(r, p, num_programs);
-      if (u >= U) break;
-      int64_t kt, head;
-      fa::sched_decode(u, ZH, &kt, &head);
+    int64_t head = 0, kt = 0;
+    for (int64_t r = 0; fa::sched_unit(r, p, num_programs, ZH, n_kt, &head, &kt); ++r) {
       ++units;
       work += n_qt - fa::sched_first_qtile(kt, bk, bq, causal);
     }

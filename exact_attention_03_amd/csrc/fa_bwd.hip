@@ -66,12 +66,14 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const void* __restrict_
 
 // ============================================================ dK / dV pass
 // A persistent workgroup of 4 waves owns a unit = (head, 128-key tile); wave w
-// owns keys kt0 + 32w .. +31 and keeps their K and V rows in registers, with
-// its dK and dV tiles as fp32 accumulators.  Query tiles of 64 rows (Q, dO and
-// their lse/Delta values) stream through a two-stage LDS ring.  Per 32-query
-// block the wave computes
+// owns keys kw0 = k0 + 32w .. kw0+31, keeps their K rows in registers (and
+// their V rows too at D = 64; at D >= 128 the unit's V rows stay in LDS, which
+// frees the registers for two workgroups per compute unit at D = 128), and
+// accumulates its dK and dV rows in fp32 registers.  Query tiles of 32 rows (Q, dO, lse, Delta) stream through a
+// two-stage LDS ring filled by direct global -> LDS copies.  Per query tile
+// the wave computes
 //     S  = Q K^T        (A = Q rows from LDS, B = K from registers)
-//     dP = dO V^T       (A = dO rows from LDS, B = V from registers)
+//     dP = dO V^T       (A = dO rows from LDS, B = V)
 //     P  = exp2(S c - lse2),  dS = P (dP - Delta)
 //     dV^T += dO^T P    (A = dO^T by transposing LDS reads, B = P)
 //     dK^T += Q^T dS    (A = Q^T by transposing LDS reads, B = dS)
@@ -80,41 +82,47 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const void* __restrict_
 template <int D>
 struct DkdvTile {
   static constexpr int NW = 4;
-  static constexpr int BK = kDkdvKeys;          // keys per unit (32 per wave)
+  static constexpr int BK = kDkdvKeys;           // keys per unit (32 per wave)
   static constexpr int BQ = dkdv_queries(D);     // queries per staged tile
+  static_assert(BQ == 32, "one 32-query MFMA block per stage");
   static constexpr int CPR = D / 8;
-  static constexpr int TILE_BYTES = BQ * D * 2;
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES + 2 * BQ * 4;  // Q, dO, lse2, Delta
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr bool V_LDS = D >= 128;        // V rows in LDS instead of registers
+  static constexpr int QT_BYTES = BQ * D * 2;    // one Q (or dO) tile
+  static constexpr int STAT_OFF = 2 * QT_BYTES;  // 64 lse values, then 64 Delta values
+  static constexpr int STAGE_BYTES = 2 * QT_BYTES + 512;
+  static constexpr int V_OFF = 2 * STAGE_BYTES;
+  static constexpr int V_BYTES = V_LDS ? BK * D * 2 : 0;
+  static constexpr int LDS_BYTES = V_OFF + V_BYTES;
   static constexpr int KSTEPS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int CPT = BQ * CPR / (NW * 64);  // chunks per thread per tile
-  static_assert(CPT * NW * 64 == BQ * CPR, "tile must split evenly over the threads");
+  static constexpr int QDMA = QT_BYTES / (NW * 1024);  // 1 KiB copies per wave per tile
+  static constexpr int VDMA = V_BYTES / (NW * 1024);
+  static_assert(QDMA * NW * 1024 == QT_BYTES, "tile must split into 1 KiB copies per wave");
   static_assert(BK == NW * 32, "one 32-key block per wave");
+  static constexpr int OCC = D == 256 ? 1 : 2;    // waves per SIMD the registers are sized for
+  static constexpr int SB = 4;                     // k steps per scheduling group of S / dP
 };
 
 template <int D, typename T, bool CAUSAL>
-__global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int N, int ZH, int n_ktiles, int n_qtiles,
-    float c2, float scale, int P) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkdvTile<D>::OCC, DkdvTile<D>::OCC)))
+void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                        const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                        const float* __restrict__ lse, const float* __restrict__ delta, uint16_t* __restrict__ dk,
+                        uint16_t* __restrict__ dv, int N, int ZH, int n_ktiles, int n_qtiles, float c2, float scale,
+                        int P) {
   using C = DkdvTile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int h = lane >> 5;
   const int l32 = lane & 31;
-  const int64_t n_units = (int64_t)ZH * n_ktiles;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
 
   for (int64_t round = 0;; ++round) {
-    const int64_t u = sched_unit(round, blockIdx.x, P);
-    if (u >= n_units) break;  // uniform across the workgroup
-    int64_t kt64, head64;
-    sched_decode(u, ZH, &kt64, &head64);
+    int64_t head64, kt64;
+    if (!sched_unit(round, blockIdx.x, P, ZH, n_ktiles, &head64, &kt64)) break;  // uniform
     const int kt = (int)kt64, head = (int)head64;
     const int k0 = kt * C::BK;
     const int kw0 = k0 + 32 * w;  // first key of this wave
@@ -125,14 +133,49 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(
     const auto rdo = make_rsrc(dout + hoff, head_bytes);
     const auto rl = make_rsrc(lse + (size_t)head * N, (uint32_t)N * 4);
     const auto rd = make_rsrc(delta + (size_t)head * N, (uint32_t)N * 4);
+    const int i0 = (int)sched_first_qtile(kt, C::BK, C::BQ, CAUSAL);
+    const int nq = n_qtiles - i0;
 
-    // K and V rows of this wave's keys, B-operand layout (lane = key, k = d).
-    u32x4 kf[C::KSTEPS], vf[C::KSTEPS];
+    // Copy query tile i (Q, dO, and the lse / Delta values from its first
+    // query on) into ring stage st.
+    auto issue_qtile = [&](int i, int st) {
+      char* base = smem + st * C::STAGE_BYTES;
+      const int qq0 = i * C::BQ;
+#pragma unroll
+      for (int x = 0; x < C::QDMA; ++x) {
+        const int blk = w * C::QDMA + x;
+        const int sl = blk * 64 + lane;
+        const int row = sl / C::CPR, pos = sl % C::CPR;
+        const uint32_t off = (uint32_t)(((qq0 + row) * D + 8 * (pos ^ swz<C::CPR>(row))) * 2);
+        dma16(rq, base + blk * 1024, off);
+        dma16(rdo, base + C::QT_BYTES + blk * 1024, off);
+      }
+      if (w == 0) dma4(rl, base + C::STAT_OFF, (uint32_t)(qq0 + lane) * 4);
+      if (w == 1) dma4(rd, base + C::STAT_OFF + 256, (uint32_t)(qq0 + lane) * 4);
+    };
+
+    // Every wave is done with the previous unit's LDS before it is refilled.
+    __syncthreads();
+    if constexpr (C::V_LDS) {
+#pragma unroll
+      for (int x = 0; x < C::VDMA; ++x) {
+        const int blk = w * C::VDMA + x;
+        const int sl = blk * 64 + lane;
+        const int row = sl / C::CPR, pos = sl % C::CPR;
+        dma16(rv, smem + C::V_OFF + blk * 1024,
+              (uint32_t)(((k0 + row) * D + 8 * (pos ^ swz<C::CPR>(row))) * 2));
+      }
+    }
+    issue_qtile(i0, 0);
+
+    // K (and V) rows of this wave's keys, B-operand layout (lane = key, k = d).
+    u32x4 kf[C::KSTEPS];
+    u32x4 vf[C::V_LDS ? 1 : C::KSTEPS];
 #pragma unroll
     for (int t = 0; t < C::KSTEPS; ++t) {
       const uint32_t off = (uint32_t)(((kw0 + l32) * D + 16 * t + 8 * h) * 2);
       kf[t] = gload16(rk, off);
-      vf[t] = gload16(rv, off);
+      if constexpr (!C::V_LDS) vf[t] = gload16(rv, off);
     }
     f32x16 dka[C::DB], dva[C::DB];
 #pragma unroll
@@ -140,102 +183,65 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(
       dka[db] = f32x16{};
       dva[db] = f32x16{};
     }
+    const int key = kw0 + l32;
 
-    const int i0 = (int)sched_first_qtile(kt, C::BK, C::BQ, CAUSAL);
-    u32x4 qst[C::CPT], dost[C::CPT];
-    float lst = 0.f, dst = 0.f;
-    auto gload_tile = [&](int i) {
-      const int qq0 = i * C::BQ;
+    for (int it = 0; it < nq; ++it) {
+      // Tile it has landed for every wave; every wave is done with tile it-1.
+      wait_vmem();
+      __syncthreads();
+      if (it + 1 < nq) issue_qtile(i0 + it + 1, (it + 1) & 1);
+      const int qb0 = (i0 + it) * C::BQ;  // first query of the tile
+      // Causal: a tile whose last query precedes the wave's first key is empty.
+      if (CAUSAL && qb0 + 31 < kw0) continue;
+      const char* qt = smem + (it & 1) * C::STAGE_BYTES;
+      const char* dot = qt + C::QT_BYTES;
+      const float* stats = reinterpret_cast<const float*>(qt + C::STAT_OFF);
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int x = 0; x < C::CPT; ++x) {
-        const int uu = tid + 256 * x;
-        const int row = uu / C::CPR, c = uu % C::CPR;
-        const uint32_t off = (uint32_t)(((qq0 + row) * D + 8 * c) * 2);
-        qst[x] = gload16(rq, off);
-        dost[x] = gload16(rdo, off);
+      for (int t = 0; t < C::KSTEPS; ++t) {
+        // Bound how far ahead the operand reads are hoisted (register budget).
+        if (t % C::SB == 0) __builtin_amdgcn_sched_barrier(0);
+        const int off = tile_off<C::CPR>(sigma32(l32), 16 * t + 8 * h);
+        s = mfma32<T>(lds_read16(qt, off), kf[t], s);
+        u32x4 vb;
+        if constexpr (C::V_LDS)
+          vb = lds_read16(smem + C::V_OFF, tile_off<C::CPR>(32 * w + l32, 16 * t + 8 * h));
+        else
+          vb = vf[t];
+        dp = mfma32<T>(lds_read16(dot, off), vb, dp);
       }
-      if (tid < C::BQ) {
-        lst = gload_f32(rl, (uint32_t)(qq0 + tid) * 4) * kLog2e;
-        dst = gload_f32(rd, (uint32_t)(qq0 + tid) * 4);
-      }
-    };
-    auto lds_store_tile = [&](int stage) {
-      char* base = smem + stage * C::STAGE_BYTES;
+      // Register jj holds query qb0 + 16(jj/8) + 8h + jj%8 for key kw0 + l32.
+      // Each half (t2) of the registers is finished and fed to the dV / dK
+      // products before the next, which keeps fewer values live.
+      const bool need_mask = (CAUSAL && qb0 < kw0 + 31) || (qb0 + 32 > N);
 #pragma unroll
-      for (int x = 0; x < C::CPT; ++x) {
-        const int uu = tid + 256 * x;
-        const int row = uu / C::CPR, c = uu % C::CPR;
-        const int off = tile_off<C::CPR>(row, 8 * c);
-        lds_write16(base, off, qst[x]);
-        lds_write16(base + C::TILE_BYTES, off, dost[x]);
-      }
-      if (tid < C::BQ) {
-        float* st = reinterpret_cast<float*>(base + 2 * C::TILE_BYTES);
-        st[tid] = lst;
-        st[C::BQ + tid] = dst;
-      }
-    };
-
-    gload_tile(i0);
-    lds_store_tile(0);
-    __syncthreads();
-    for (int i = i0; i < n_qtiles; ++i) {
-      const int stage = (i - i0) & 1;
-      const bool more = i + 1 < n_qtiles;
-      if (more) gload_tile(i + 1);
-      const char* qt = smem + stage * C::STAGE_BYTES;
-      const char* dot = qt + C::TILE_BYTES;
-      const float* lst_l = reinterpret_cast<const float*>(qt + 2 * C::TILE_BYTES);
-      const float* dst_l = lst_l + C::BQ;
-      const int qq0 = i * C::BQ;
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int qi = 16 * t2 + 8 * h;
+        const f32x4 la = *reinterpret_cast<const f32x4*>(stats + qi);
+        const f32x4 lb = *reinterpret_cast<const f32x4*>(stats + qi + 4);
+        const f32x4 da = *reinterpret_cast<const f32x4*>(stats + 64 + qi);
+        const f32x4 dbv = *reinterpret_cast<const f32x4*>(stats + 64 + qi + 4);
 #pragma unroll
-      for (int qb = 0; qb < C::BQ / 32; ++qb) {
-        const int qb0 = qq0 + 32 * qb;  // first query of the block
-        // Causal: a block whose last query precedes the wave's first key is empty.
-        if (CAUSAL && qb0 + 31 < kw0) continue;
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int t = 0; t < C::KSTEPS; ++t) {
-          const int off = tile_off<C::CPR>(32 * qb + sigma32(l32), 16 * t + 8 * h);
-          s = mfma32<T>(lds_read16(qt, off), kf[t], s);
-          dp = mfma32<T>(lds_read16(dot, off), vf[t], dp);
-        }
-        // Register jj holds query qb0 + 16(jj/8) + 8h + jj%8 for key kw0 + l32.
-        f32x4 lv[4], dv4[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int qi = 32 * qb + 16 * (x >> 1) + 8 * h + 4 * (x & 1);
-          lv[x] = *reinterpret_cast<const f32x4*>(lst_l + qi);
-          dv4[x] = *reinterpret_cast<const f32x4*>(dst_l + qi);
-        }
-        const int key = kw0 + l32;
-        const bool need_mask = (CAUSAL && qb0 < kw0 + 31) || (qb0 + 32 > N);
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-          const float l2 = lv[jj >> 2][jj & 3];
-          const float dl = dv4[jj >> 2][jj & 3];
+        for (int i = 0; i < 8; ++i) {
+          const int jj = 8 * t2 + i;
+          const float l2 = (i < 4 ? la[i & 3] : lb[i & 3]) * kLog2e;
+          const float dl = i < 4 ? da[i & 3] : dbv[i & 3];
           float p = fast_exp2(__builtin_fmaf(s[jj], c2, -l2));
           if (need_mask) {
-            const int query = qb0 + 16 * (jj >> 3) + 8 * h + (jj & 7);
+            const int query = qb0 + qi + i;
             if ((CAUSAL && key > query) || query >= N) p = 0.f;
           }
           s[jj] = p;
           dp[jj] = p * (dp[jj] - dl);
         }
+        const u32x4 pf = pack8<T>(s, 8 * t2);
+        const u32x4 dsf = pack8<T>(dp, 8 * t2);
 #pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const u32x4 pf = pack8<T>(s, 8 * t2);
-          const u32x4 dsf = pack8<T>(dp, 8 * t2);
-          const int krow0 = 32 * qb + 16 * t2 + 8 * h;
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db) {
-            dva[db] = mfma32<T>(lds_read_tr_operand<C::CPR>(dot, krow0, 32 * db, lane), pf, dva[db]);
-            dka[db] = mfma32<T>(lds_read_tr_operand<C::CPR>(qt, krow0, 32 * db, lane), dsf, dka[db]);
-          }
+        for (int db = 0; db < C::DB; ++db) {
+          dva[db] = mfma32<T>(lds_read_tr_operand<C::CPR>(dot, qi, 32 * db, lane), pf, dva[db]);
+          dka[db] = mfma32<T>(lds_read_tr_operand<C::CPR>(qt, qi, 32 * db, lane), dsf, dka[db]);
         }
       }
-      if (more) lds_store_tile(stage ^ 1);
-      __syncthreads();
     }
 
     // Single write of this wave's dK and dV rows.  Register jj of block db
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(
       const f32x16 ks = dka[db] * scale;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const uint32_t off = (uint32_t)(((kw0 + l32) * D + 32 * db + 16 * half + 8 * h) * 2);
+        const uint32_t off = (uint32_t)((key * D + 32 * db + 16 * half + 8 * h) * 2);
         gstore16(rdk, off, pack8<T>(ks, 8 * half));
         gstore16(rdv, off, pack8<T>(dva[db], 8 * half));
       }
@@ -257,45 +263,50 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(
 
 // ============================================================ dQ pass
 // One workgroup of 4 waves owns 128 queries of one head (32 per wave, kept in
-// registers together with their dO rows, lse and Delta) and streams K/V tiles
-// through a two-stage LDS ring.  Per key tile the wave computes, transposed so
+// registers together with their dO rows, lse and Delta); two workgroups share
+// a compute unit.  K/V tiles stream through a two-stage LDS ring filled by
+// direct global -> LDS copies.  Per key tile the wave computes, transposed so
 // that each lane owns one query,
 //     S^T  = K Q^T,  dP^T = V dO^T          (A = K/V rows from LDS)
 //     P^T  = exp2(S^T c - lse2),  dS^T = P^T (dP^T - Delta)
 //     dQ^T += K^T dS^T                      (A = K^T by transposing LDS reads)
+// The query tiles of one head run back to back on one XCD.
 template <int D>
 struct DqTile {
   static constexpr int NW = 4;
   static constexpr int BM = NW * 32;
-  static constexpr int KB = D == 256 ? 1 : 2;
-  static constexpr int BN = 32 * KB;
+  static constexpr int BN = D == 64 ? 64 : 32;
+  static constexpr int KB = BN / 32;
   static constexpr int CPR = D / 8;
   static constexpr int TILE_BYTES = BN * D * 2;
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
   static constexpr int KSTEPS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int CPT = BN * CPR / (NW * 64);
-  static_assert(CPT * NW * 64 == BN * CPR, "tile must split evenly over the threads");
+  static constexpr int DMA = TILE_BYTES / (NW * 1024);
+  static_assert(DMA * NW * 1024 == TILE_BYTES, "tile must split into 1 KiB copies per wave");
+  static constexpr int OCC = D == 256 ? 1 : 2;
 };
 
 template <int D, typename T, bool CAUSAL>
-__global__ __launch_bounds__(256) void fa_bwd_dq_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    uint16_t* __restrict__ dq, int N, int ZH, int n_qtiles, float c2, float scale) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqTile<D>::OCC, DqTile<D>::OCC)))
+void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                      const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                      const float* __restrict__ lse, const float* __restrict__ delta, uint16_t* __restrict__ dq,
+                      int N, int ZH, int n_qtiles, float c2, float scale) {
   using C = DqTile<D>;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int h = lane >> 5;
   const int l32 = lane & 31;
-  const int bid = blockIdx.x;
-  const int tq = bid / ZH;
-  const int head = bid - tq * ZH;
-  const int qt = CAUSAL ? (n_qtiles - 1 - tq) : tq;
+  int64_t head64, slot64;
+  xcd_tile(blockIdx.x, n_qtiles, &head64, &slot64);
+  if (head64 >= ZH) return;  // padding block
+  const int head = (int)head64;
+  const int qt = CAUSAL ? (n_qtiles - 1 - (int)slot64) : (int)slot64;
   const int q0 = qt * C::BM;
   const int wq0 = q0 + 32 * w;
   const int query = wq0 + l32;
@@ -305,6 +316,25 @@ __global__ __launch_bounds__(256) void fa_bwd_dq_kernel(
   const auto rk = make_rsrc(k + hoff, head_bytes);
   const auto rv = make_rsrc(v + hoff, head_bytes);
   const auto rdo = make_rsrc(dout + hoff, head_bytes);
+
+  const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
+  const int nt = (kv_end + C::BN - 1) / C::BN;
+
+  auto issue_tile = [&](int j, int st) {
+    char* kdst = smem + st * C::STAGE_BYTES;
+    char* vdst = kdst + C::TILE_BYTES;
+    const int kv0 = j * C::BN;
+#pragma unroll
+    for (int i = 0; i < C::DMA; ++i) {
+      const int blk = w * C::DMA + i;
+      const int sl = blk * 64 + lane;
+      const int row = sl / C::CPR, pos = sl % C::CPR;
+      const uint32_t off = (uint32_t)(((kv0 + row) * D + 8 * (pos ^ swz<C::CPR>(row))) * 2);
+      dma16(rk, kdst + blk * 1024, off);
+      dma16(rv, vdst + blk * 1024, off);
+    }
+  };
+  issue_tile(0, 0);
 
   u32x4 qf[C::KSTEPS], dof[C::KSTEPS];
 #pragma unroll
@@ -316,88 +346,54 @@ __global__ __launch_bounds__(256) void fa_bwd_dq_kernel(
   const float l2 = gload_f32(make_rsrc(lse + (size_t)head * N, (uint32_t)N * 4), (uint32_t)query * 4) * kLog2e;
   const float dl = gload_f32(make_rsrc(delta + (size_t)head * N, (uint32_t)N * 4), (uint32_t)query * 4);
 
-  const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
-  const int nt = (kv_end + C::BN - 1) / C::BN;
-
-  u32x4 kst[C::CPT], vst[C::CPT];
-  auto gload_tile = [&](int j) {
-    const int kv0 = j * C::BN;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int u = tid + 256 * i;
-      const int row = u / C::CPR, c = u % C::CPR;
-      const uint32_t off = (uint32_t)(((kv0 + row) * D + 8 * c) * 2);
-      kst[i] = gload16(rk, off);
-      vst[i] = gload16(rv, off);
-    }
-  };
-  auto lds_store_tile = [&](int stage) {
-    char* kt = smem + stage * C::STAGE_BYTES;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int u = tid + 256 * i;
-      const int row = u / C::CPR, c = u % C::CPR;
-      const int off = tile_off<C::CPR>(row, 8 * c);
-      lds_write16(kt, off, kst[i]);
-      lds_write16(kt + C::TILE_BYTES, off, vst[i]);
-    }
-  };
-
   f32x16 dqa[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) dqa[db] = f32x16{};
 
-  gload_tile(0);
-  lds_store_tile(0);
-  __syncthreads();
   for (int j = 0; j < nt; ++j) {
-    const int stage = j & 1;
-    const bool more = j + 1 < nt;
-    if (more) gload_tile(j + 1);
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < nt) issue_tile(j + 1, (j + 1) & 1);
     const int kv0 = j * C::BN;
-    const bool active = !CAUSAL || kv0 <= wq0 + 31;
-    if (active) {
-      const char* kt = smem + stage * C::STAGE_BYTES;
-      const char* vt = kt + C::TILE_BYTES;
-      f32x16 s[C::KB], dp[C::KB];
+    if (CAUSAL && kv0 > wq0 + 31) continue;
+    const char* kt = smem + (j & 1) * C::STAGE_BYTES;
+    const char* vt = kt + C::TILE_BYTES;
+    f32x16 s[C::KB], dp[C::KB];
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+    }
+#pragma unroll
+    for (int t = 0; t < C::KSTEPS; ++t)
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
-        s[kb] = f32x16{};
-        dp[kb] = f32x16{};
+        const int off = tile_off<C::CPR>(32 * kb + sigma32(l32), 16 * t + 8 * h);
+        s[kb] = mfma32<T>(lds_read16(kt, off), qf[t], s[kb]);
+        dp[kb] = mfma32<T>(lds_read16(vt, off), dof[t], dp[kb]);
+      }
+    const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > wq0) || (kv0 + C::BN > N);
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        float p = fast_exp2(__builtin_fmaf(s[kb][jj], c2, -l2));
+        if (need_mask) {
+          const int key = kv0 + 32 * kb + 16 * (jj >> 3) + 8 * h + (jj & 7);
+          if ((CAUSAL && key > query) || key >= N) p = 0.f;
+        }
+        dp[kb][jj] = p * (dp[kb][jj] - dl);
       }
 #pragma unroll
-      for (int t = 0; t < C::KSTEPS; ++t)
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-          const int off = tile_off<C::CPR>(32 * kb + sigma32(l32), 16 * t + 8 * h);
-          s[kb] = mfma32<T>(lds_read16(kt, off), qf[t], s[kb]);
-          dp[kb] = mfma32<T>(lds_read16(vt, off), dof[t], dp[kb]);
-        }
-      const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > wq0) || (kv0 + C::BN > N);
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const u32x4 dsf = pack8<T>(dp[kb], 8 * t2);
+        const int krow0 = 32 * kb + 16 * t2 + 8 * h;
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-          float p = fast_exp2(__builtin_fmaf(s[kb][jj], c2, -l2));
-          if (need_mask) {
-            const int key = kv0 + 32 * kb + 16 * (jj >> 3) + 8 * h + (jj & 7);
-            if ((CAUSAL && key > query) || key >= N) p = 0.f;
-          }
-          dp[kb][jj] = p * (dp[kb][jj] - dl);
-        }
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) {
-          const u32x4 dsf = pack8<T>(dp[kb], 8 * t2);
-          const int krow0 = 32 * kb + 16 * t2 + 8 * h;
-#pragma unroll
-          for (int db = 0; db < C::DB; ++db)
-            dqa[db] = mfma32<T>(lds_read_tr_operand<C::CPR>(kt, krow0, 32 * db, lane), dsf, dqa[db]);
-        }
-    }
-    if (more) lds_store_tile(stage ^ 1);
-    __syncthreads();
+        for (int db = 0; db < C::DB; ++db)
+          dqa[db] = mfma32<T>(lds_read_tr_operand<C::CPR>(kt, krow0, 32 * db, lane), dsf, dqa[db]);
+      }
   }
 
   const auto rdq = make_rsrc(dq + hoff, head_bytes);
@@ -490,7 +486,7 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
   using C = DqTile<D>;
   const int ZH = (int)(a.Z * a.H);
   const int n_qt = (int)((a.N + C::BM - 1) / C::BM);
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, T, CAUSAL>), dim3((unsigned)(n_qt * ZH)), dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, T, CAUSAL>), dim3((unsigned)xcd_grid(ZH, n_qt)), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, (int)a.N, ZH, n_qt,
                      a.scale * kLog2e, a.scale);

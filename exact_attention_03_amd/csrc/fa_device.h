@@ -169,6 +169,10 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 FA_DEV void dma16(__amdgpu_buffer_rsrc_t r, char* lds_base, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 16, voff, 0, 0, 0);
 }
+// The same with 4 bytes per lane: lane l's dword lands at lds_base + 4 l.
+FA_DEV void dma4(__amdgpu_buffer_rsrc_t r, char* lds_base, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 4, voff, 0, 0, 0);
+}
 // Wait until every global load of this wave (including LDS copies) is done.
 FA_DEV void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

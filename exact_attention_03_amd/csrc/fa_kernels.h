@@ -44,6 +44,6 @@ constexpr int fwd_keys(int D) { return D == 64 ? 128 : (D == 128 ? 64 : 32); }
 
 // Keys per dK/dV work unit and queries per staged tile of the dK/dV kernel.
 constexpr int kDkdvKeys = 128;
-constexpr int dkdv_queries(int D) { return D == 256 ? 32 : 64; }
+constexpr int dkdv_queries(int /*D*/) { return 32; }
 
 }  // namespace fa

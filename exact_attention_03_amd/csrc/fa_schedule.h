@@ -1,17 +1,27 @@
-// fa_schedule.h - static schedule of the persistent dK/dV kernel.
+// fa_schedule.h - work layout of the kernels: the static schedule of the
+// persistent dK/dV pass and the XCD-aware grid of the query-tile passes.
 //
 // [FA-Ascend] (the page "把 FlashAttention 搬上昇腾：Triton-Ascend CV Pipeline
 // 优化实战", BiumBiu) §五 runs as many programs as the chip has matrix cores
 // and lets each program claim heads with a fixed stride, so that one program
 // writes each gradient tile once and no atomics or cross-program reductions
 // are needed.  Here the unit of work is (head, key tile) and the grid is the
-// number of workgroups the GPU keeps resident.  Units are numbered so that, with
-// the causal mask, cost never increases with the unit index (key tile j of
-// every head comes before key tile j+1, and an earlier key tile sees more query
-// tiles); they are then dealt to the P programs in snake order (round r hands
-// units rP .. rP+P-1 to programs 0..P-1 on even rounds and P-1..0 on odd
-// rounds), which balances the causal triangle.  Without the mask all units
-// cost the same and the snake reduces to a fixed stride, as on the page.
+// number of workgroups the GPU keeps resident.
+//
+// XCD groups.  Workgroups are dealt to the 8 XCDs round-robin by block index,
+// and each XCD has its own L2.  When the program count is a multiple of 8 (and
+// there are at least 8 heads), program p belongs to group g = p % 8, which owns
+// heads g, g+8, g+16, ...; otherwise there is one group owning every head.  A
+// group lists its units head-major (all key tiles of a head, in order, then
+// the next head), so the programs of one XCD work on a few heads at a time and
+// share their Q and dO through L2.
+//
+// Dealing.  Round r hands the group's units rS .. rS+S-1 to its S programs,
+// in order on even rounds and in reverse on odd rounds ("snake").  With the
+// causal mask a unit's cost falls with its key tile; when S is a multiple of
+// the key tiles per head, the snake pairs key tile j with key tile n-1-j and
+// every program gets the same work.  Without the mask all units cost the
+// same, and with one key tile per head the dealing is the page's fixed stride.
 //
 // Pure integer code, usable on the host (tests, planning) and on the device.
 #pragma once
@@ -26,16 +36,25 @@
 
 namespace fa {
 
-// Unit handed to program p in round r (may be >= the unit count: then the
-// program has no unit in that round and every later round).
-FA_SCHED_HD int64_t sched_unit(int64_t round, int64_t p, int64_t P) {
-  return round * P + ((round & 1) ? (P - 1 - p) : p);
+constexpr int64_t kXcds = 8;
+
+// Number of XCD groups for P programs over ZH heads.
+FA_SCHED_HD int64_t sched_groups(int64_t P, int64_t ZH) {
+  return (P % kXcds == 0 && ZH >= kXcds) ? kXcds : 1;
 }
 
-// Unit index -> (key tile, head).
-FA_SCHED_HD void sched_decode(int64_t u, int64_t ZH, int64_t* key_tile, int64_t* head) {
-  *key_tile = u / ZH;
-  *head = u - (*key_tile) * ZH;
+// Unit of program p in round r: returns false when p has no unit in round r,
+// and then none in any later round.
+FA_SCHED_HD bool sched_unit(int64_t r, int64_t p, int64_t P, int64_t ZH, int64_t n_ktiles,
+                            int64_t* head, int64_t* key_tile) {
+  const int64_t G = sched_groups(P, ZH);
+  const int64_t g = p % G, s = p / G, S = P / G;
+  const int64_t heads_g = (ZH - g + G - 1) / G;  // heads g, g+G, ... below ZH
+  const int64_t i = r * S + ((r & 1) ? (S - 1 - s) : s);
+  if (i >= heads_g * n_ktiles) return false;
+  *head = g + G * (i / n_ktiles);
+  *key_tile = i % n_ktiles;
+  return true;
 }
 
 // Query tiles a unit visits: all of them, or with the causal mask those from
@@ -52,7 +71,6 @@ FA_SCHED_HD int64_t sched_first_qtile(int64_t key_tile, int64_t keys_per_unit,
 // x + kXcds * (s / n_qtiles) and tile slot s % n_qtiles.  The grid is padded to
 // kXcds * ceil(ZH / kXcds) * n_qtiles blocks; a block whose head is past the
 // last one has no work.
-constexpr int64_t kXcds = 8;
 FA_SCHED_HD int64_t xcd_grid(int64_t ZH, int64_t n_qtiles) {
   return ((ZH + kXcds - 1) / kXcds) * kXcds * n_qtiles;
 }

@@ -125,7 +125,7 @@ def test_persistent_dealing_matches_page(fa):
 def test_schedule_covers_units_and_balances(fa, Z, H, N, D, causal, Pn):
     units, work, n = fa.dkdv_schedule(Z, H, N, D, causal, Pn)
     assert sum(units) == n == Z * H * ((N + 127) // 128)
-    bq = 32 if D == 256 else 64
+    bq = 32
     nq = (N + bq - 1) // bq
     total = sum(nq - ((kt * 128) // bq if causal else 0) for kt in range((N + 127) // 128)) * Z * H
     assert sum(work) == total
