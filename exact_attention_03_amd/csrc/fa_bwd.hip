@@ -85,7 +85,6 @@ struct DkdvTile {
   static constexpr int BK = kDkdvKeys;           // keys per unit (32 per wave)
   static constexpr int BQ = dkdv_queries(D);     // queries per staged tile
   static_assert(BQ == 32, "one 32-query MFMA block per stage");
-  static constexpr int CPR = D / 8;
   static constexpr bool V_LDS = D >= 128;        // V rows in LDS instead of registers
   static constexpr int QT_BYTES = BQ * D * 2;    // one Q (or dO) tile
   static constexpr int STAT_OFF = 2 * QT_BYTES;  // 64 lse values, then 64 Delta values
@@ -100,7 +99,6 @@ struct DkdvTile {
   static_assert(QDMA * NW * 1024 == QT_BYTES, "tile must split into 1 KiB copies per wave");
   static_assert(BK == NW * 32, "one 32-key block per wave");
   static constexpr int OCC = D == 256 ? 1 : 2;    // waves per SIMD the registers are sized for
-  static constexpr int SB = 4;                     // k steps per scheduling group of S / dP
 };
 
 template <int D, typename T, bool CAUSAL>
@@ -111,6 +109,8 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
                         uint16_t* __restrict__ dv, int N, int ZH, int n_ktiles, int n_qtiles, float c2, float scale,
                         int P) {
   using C = DkdvTile<D>;
+  using QTile = CmTile<C::BQ>;
+  using VTile = CmTile<C::BK>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -145,8 +145,8 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
       for (int x = 0; x < C::QDMA; ++x) {
         const int blk = w * C::QDMA + x;
         const int sl = blk * 64 + lane;
-        const int row = sl / C::CPR, pos = sl % C::CPR;
-        const uint32_t off = (uint32_t)(((qq0 + row) * D + 8 * (pos ^ swz<C::CPR>(row))) * 2);
+        const int row = QTile::slot_row(sl), chunk = QTile::slot_chunk(sl);
+        const uint32_t off = (uint32_t)(((qq0 + row) * D + 8 * chunk) * 2);
         dma16(rq, base + blk * 1024, off);
         dma16(rdo, base + C::QT_BYTES + blk * 1024, off);
       }
@@ -161,9 +161,8 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
       for (int x = 0; x < C::VDMA; ++x) {
         const int blk = w * C::VDMA + x;
         const int sl = blk * 64 + lane;
-        const int row = sl / C::CPR, pos = sl % C::CPR;
-        dma16(rv, smem + C::V_OFF + blk * 1024,
-              (uint32_t)(((k0 + row) * D + 8 * (pos ^ swz<C::CPR>(row))) * 2));
+        const int row = VTile::slot_row(sl), chunk = VTile::slot_chunk(sl);
+        dma16(rv, smem + C::V_OFF + blk * 1024, (uint32_t)(((k0 + row) * D + 8 * chunk) * 2));
       }
     }
     issue_qtile(i0, 0);
@@ -184,6 +183,12 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
       dva[db] = f32x16{};
     }
     const int key = kw0 + l32;
+    // Per-lane LDS read bases: Q / dO rows sigma(l32) as A operands, this
+    // wave's V rows as the B operand, Q^T / dO^T through transposing reads.
+    const RowRead<C::BQ> qrd(sigma32(l32), h);
+    const RowRead<C::BK> vrd(l32, h);
+    const char* vbase = smem + C::V_OFF + kRowBlockBytes * w;
+    const TrRead<C::BQ> trd(lane);
 
     for (int it = 0; it < nq; ++it) {
       // Tile it has landed for every wave; every wave is done with tile it-1.
@@ -199,13 +204,11 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int t = 0; t < C::KSTEPS; ++t) {
-        // Bound how far ahead the operand reads are hoisted (register budget).
-        if (t % C::SB == 0) __builtin_amdgcn_sched_barrier(0);
-        const int off = tile_off<C::CPR>(sigma32(l32), 16 * t + 8 * h);
+        const int off = qrd.at(t);
         s = mfma32<T>(lds_read16(qt, off), kf[t], s);
         u32x4 vb;
         if constexpr (C::V_LDS)
-          vb = lds_read16(smem + C::V_OFF, tile_off<C::CPR>(32 * w + l32, 16 * t + 8 * h));
+          vb = lds_read16(vbase, vrd.at(t));
         else
           vb = vf[t];
         dp = mfma32<T>(lds_read16(dot, off), vb, dp);
@@ -229,7 +232,7 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
           float p = fast_exp2(__builtin_fmaf(s[jj], c2, -l2));
           if (need_mask) {
             const int query = qb0 + qi + i;
-            if ((CAUSAL && key > query) || query >= N) p = 0.f;
+            p = ((CAUSAL && key > query) || query >= N) ? 0.f : p;
           }
           s[jj] = p;
           dp[jj] = p * (dp[jj] - dl);
@@ -238,8 +241,8 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
         const u32x4 dsf = pack8<T>(dp, 8 * t2);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          dva[db] = mfma32<T>(lds_read_tr_operand<C::CPR>(dot, qi, 32 * db, lane), pf, dva[db]);
-          dka[db] = mfma32<T>(lds_read_tr_operand<C::CPR>(qt, qi, 32 * db, lane), dsf, dka[db]);
+          dva[db] = mfma32<T>(lds_read_tr_operand<C::BQ>(dot, trd, 16 * t2, db), pf, dva[db]);
+          dka[db] = mfma32<T>(lds_read_tr_operand<C::BQ>(qt, trd, 16 * t2, db), dsf, dka[db]);
         }
       }
     }
@@ -277,7 +280,6 @@ struct DqTile {
   static constexpr int BM = NW * 32;
   static constexpr int BN = D == 64 ? 64 : 32;
   static constexpr int KB = BN / 32;
-  static constexpr int CPR = D / 8;
   static constexpr int TILE_BYTES = BN * D * 2;
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
@@ -295,6 +297,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       const float* __restrict__ lse, const float* __restrict__ delta, uint16_t* __restrict__ dq,
                       int N, int ZH, int n_qtiles, float c2, float scale) {
   using C = DqTile<D>;
+  using Tile = CmTile<C::BN>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -328,8 +331,8 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     for (int i = 0; i < C::DMA; ++i) {
       const int blk = w * C::DMA + i;
       const int sl = blk * 64 + lane;
-      const int row = sl / C::CPR, pos = sl % C::CPR;
-      const uint32_t off = (uint32_t)(((kv0 + row) * D + 8 * (pos ^ swz<C::CPR>(row))) * 2);
+      const int row = Tile::slot_row(sl), chunk = Tile::slot_chunk(sl);
+      const uint32_t off = (uint32_t)(((kv0 + row) * D + 8 * chunk) * 2);
       dma16(rk, kdst + blk * 1024, off);
       dma16(rv, vdst + blk * 1024, off);
     }
@@ -345,6 +348,11 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   }
   const float l2 = gload_f32(make_rsrc(lse + (size_t)head * N, (uint32_t)N * 4), (uint32_t)query * 4) * kLog2e;
   const float dl = gload_f32(make_rsrc(delta + (size_t)head * N, (uint32_t)N * 4), (uint32_t)query * 4);
+
+  // Per-lane LDS read bases: K / V rows 32 kb + sigma(l32) as A operands,
+  // K^T through transposing reads.
+  const RowRead<C::BN> krd(sigma32(l32), h);
+  const TrRead<C::BN> trd(lane);
 
   f32x16 dqa[C::DB];
 #pragma unroll
@@ -368,7 +376,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     for (int t = 0; t < C::KSTEPS; ++t)
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
-        const int off = tile_off<C::CPR>(32 * kb + sigma32(l32), 16 * t + 8 * h);
+        const int off = krd.at(t) + kRowBlockBytes * kb;
         s[kb] = mfma32<T>(lds_read16(kt, off), qf[t], s[kb]);
         dp[kb] = mfma32<T>(lds_read16(vt, off), dof[t], dp[kb]);
       }
@@ -380,7 +388,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         float p = fast_exp2(__builtin_fmaf(s[kb][jj], c2, -l2));
         if (need_mask) {
           const int key = kv0 + 32 * kb + 16 * (jj >> 3) + 8 * h + (jj & 7);
-          if ((CAUSAL && key > query) || key >= N) p = 0.f;
+          p = ((CAUSAL && key > query) || key >= N) ? 0.f : p;
         }
         dp[kb][jj] = p * (dp[kb][jj] - dl);
       }
@@ -389,10 +397,9 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const u32x4 dsf = pack8<T>(dp[kb], 8 * t2);
-        const int krow0 = 32 * kb + 16 * t2 + 8 * h;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
-          dqa[db] = mfma32<T>(lds_read_tr_operand<C::CPR>(kt, krow0, 32 * db, lane), dsf, dqa[db]);
+          dqa[db] = mfma32<T>(lds_read_tr_operand<C::BN>(kt, trd, 32 * kb + 16 * t2, db), dsf, dqa[db]);
       }
   }
 

@@ -177,34 +177,48 @@ FA_DEV void dma4(__amdgpu_buffer_rsrc_t r, char* lds_base, uint32_t voff) {
 FA_DEV void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ----------------------------------------------------------------- LDS tiles
-// A tile is `rows` x D 16-bit elements stored row-major in LDS, in 16-byte
-// chunks (CPR = D/8 chunks per row).  Chunk c of row r sits at chunk position
-// c ^ swz(r).  The XOR keeps both access patterns free of bank conflicts:
-//  * plain 16-byte reads of one chunk column by 16 lanes whose rows are a
-//    permutation of 16 consecutive rows, and
-//  * transposed reads, where 16 lanes read 4 consecutive rows x 32 bytes.
-template <int CPR>
-FA_HD int swz(int row) {
-  if constexpr (CPR >= 16) {
-    return ((row & 7) << 1) | ((row >> 3) & 1);
-  } else {
-    static_assert(CPR == 8, "rows of 64 or more elements");
-    return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+// A tile of R rows x D 16-bit elements (D a multiple of 32) is stored in LDS
+// as D/32 column groups; group G holds chunks 4G .. 4G+3 (16 bytes = 8
+// elements each) of every row, 64 bytes per row, rows in order, and inside a
+// row chunk 4G + j sits at position j ^ ((row / 4) % 4).
+//  * 16-byte reads of one chunk by 16 lanes whose rows are a permutation of an
+//    aligned block of 16 rows: row % 4 picks the 64-byte quarter of the
+//    256-byte bank window and (row / 4) % 4 the 16-byte position in it, so the
+//    16 reads hit each bank once.
+//  * transposing 8-byte reads, where 32 lanes read 4 consecutive rows x the 4
+//    chunks of one group: 4 rows x 64 bytes, each bank once.
+//  * the swizzle only depends on bits 2-3 of the row, which the loops never
+//    vary, so every address the matrix loops need is one of two per-lane bases
+//    plus a compile-time offset: the loops do no address arithmetic.
+//  * global -> LDS copies fill the slots in order: a 1 KiB copy covers 16 rows
+//    x 64 contiguous bytes of the source.
+template <int R>
+struct CmTile {
+  static_assert(R % 16 == 0, "tiles are whole 16-row blocks");
+  static constexpr int GB = R * 64;  // bytes per group of 4 chunks
+  FA_HD static int swz(int row) { return (row >> 2) & 3; }
+  FA_HD static int off(int row, int chunk) {
+    return (chunk >> 2) * GB + row * 64 + (((chunk & 3) ^ swz(row)) << 4);
   }
-}
-
-// Byte offset of element (row, col) in a swizzled tile; col % 4 == 0 keeps an
-// 8-byte access inside one chunk.
-template <int CPR>
-FA_HD int tile_off(int row, int col) {
-  const int c = col >> 3;
-  return row * (CPR * 16) + ((c ^ swz<CPR>(row)) << 4) + ((col & 7) << 1);
-}
+  // Slot s (the 16 bytes at 16 s) holds (slot_row(s), slot_chunk(s)).
+  FA_HD static int slot_row(int s) { return (s >> 2) % R; }
+  FA_HD static int slot_chunk(int s) { return 4 * (s / (4 * R)) + ((s & 3) ^ swz(slot_row(s))); }
+};
 
 FA_DEV u32x4 lds_read16(const char* base, int off) {
   return *reinterpret_cast<const u32x4*>(base + off);
 }
-FA_DEV void lds_write16(char* base, int off, u32x4 v) { *reinterpret_cast<u32x4*>(base + off) = v; }
+
+// 16-byte operand reads of row `row` at k step t (chunk 2t + h):
+// at(t) = base[t % 2] + (t / 2) GB.  Rows 32 b + row of other 32-row blocks
+// are 2048 b bytes further on.
+template <int R>
+struct RowRead {
+  int b0, b1;
+  FA_DEV RowRead(int row, int h) : b0(CmTile<R>::off(row, h)), b1(CmTile<R>::off(row, 2 + h)) {}
+  FA_DEV int at(int t) const { return ((t & 1) ? b1 : b0) + (t >> 1) * CmTile<R>::GB; }
+};
+constexpr int kRowBlockBytes = 32 * 64;  // one 32-row block of a tile
 
 // Transposed 8-byte LDS read (ds_read_b64_tr_b16).  Within each group of 16
 // lanes, lane i receives element (i%4) of the 8-byte chunks fetched by lanes
@@ -214,18 +228,31 @@ FA_DEV u32x2 lds_read_tr(const char* base, int off) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// MFMA operand of 8 consecutive k (rows krow0..krow0+7 of the tile) for column
-// n of a 32-column block starting at col0, where the 32 operand lanes take the
-// tile columns in sigma order:  lane l receives T[krow0 + i][col0 + sigma(l%32)]
-// for i = 0..7.  `krow0` may differ between the two lane halves.
-template <int CPR>
-FA_DEV u32x4 lds_read_tr_operand(const char* tile, int krow0, int col0, int lane) {
-  const int g = lane >> 4;     // group of 16 lanes
-  const int r = (lane & 15) >> 2;
-  const int c = lane & 3;
-  const int col = col0 + 16 * (g & 1) + 4 * swap01(c);
-  const u32x2 lo = lds_read_tr(tile, tile_off<CPR>(krow0 + r, col));
-  const u32x2 hi = lds_read_tr(tile, tile_off<CPR>(krow0 + 4 + r, col));
+// Per-lane bases of the transposing operand reads below.  Lane (g = group of
+// 16, r = (lane % 16) / 4, c = lane % 4) fetches 4 elements of row
+// 8h + r (and 8h + 4 + r) at column 16 (g % 2) + 4 swap01(c) of a 32-column
+// block.
+template <int R>
+struct TrRead {
+  int lo, hi;
+  FA_DEV explicit TrRead(int lane) {
+    const int g = lane >> 4, h = lane >> 5, r = (lane & 15) >> 2, c = swap01(lane & 3);
+    const int x = 2 * (g & 1) + (c >> 1);  // chunk within the 32-column block
+    const int e = 4 * (c & 1);              // first element within the chunk
+    lo = CmTile<R>::off(8 * h + r, x) + 2 * e;
+    hi = CmTile<R>::off(8 * h + 4 + r, x) + 2 * e;
+  }
+};
+
+// MFMA operand of 8 consecutive k (tile rows k0 + 8h .. k0 + 8h + 7 for lane
+// half h; k0 a multiple of 16) for the 32-column block db, where the 32 operand
+// lanes take the columns in sigma order: lane l receives
+// T[k0 + 8h + i][32 db + sigma(l % 32)] for i = 0..7.
+template <int R>
+FA_DEV u32x4 lds_read_tr_operand(const char* tile, const TrRead<R>& b, int k0, int db) {
+  const int o = k0 * 64 + db * CmTile<R>::GB;
+  const u32x2 lo = lds_read_tr(tile, b.lo + o);
+  const u32x2 hi = lds_read_tr(tile, b.hi + o);
   return u32x4{lo.x, lo.y, hi.x, hi.y};
 }
 

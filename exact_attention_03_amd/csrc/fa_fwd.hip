@@ -23,7 +23,9 @@
 //     query (a column of the MFMA result) and its softmax statistics are
 //     per-lane values; a row max needs one exchange between lane halves;
 //   * the output is accumulated transposed as well, O^T = V^T P^T, with V^T
-//     read straight from the row-major V tile by transposing LDS reads;
+//     read straight from the V tile by transposing LDS reads;
+//   * LDS tiles are chunk-major (see CmTile), so all LDS addresses in the loop
+//     are per-lane bases plus compile-time offsets;
 //   * the query tiles of one head are dispatched back to back on one XCD so
 //     that the head's K and V are read from HBM about once.
 // Refinement over the page's rescale-on-every-new-max (fp16 only): the running
@@ -47,7 +49,6 @@ struct FwdTile {
   static constexpr int BN = fwd_keys(D);                     // keys per tile
   static constexpr int KB = BN / 32;                         // 32-key blocks per tile
   static_assert(BM == NW * 32, "32 queries per wave");
-  static constexpr int CPR = D / 8;                          // 16-byte chunks per row
   static constexpr int TILE_BYTES = BN * D * 2;
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;         // K tile, then V tile
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES;          // two-stage ring
@@ -69,6 +70,7 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                    const uint16_t* __restrict__ v, void* __restrict__ o, float* __restrict__ lse, int N,
                    int ZH, int n_qtiles, float c2) {
   using C = FwdTile<D>;
+  using Tile = CmTile<C::BN>;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
@@ -94,8 +96,7 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
   const int nt = (kv_end + C::BN - 1) / C::BN;
 
-  // Copy K/V tile j into ring stage st.  LDS slot sl (16 bytes) of a tile holds
-  // row sl / CPR, chunk (sl % CPR) ^ swz(row): the swizzled layout of tile_off.
+  // Copy K/V tile j into ring stage st (chunk-major layout, see CmTile).
   auto issue_tile = [&](int j, int st) {
     char* kdst = smem + st * C::STAGE_BYTES;
     char* vdst = kdst + C::TILE_BYTES;
@@ -104,8 +105,8 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     for (int i = 0; i < C::DMA; ++i) {
       const int blk = w * C::DMA + i;
       const int sl = blk * 64 + lane;
-      const int row = sl / C::CPR, pos = sl % C::CPR;
-      const uint32_t off = (uint32_t)(((kv0 + row) * D + 8 * (pos ^ swz<C::CPR>(row))) * 2);
+      const int row = Tile::slot_row(sl), chunk = Tile::slot_chunk(sl);
+      const uint32_t off = (uint32_t)(((kv0 + row) * D + 8 * chunk) * 2);
       dma16(rk, kdst + blk * 1024, off);
       dma16(rv, vdst + blk * 1024, off);
     }
@@ -117,6 +118,11 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
   for (int t = 0; t < C::KSTEPS; ++t)
     qf[t] = gload16(rq, (uint32_t)(((wq0 + l32) * D + 16 * t + 8 * h) * 2));
+
+  // Per-lane LDS read bases: K rows 32 kb + sigma(l32) as the A operand of
+  // the score product, V^T through transposing reads.
+  const RowRead<C::BN> krd(sigma32(l32), h);
+  const TrRead<C::BN> vrd(lane);
 
   float m_run = -1e30f;  // running max, exp2 units
   float l_run = 0.f;     // running denominator (this lane half's keys)
@@ -144,7 +150,7 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     for (int t = 0; t < C::KSTEPS; ++t) {
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) {
-        const u32x4 a = lds_read16(kt, tile_off<C::CPR>(32 * kb + sigma32(l32), 16 * t + 8 * h));
+        const u32x4 a = lds_read16(kt, krd.at(t) + kRowBlockBytes * kb);
         s[kb] = mfma32<T>(a, qf[t], s[kb]);
       }
     }
@@ -157,7 +163,7 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
           const int key = kv0 + 32 * kb + 16 * (jj >> 3) + 8 * h + (jj & 7);
-          if ((CAUSAL && key > query) || key >= N) s[kb][jj] = -INFINITY;
+          s[kb][jj] = ((CAUSAL && key > query) || key >= N) ? -INFINITY : s[kb][jj];
         }
     }
     // ---- online softmax, exp2 units
@@ -193,10 +199,9 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const u32x4 pk = pack8<T>(s[kb], 8 * t2);
-        const int krow0 = 32 * kb + 16 * t2 + 8 * h;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) {
-          const u32x4 a = lds_read_tr_operand<C::CPR>(vt, krow0, 32 * db, lane);
+          const u32x4 a = lds_read_tr_operand<C::BN>(vt, vrd, 32 * kb + 16 * t2, db);
           acc[db] = mfma32<T>(a, pk, acc[db]);
         }
       }
