@@ -266,8 +266,8 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
 
 // ============================================================ dQ pass
 // One workgroup of 4 waves owns 128 queries of one head (32 per wave, kept in
-// registers together with their dO rows, lse and Delta); two workgroups share
-// a compute unit.  K/V tiles stream through a two-stage LDS ring filled by
+// registers together with their dO rows, lse and Delta); two (D = 128) or
+// three (D = 64) workgroups share a compute unit.  K/V tiles stream through a two-stage LDS ring filled by
 // direct global -> LDS copies.  Per key tile the wave computes, transposed so
 // that each lane owns one query,
 //     S^T  = K Q^T,  dP^T = V dO^T          (A = K/V rows from LDS)
@@ -287,7 +287,7 @@ struct DqTile {
   static constexpr int DB = D / 32;
   static constexpr int DMA = TILE_BYTES / (NW * 1024);
   static_assert(DMA * NW * 1024 == TILE_BYTES, "tile must split into 1 KiB copies per wave");
-  static constexpr int OCC = D == 256 ? 1 : 2;
+  static constexpr int OCC = D == 256 ? 1 : (D == 128 ? 2 : 3);  // waves per SIMD (registers)
 };
 
 template <int D, typename T, bool CAUSAL>

@@ -13,9 +13,9 @@
 //   * one workgroup = 4 waves = one Q tile of BM = 128 queries of one head;
 //     wave w owns 32 consecutive queries and keeps them in registers as the
 //     B operand of the score MFMA for the whole kernel;
-//   * two workgroups share a compute unit (at most 256 registers per lane and
-//     64 KiB of LDS each), so one wave's softmax arithmetic overlaps the other
-//     wave's matrix instructions on the same SIMD;
+//   * several workgroups share a compute unit (3 at D = 128, 4 at D = 64, with
+//     registers and LDS sized for that), so one wave's softmax arithmetic and
+//     memory waits overlap other waves' matrix instructions on the same SIMD;
 //   * K/V tiles of BN keys are copied global -> LDS by the buffer unit itself
 //     (no register staging) into a two-stage ring: the copy of tile j+1 is in
 //     flight while tile j is consumed, with one barrier per tile;
@@ -56,8 +56,10 @@ struct FwdTile {
   static constexpr int DB = D / 32;                          // 32-wide d blocks of O
   static constexpr int DMA = TILE_BYTES / (NW * 1024);       // 1 KiB copies per wave per tile
   static_assert(DMA * NW * 1024 == TILE_BYTES, "tile must split into 1 KiB copies per wave");
-  // Waves per SIMD the register budget is sized for.
-  static constexpr int OCC = D == 256 ? 1 : 2;
+  // Waves per SIMD the register budget is sized for (measured best: more
+  // resident waves hide the latency of each wave's chain of copy wait, LDS
+  // reads, matrix products and softmax).
+  static constexpr int OCC = D == 256 ? 1 : (D == 128 ? 3 : 4);
 };
 
 // Rescale threshold in exp2 units (see file comment).

@@ -40,7 +40,7 @@ hipError_t dkdv_blocks_per_cu(int D, int dtype, int* out);
 
 // Queries per forward workgroup and keys per forward K/V tile.
 constexpr int kFwdQueries = 128;
-constexpr int fwd_keys(int D) { return D == 64 ? 128 : (D == 128 ? 64 : 32); }
+constexpr int fwd_keys(int D) { return D == 64 ? 64 : 32; }
 
 // Keys per dK/dV work unit and queries per staged tile of the dK/dV kernel.
 constexpr int kDkdvKeys = 128;
