@@ -97,15 +97,17 @@ def test_stage_argument_errors(fa):
 
 def test_causal_tile_count_matches_page(fa):
     g = _golden("causal_tile_count.txt")
-    # At D=64 the forward uses 128 x 128 tiles, so N = 8 * 128 is the page's 8 x 8 grid.
-    vis, tot = fa.fwd_tile_pairs(8 * 128, 64, True)
-    assert (vis, tot) == (g["causal_tiles"], g["full_tiles"])
-    assert 100.0 * (1 - vis / tot) == pytest.approx(g["saved_percent"])
-    assert fa.fwd_tile_pairs(8 * 128, 64, False) == (g["full_tiles"], g["full_tiles"])
-    # other head dims use narrower key tiles; the saved fraction is the same
-    for D in (128, 256):
+    # The forward's query tiles are 128 rows, so N = 8 * 128 is the page's grid
+    # of 8 query tiles.  Its key tiles are narrower (128 / r keys), so every
+    # cell of the page's 8 x 8 grid is r key tiles: the visited count is the
+    # page's 36 of 64, scaled by r, for every head dim.
+    for D in (64, 128, 256):
         vis, tot = fa.fwd_tile_pairs(8 * 128, D, True)
-        assert 1 - vis / tot == pytest.approx(g["saved_percent"] / 100)
+        r = tot // g["full_tiles"]
+        assert r * g["full_tiles"] == tot
+        assert (vis, tot) == (r * g["causal_tiles"], r * g["full_tiles"])
+        assert 100.0 * (1 - vis / tot) == pytest.approx(g["saved_percent"])
+        assert fa.fwd_tile_pairs(8 * 128, D, False) == (tot, tot)
 
 
 def test_persistent_dealing_matches_page(fa):
