@@ -50,8 +50,6 @@ struct FwdTile {
   static constexpr int KB = BN / 32;                         // 32-key blocks per tile
   static_assert(BM == NW * 32, "32 queries per wave");
   static constexpr int TILE_BYTES = BN * D * 2;
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;         // K tile, then V tile
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;          // two-stage ring
   static constexpr int KSTEPS = D / 16;                      // k steps of the score MFMA
   static constexpr int DB = D / 32;                          // 32-wide d blocks of O
   static constexpr int DMA = TILE_BYTES / (NW * 1024);       // 1 KiB copies per wave per tile
@@ -73,7 +71,14 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                    int ZH, int n_qtiles, float c2) {
   using C = FwdTile<D>;
   using Tile = CmTile<C::BN>;
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  // One LDS object per ring stage and operand.  With the stage of every
+  // access known at compile time (the loop below handles tiles in pairs), the
+  // compiler can tell that the copy of tile j+1 does not alias the reads of
+  // tile j and need not make those reads wait for it.
+  __shared__ __attribute__((aligned(1024))) char k0s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v0s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k1s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v1s[C::TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -98,10 +103,8 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
   const int nt = (kv_end + C::BN - 1) / C::BN;
 
-  // Copy K/V tile j into ring stage st (chunk-major layout, see CmTile).
-  auto issue_tile = [&](int j, int st) {
-    char* kdst = smem + st * C::STAGE_BYTES;
-    char* vdst = kdst + C::TILE_BYTES;
+  // Copy K/V tile j into a ring stage (chunk-major layout, see CmTile).
+  auto issue_tile = [&](int j, char* kdst, char* vdst) {
     const int kv0 = j * C::BN;
 #pragma unroll
     for (int i = 0; i < C::DMA; ++i) {
@@ -113,7 +116,7 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       dma16(rv, vdst + blk * 1024, off);
     }
   };
-  issue_tile(0, 0);
+  issue_tile(0, k0s, v0s);
 
   // Q tile -> registers, B-operand layout: lane owns query wq0 + l32, k = d.
   u32x4 qf[C::KSTEPS];
@@ -132,18 +135,17 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
 
-  for (int j = 0; j < nt; ++j) {
+  // Tile j, read from kt/vt; the copy of tile j+1 goes to kn/vn.
+  auto tile = [&](int j, const char* kt, const char* vt, char* kn, char* vn) {
     // Tile j has landed for every wave, and every wave is done with tile j-1,
     // whose stage the copy of tile j+1 now overwrites.
     wait_vmem();
     __syncthreads();
-    if (j + 1 < nt) issue_tile(j + 1, (j + 1) & 1);
+    if (j + 1 < nt) issue_tile(j + 1, kn, vn);
     const int kv0 = j * C::BN;
     // With the causal mask a wave whose last query precedes the tile skips it.
     const bool active = !CAUSAL || kv0 <= wq0 + 31;
-    if (!active) continue;
-    const char* kt = smem + (j & 1) * C::STAGE_BYTES;
-    const char* vt = kt + C::TILE_BYTES;
+    if (!active) return;
     // ---- S^T = K Q^T : rows = keys (sigma order), columns = this wave's queries
     f32x16 s[C::KB];
 #pragma unroll
@@ -208,6 +210,10 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         }
       }
     }
+  };
+  for (int j = 0; j < nt; j += 2) {
+    tile(j, k0s, v0s, k1s, v1s);
+    if (j + 1 < nt) tile(j + 1, k1s, v1s, k0s, v0s);
   }
 
   // ---- epilogue: O = acc / l written once; lse = ln(sum exp(S)) per query
