@@ -89,9 +89,7 @@ struct DkdvTile {
   static constexpr int QT_BYTES = BQ * D * 2;    // one Q (or dO) tile
   static constexpr int STAT_OFF = 2 * QT_BYTES;  // 64 lse values, then 64 Delta values
   static constexpr int STAGE_BYTES = 2 * QT_BYTES + 512;
-  static constexpr int V_OFF = 2 * STAGE_BYTES;
   static constexpr int V_BYTES = V_LDS ? BK * D * 2 : 0;
-  static constexpr int LDS_BYTES = V_OFF + V_BYTES;
   static constexpr int KSTEPS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int QDMA = QT_BYTES / (NW * 1024);  // 1 KiB copies per wave per tile
@@ -99,6 +97,10 @@ struct DkdvTile {
   static_assert(QDMA * NW * 1024 == QT_BYTES, "tile must split into 1 KiB copies per wave");
   static_assert(BK == NW * 32, "one 32-key block per wave");
   static constexpr int OCC = D == 256 ? 1 : 2;    // waves per SIMD the registers are sized for
+  // Query tiles handled in pairs with compile-time ring stages (see the LDS
+  // declarations).  At D = 256 the doubled loop body costs more registers
+  // than the stage-aliasing waits it removes.
+  static constexpr bool PAIRS = D <= 128;
 };
 
 template <int D, typename T, bool CAUSAL>
@@ -111,7 +113,13 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   using C = DkdvTile<D>;
   using QTile = CmTile<C::BQ>;
   using VTile = CmTile<C::BK>;
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  // One LDS object per ring stage (Q tile, dO tile, lse and Delta) and one
+  // for the unit's V rows, accessed with compile-time stages (query tiles in
+  // pairs), so that the copy of the next query tile provably does not alias
+  // the reads of the current one and does not hold them up.
+  __shared__ __attribute__((aligned(1024))) char st0[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char st1[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vsm[C::V_LDS ? C::V_BYTES : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -138,8 +146,7 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
 
     // Copy query tile i (Q, dO, and the lse / Delta values from its first
     // query on) into ring stage st.
-    auto issue_qtile = [&](int i, int st) {
-      char* base = smem + st * C::STAGE_BYTES;
+    auto issue_qtile = [&](int i, char* base) {
       const int qq0 = i * C::BQ;
 #pragma unroll
       for (int x = 0; x < C::QDMA; ++x) {
@@ -162,10 +169,10 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
         const int blk = w * C::VDMA + x;
         const int sl = blk * 64 + lane;
         const int row = VTile::slot_row(sl), chunk = VTile::slot_chunk(sl);
-        dma16(rv, smem + C::V_OFF + blk * 1024, (uint32_t)(((k0 + row) * D + 8 * chunk) * 2));
+        dma16(rv, vsm + blk * 1024, (uint32_t)(((k0 + row) * D + 8 * chunk) * 2));
       }
     }
-    issue_qtile(i0, 0);
+    issue_qtile(i0, st0);
 
     // K (and V) rows of this wave's keys, B-operand layout (lane = key, k = d).
     u32x4 kf[C::KSTEPS];
@@ -187,18 +194,19 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     // wave's V rows as the B operand, Q^T / dO^T through transposing reads.
     const RowRead<C::BQ> qrd(sigma32(l32), h);
     const RowRead<C::BK> vrd(l32, h);
-    const char* vbase = smem + C::V_OFF + kRowBlockBytes * w;
+    const char* vbase = vsm + kRowBlockBytes * w;
     const TrRead<C::BQ> trd(lane);
 
-    for (int it = 0; it < nq; ++it) {
+    // Query tile it, read from stage cs; the copy of tile it+1 goes to ns.
+    auto qtile = [&](int it, const char* cs, char* ns) {
       // Tile it has landed for every wave; every wave is done with tile it-1.
       wait_vmem();
       __syncthreads();
-      if (it + 1 < nq) issue_qtile(i0 + it + 1, (it + 1) & 1);
+      if (it + 1 < nq) issue_qtile(i0 + it + 1, ns);
       const int qb0 = (i0 + it) * C::BQ;  // first query of the tile
       // Causal: a tile whose last query precedes the wave's first key is empty.
-      if (CAUSAL && qb0 + 31 < kw0) continue;
-      const char* qt = smem + (it & 1) * C::STAGE_BYTES;
+      if (CAUSAL && qb0 + 31 < kw0) return;
+      const char* qt = cs;
       const char* dot = qt + C::QT_BYTES;
       const float* stats = reinterpret_cast<const float*>(qt + C::STAT_OFF);
       f32x16 s = f32x16{}, dp = f32x16{};
@@ -245,6 +253,14 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
           dka[db] = mfma32<T>(lds_read_tr_operand<C::BQ>(qt, trd, 16 * t2, db), dsf, dka[db]);
         }
       }
+    };
+    if constexpr (C::PAIRS) {
+      for (int it = 0; it < nq; it += 2) {
+        qtile(it, st0, st1);
+        if (it + 1 < nq) qtile(it + 1, st1, st0);
+      }
+    } else {
+      for (int it = 0; it < nq; ++it) qtile(it, (it & 1) ? st1 : st0, (it & 1) ? st0 : st1);
     }
 
     // Single write of this wave's dK and dV rows.  Register jj of block db
@@ -281,13 +297,13 @@ struct DqTile {
   static constexpr int BN = D == 64 ? 64 : 32;
   static constexpr int KB = BN / 32;
   static constexpr int TILE_BYTES = BN * D * 2;
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
   static constexpr int KSTEPS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int DMA = TILE_BYTES / (NW * 1024);
   static_assert(DMA * NW * 1024 == TILE_BYTES, "tile must split into 1 KiB copies per wave");
   static constexpr int OCC = D == 256 ? 1 : (D == 128 ? 2 : 3);  // waves per SIMD (registers)
+  // Key tiles in pairs with compile-time ring stages (as in the dK/dV pass).
+  static constexpr bool PAIRS = D <= 128;
 };
 
 template <int D, typename T, bool CAUSAL>
@@ -298,7 +314,13 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       int N, int ZH, int n_qtiles, float c2, float scale) {
   using C = DqTile<D>;
   using Tile = CmTile<C::BN>;
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  // One LDS object per ring stage and operand, accessed with compile-time
+  // stages (tiles in pairs), so that the copy of tile j+1 provably does not
+  // alias the reads of tile j and does not hold them up.
+  __shared__ __attribute__((aligned(1024))) char k0s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v0s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k1s[C::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v1s[C::TILE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -323,9 +345,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
   const int nt = (kv_end + C::BN - 1) / C::BN;
 
-  auto issue_tile = [&](int j, int st) {
-    char* kdst = smem + st * C::STAGE_BYTES;
-    char* vdst = kdst + C::TILE_BYTES;
+  auto issue_tile = [&](int j, char* kdst, char* vdst) {
     const int kv0 = j * C::BN;
 #pragma unroll
     for (int i = 0; i < C::DMA; ++i) {
@@ -337,7 +357,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       dma16(rv, vdst + blk * 1024, off);
     }
   };
-  issue_tile(0, 0);
+  issue_tile(0, k0s, v0s);
 
   u32x4 qf[C::KSTEPS], dof[C::KSTEPS];
 #pragma unroll
@@ -358,14 +378,13 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
   for (int db = 0; db < C::DB; ++db) dqa[db] = f32x16{};
 
-  for (int j = 0; j < nt; ++j) {
+  // Key tile j, read from kt/vt; the copy of tile j+1 goes to kn/vn.
+  auto tile = [&](int j, const char* kt, const char* vt, char* kn, char* vn) {
     wait_vmem();
     __syncthreads();
-    if (j + 1 < nt) issue_tile(j + 1, (j + 1) & 1);
+    if (j + 1 < nt) issue_tile(j + 1, kn, vn);
     const int kv0 = j * C::BN;
-    if (CAUSAL && kv0 > wq0 + 31) continue;
-    const char* kt = smem + (j & 1) * C::STAGE_BYTES;
-    const char* vt = kt + C::TILE_BYTES;
+    if (CAUSAL && kv0 > wq0 + 31) return;
     f32x16 s[C::KB], dp[C::KB];
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
@@ -401,6 +420,17 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         for (int db = 0; db < C::DB; ++db)
           dqa[db] = mfma32<T>(lds_read_tr_operand<C::BN>(kt, trd, 32 * kb + 16 * t2, db), dsf, dqa[db]);
       }
+  };
+  if constexpr (C::PAIRS) {
+    for (int j = 0; j < nt; j += 2) {
+      tile(j, k0s, v0s, k1s, v1s);
+      if (j + 1 < nt) tile(j + 1, k1s, v1s, k0s, v0s);
+    }
+  } else {
+    for (int j = 0; j < nt; ++j) {
+      const bool odd = j & 1;
+      tile(j, odd ? k1s : k0s, odd ? v1s : v0s, odd ? k0s : k1s, odd ? v0s : v1s);
+    }
   }
 
   const auto rdq = make_rsrc(dq + hoff, head_bytes);
