@@ -281,15 +281,19 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
 }
 
 // ============================================================ dQ pass
-// One workgroup of 4 waves owns 128 queries of one head (32 per wave, kept in
-// registers together with their dO rows, lse and Delta); two (D = 128) or
-// three (D = 64) workgroups share a compute unit.  K/V tiles stream through a two-stage LDS ring filled by
-// direct global -> LDS copies.  Per key tile the wave computes, transposed so
-// that each lane owns one query,
+// A workgroup of 4 waves owns a query tile of 128 queries of one head (32 per
+// wave, kept in registers together with their dO rows, lse and Delta); two
+// (D = 128) or three (D = 64) workgroups share a compute unit.  With the
+// causal mask a workgroup owns two tiles, a long and a short one, so every
+// workgroup has the same work, and finishes them one after the other; the
+// second tile's rows and first K/V tile are fetched while the first finishes.  K/V
+// tiles stream through a two-stage LDS ring filled by direct global -> LDS
+// copies.  Per key tile the wave computes, transposed so that each lane owns
+// one query,
 //     S^T  = K Q^T,  dP^T = V dO^T          (A = K/V rows from LDS)
 //     P^T  = exp2(S^T c - lse2),  dS^T = P^T (dP^T - Delta)
 //     dQ^T += K^T dS^T                      (A = K^T by transposing LDS reads)
-// The query tiles of one head run back to back on one XCD.
+// The workgroups of one head run back to back on one XCD.
 template <int D>
 struct DqTile {
   static constexpr int NW = 4;
@@ -305,6 +309,12 @@ struct DqTile {
   // Key tiles in pairs with compile-time ring stages (as in the dK/dV pass).
   static constexpr bool PAIRS = D <= 128;
 };
+
+// Workgroups per head of the dQ pass (see the kernel).
+template <bool CAUSAL>
+FA_HD int dq_groups(int n_qtiles) {
+  return CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
+}
 
 template <int D, typename T, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqTile<D>::OCC, DqTile<D>::OCC)))
@@ -327,23 +337,32 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const int w = tid >> 6;
   const int h = lane >> 5;
   const int l32 = lane & 31;
+  // With the causal mask a workgroup takes two query tiles of one head, n-1-i
+  // and i, one after the other: a long and a short one, so every workgroup
+  // has the same work (with an odd tile count the middle tile is alone).
+  // Without the mask every workgroup takes one tile.
+  const int n_groups = dq_groups<CAUSAL>(n_qtiles);
   int64_t head64, slot64;
-  xcd_tile(blockIdx.x, n_qtiles, &head64, &slot64);
+  xcd_tile(blockIdx.x, n_groups, &head64, &slot64);
   if (head64 >= ZH) return;  // padding block
   const int head = (int)head64;
-  const int qt = CAUSAL ? (n_qtiles - 1 - (int)slot64) : (int)slot64;
-  const int q0 = qt * C::BM;
-  const int wq0 = q0 + 32 * w;
-  const int query = wq0 + l32;
+  const int pr = (int)slot64;
+  const int qt_a = CAUSAL ? n_qtiles - 1 - pr : pr;
+  const int qt_b = CAUSAL ? pr : pr;
+  const int n_items = (CAUSAL && qt_b != qt_a) ? 2 : 1;
   const size_t hoff = (size_t)head * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc(q + hoff, head_bytes);
   const auto rk = make_rsrc(k + hoff, head_bytes);
   const auto rv = make_rsrc(v + hoff, head_bytes);
   const auto rdo = make_rsrc(dout + hoff, head_bytes);
-
-  const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
-  const int nt = (kv_end + C::BN - 1) / C::BN;
+  const auto rl = make_rsrc(lse + (size_t)head * N, (uint32_t)N * 4);
+  const auto rdl = make_rsrc(delta + (size_t)head * N, (uint32_t)N * 4);
+  const auto rdq = make_rsrc(dq + hoff, head_bytes);
+  auto n_tiles = [&](int qt) {
+    const int kv_end = CAUSAL ? min(N, (qt + 1) * C::BM) : N;
+    return (kv_end + C::BN - 1) / C::BN;
+  };
 
   auto issue_tile = [&](int j, char* kdst, char* vdst) {
     const int kv0 = j * C::BN;
@@ -357,89 +376,124 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       dma16(rv, vdst + blk * 1024, off);
     }
   };
-  issue_tile(0, k0s, v0s);
-
+  // The wave's query rows of tile qt: Q and dO in B-operand layout (lane =
+  // query, k = d), lse (as lse * log2 e) and Delta.
   u32x4 qf[C::KSTEPS], dof[C::KSTEPS];
+  float l2 = 0.f, dl = 0.f;
+  auto load_rows = [&](int qt) {
+    const int query = qt * C::BM + 32 * w + l32;
 #pragma unroll
-  for (int t = 0; t < C::KSTEPS; ++t) {
-    const uint32_t off = (uint32_t)((query * D + 16 * t + 8 * h) * 2);
-    qf[t] = gload16(rq, off);
-    dof[t] = gload16(rdo, off);
-  }
-  const float l2 = gload_f32(make_rsrc(lse + (size_t)head * N, (uint32_t)N * 4), (uint32_t)query * 4) * kLog2e;
-  const float dl = gload_f32(make_rsrc(delta + (size_t)head * N, (uint32_t)N * 4), (uint32_t)query * 4);
+    for (int t = 0; t < C::KSTEPS; ++t) {
+      const uint32_t off = (uint32_t)((query * D + 16 * t + 8 * h) * 2);
+      qf[t] = gload16(rq, off);
+      dof[t] = gload16(rdo, off);
+    }
+    l2 = gload_f32(rl, (uint32_t)query * 4) * kLog2e;
+    dl = gload_f32(rdl, (uint32_t)query * 4);
+  };
 
   // Per-lane LDS read bases: K / V rows 32 kb + sigma(l32) as A operands,
   // K^T through transposing reads.
   const RowRead<C::BN> krd(sigma32(l32), h);
   const TrRead<C::BN> trd(lane);
 
-  f32x16 dqa[C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) dqa[db] = f32x16{};
+  issue_tile(0, k0s, v0s);
+  load_rows(qt_a);
+  bool first_tile_issued = true;
+  for (int it = 0; it < n_items; ++it) {
+    const int qt = it == 0 ? qt_a : qt_b;
+    const int q0 = qt * C::BM;
+    const int wq0 = q0 + 32 * w;
+    const int query = wq0 + l32;
+    const int nt = n_tiles(qt);
+    const bool more = it + 1 < n_items;
+    // With an even tile count the next item's first tile follows in the
+    // same ring (it lands in stage 0): copy it, and load the next rows,
+    // during this item's last tile.
+    const bool chain = more && (nt % 2 == 0);
+    if (!first_tile_issued) issue_tile(0, k0s, v0s);
 
-  // Key tile j, read from kt/vt; the copy of tile j+1 goes to kn/vn.
-  auto tile = [&](int j, const char* kt, const char* vt, char* kn, char* vn) {
-    wait_vmem();
-    __syncthreads();
-    if (j + 1 < nt) issue_tile(j + 1, kn, vn);
-    const int kv0 = j * C::BN;
-    if (CAUSAL && kv0 > wq0 + 31) return;
-    f32x16 s[C::KB], dp[C::KB];
+    f32x16 dqa[C::DB];
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
-    }
+    for (int db = 0; db < C::DB; ++db) dqa[db] = f32x16{};
+
+    // Key tile j, read from kt/vt; the copy of tile j+1 goes to kn/vn.
+    auto tile = [&](int j, const char* kt, const char* vt, char* kn, char* vn) {
+      wait_vmem();
+      __syncthreads();
+      if (j + 1 < nt)
+        issue_tile(j + 1, kn, vn);
+      else if (chain)
+        issue_tile(0, kn, vn);
+      const int kv0 = j * C::BN;
+      const bool active = !CAUSAL || kv0 <= wq0 + 31;
+      f32x16 s[C::KB], dp[C::KB];
+      if (active) {
 #pragma unroll
-    for (int t = 0; t < C::KSTEPS; ++t)
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        const int off = krd.at(t) + kRowBlockBytes * kb;
-        s[kb] = mfma32<T>(lds_read16(kt, off), qf[t], s[kb]);
-        dp[kb] = mfma32<T>(lds_read16(vt, off), dof[t], dp[kb]);
-      }
-    const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > wq0) || (kv0 + C::BN > N);
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        float p = fast_exp2(__builtin_fmaf(s[kb][jj], c2, -l2));
-        if (need_mask) {
-          const int key = kv0 + 32 * kb + 16 * (jj >> 3) + 8 * h + (jj & 7);
-          p = ((CAUSAL && key > query) || key >= N) ? 0.f : p;
+        for (int kb = 0; kb < C::KB; ++kb) {
+          s[kb] = f32x16{};
+          dp[kb] = f32x16{};
         }
-        dp[kb][jj] = p * (dp[kb][jj] - dl);
+#pragma unroll
+        for (int t = 0; t < C::KSTEPS; ++t)
+#pragma unroll
+          for (int kb = 0; kb < C::KB; ++kb) {
+            const int off = krd.at(t) + kRowBlockBytes * kb;
+            s[kb] = mfma32<T>(lds_read16(kt, off), qf[t], s[kb]);
+            dp[kb] = mfma32<T>(lds_read16(vt, off), dof[t], dp[kb]);
+          }
       }
+      // This item's rows are not needed any more: load the next item's.
+      const float l2c = l2, dlc = dl;
+      if (j == nt - 1 && more) load_rows(qt_b);
+      if (!active) return;
+      const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > wq0) || (kv0 + C::BN > N);
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const u32x4 dsf = pack8<T>(dp[kb], 8 * t2);
+        for (int jj = 0; jj < 16; ++jj) {
+          float p = fast_exp2(__builtin_fmaf(s[kb][jj], c2, -l2c));
+          if (need_mask) {
+            const int key = kv0 + 32 * kb + 16 * (jj >> 3) + 8 * h + (jj & 7);
+            p = ((CAUSAL && key > query) || key >= N) ? 0.f : p;
+          }
+          dp[kb][jj] = p * (dp[kb][jj] - dlc);
+        }
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-          dqa[db] = mfma32<T>(lds_read_tr_operand<C::BN>(kt, trd, 32 * kb + 16 * t2, db), dsf, dqa[db]);
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const u32x4 dsf = pack8<T>(dp[kb], 8 * t2);
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db)
+            dqa[db] = mfma32<T>(lds_read_tr_operand<C::BN>(kt, trd, 32 * kb + 16 * t2, db), dsf, dqa[db]);
+        }
+    };
+    if constexpr (C::PAIRS) {
+      for (int j = 0; j < nt; j += 2) {
+        tile(j, k0s, v0s, k1s, v1s);
+        if (j + 1 < nt) tile(j + 1, k1s, v1s, k0s, v0s);
       }
-  };
-  if constexpr (C::PAIRS) {
-    for (int j = 0; j < nt; j += 2) {
-      tile(j, k0s, v0s, k1s, v1s);
-      if (j + 1 < nt) tile(j + 1, k1s, v1s, k0s, v0s);
+    } else {
+      for (int j = 0; j < nt; ++j) {
+        const bool odd = j & 1;
+        tile(j, odd ? k1s : k0s, odd ? v1s : v0s, odd ? k0s : k1s, odd ? v0s : v1s);
+      }
     }
-  } else {
-    for (int j = 0; j < nt; ++j) {
-      const bool odd = j & 1;
-      tile(j, odd ? k1s : k0s, odd ? v1s : v0s, odd ? k0s : k1s, odd ? v0s : v1s);
-    }
-  }
 
-  const auto rdq = make_rsrc(dq + hoff, head_bytes);
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db) {
-    const f32x16 y = dqa[db] * scale;
+    for (int db = 0; db < C::DB; ++db) {
+      const f32x16 y = dqa[db] * scale;
 #pragma unroll
-    for (int half = 0; half < 2; ++half)
-      gstore16(rdq, (uint32_t)((query * D + 32 * db + 16 * half + 8 * h) * 2), pack8<T>(y, 8 * half));
+      for (int half = 0; half < 2; ++half)
+        gstore16(rdq, (uint32_t)((query * D + 32 * db + 16 * half + 8 * h) * 2), pack8<T>(y, 8 * half));
+    }
+    first_tile_issued = chain;
+    if (more && !chain) {
+      // The ring restarts at stage 0 for the next item; every wave must be
+      // done with this item's last tile before it is overwritten.
+      __syncthreads();
+    }
   }
 }
 
@@ -523,7 +577,8 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
   using C = DqTile<D>;
   const int ZH = (int)(a.Z * a.H);
   const int n_qt = (int)((a.N + C::BM - 1) / C::BM);
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, T, CAUSAL>), dim3((unsigned)xcd_grid(ZH, n_qt)), dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, T, CAUSAL>), dim3((unsigned)xcd_grid(ZH, dq_groups<CAUSAL>(n_qt))),
+                     dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, (int)a.N, ZH, n_qt,
                      a.scale * kLog2e, a.scale);
