@@ -300,7 +300,7 @@ int fa_dkdv_schedule(int64_t Z, int64_t H, int64_t N, int64_t D, int causal, int
   FA_TRY(check_shape(s));
   if (causal != 0 && causal != 1) return fail(FA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1");
   if (num_programs <= 0) return fail(FA_ERR_INVALID_ARGUMENT, "num_programs must be > 0");
-  const int64_t bk = fa::kDkdvKeys, bq = fa::dkdv_queries((int)D);
+  const int64_t bk = fa::dkdv_keys((int)D), bq = fa::dkdv_queries((int)D);
   const int64_t ZH = s.heads();
   const int64_t n_kt = (N + bk - 1) / bk, n_qt = (N + bq - 1) / bq;
   const int64_t U = ZH * n_kt;

@@ -68,8 +68,8 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const void* __restrict_
 // A persistent workgroup of 4 waves owns a unit = (head, 128-key tile); wave w
 // owns keys kw0 = k0 + 32w .. kw0+31, keeps their K rows in registers (and
 // their V rows too at D = 64; at D >= 128 the unit's V rows stay in LDS, which
-// frees the registers for two workgroups per compute unit at D = 128), and
-// accumulates its dK and dV rows in fp32 registers.  Query tiles of 32 rows (Q, dO, lse, Delta) stream through a
+// frees the registers for two waves per SIMD at D = 128), and accumulates its
+// dK and dV rows in fp32 registers.  Query tiles of 32 rows (Q, dO, lse, Delta) stream through a
 // two-stage LDS ring filled by direct global -> LDS copies.  Per query tile
 // the wave computes
 //     S  = Q K^T        (A = Q rows from LDS, B = K from registers)
@@ -81,8 +81,8 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const void* __restrict_
 // out of the first two products already in the operand layout of the last two.
 template <int D>
 struct DkdvTile {
-  static constexpr int NW = 4;
-  static constexpr int BK = kDkdvKeys;           // keys per unit (32 per wave)
+  static constexpr int NW = dkdv_waves(D);       // waves per workgroup
+  static constexpr int BK = dkdv_keys(D);        // keys per unit (32 per wave)
   static constexpr int BQ = dkdv_queries(D);     // queries per staged tile
   static_assert(BQ == 32, "one 32-query MFMA block per stage");
   static constexpr bool V_LDS = D >= 128;        // V rows in LDS instead of registers
@@ -92,9 +92,13 @@ struct DkdvTile {
   static constexpr int V_BYTES = V_LDS ? BK * D * 2 : 0;
   static constexpr int KSTEPS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int QDMA = QT_BYTES / (NW * 1024);  // 1 KiB copies per wave per tile
-  static constexpr int VDMA = V_BYTES / (NW * 1024);
-  static_assert(QDMA * NW * 1024 == QT_BYTES, "tile must split into 1 KiB copies per wave");
+  static constexpr int QCOPIES = QT_BYTES / 1024;     // 1 KiB copies per Q (or dO) tile
+  static constexpr int VCOPIES = V_BYTES / 1024;      // 1 KiB copies per V tile
+  static_assert(QCOPIES * 1024 == QT_BYTES && QCOPIES % NW == 0, "tile must split into 1 KiB copies per wave");
+  static_assert(VCOPIES % NW == 0, "V tile must split into 1 KiB copies per wave");
+  // Copy loops unrolled except at D = 256, where the unrolled form costs
+  // registers the accumulators need.
+  static constexpr int COPY_UNROLL = D == 256 ? 1 : 16;
   static_assert(BK == NW * 32, "one 32-key block per wave");
   static constexpr int OCC = D == 256 ? 1 : 2;    // waves per SIMD the registers are sized for
   // Query tiles handled in pairs with compile-time ring stages (see the LDS
@@ -104,7 +108,8 @@ struct DkdvTile {
 };
 
 template <int D, typename T, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DkdvTile<D>::OCC, DkdvTile<D>::OCC)))
+__global__ __launch_bounds__(DkdvTile<D>::NW * 64)
+__attribute__((amdgpu_waves_per_eu(DkdvTile<D>::OCC, DkdvTile<D>::OCC)))
 void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                         const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                         const float* __restrict__ lse, const float* __restrict__ delta, uint16_t* __restrict__ dk,
@@ -148,9 +153,9 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     // query on) into ring stage st.
     auto issue_qtile = [&](int i, char* base) {
       const int qq0 = i * C::BQ;
-#pragma unroll
-      for (int x = 0; x < C::QDMA; ++x) {
-        const int blk = w * C::QDMA + x;
+#pragma unroll(C::COPY_UNROLL)
+      for (int x = 0; x < C::QCOPIES / C::NW; ++x) {
+        const int blk = w * (C::QCOPIES / C::NW) + x;
         const int sl = blk * 64 + lane;
         const int row = QTile::slot_row(sl), chunk = QTile::slot_chunk(sl);
         const uint32_t off = (uint32_t)(((qq0 + row) * D + 8 * chunk) * 2);
@@ -164,9 +169,9 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     // Every wave is done with the previous unit's LDS before it is refilled.
     __syncthreads();
     if constexpr (C::V_LDS) {
-#pragma unroll
-      for (int x = 0; x < C::VDMA; ++x) {
-        const int blk = w * C::VDMA + x;
+#pragma unroll(C::COPY_UNROLL)
+      for (int x = 0; x < C::VCOPIES / C::NW; ++x) {
+        const int blk = w * (C::VCOPIES / C::NW) + x;
         const int sl = blk * 64 + lane;
         const int row = VTile::slot_row(sl), chunk = VTile::slot_chunk(sl);
         dma16(rv, vsm + blk * 1024, (uint32_t)(((k0 + row) * D + 8 * chunk) * 2));
@@ -529,7 +534,7 @@ static hipError_t launch_dkdv_t(const BwdArgs& a) {
   const int ZH = (int)(a.Z * a.H);
   const int n_kt = (int)((a.N + C::BK - 1) / C::BK);
   const int n_qt = (int)((a.N + C::BQ - 1) / C::BQ);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, T, CAUSAL>), dim3((unsigned)a.num_programs), dim3(256), 0,
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, T, CAUSAL>), dim3((unsigned)a.num_programs), dim3(C::NW * 64), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, (int)a.N,
                      ZH, n_kt, n_qt, a.scale * kLog2e, a.scale, a.num_programs);
@@ -554,10 +559,11 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a) {
 template <int D, typename T>
 static hipError_t occ_dkdv(int* out) {
   int n = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fa_bwd_dkdv_kernel<D, T, true>, 256, 0);
+  constexpr int threads = DkdvTile<D>::NW * 64;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fa_bwd_dkdv_kernel<D, T, true>, threads, 0);
   if (e != hipSuccess) return e;
   int n2 = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n2, fa_bwd_dkdv_kernel<D, T, false>, 256, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n2, fa_bwd_dkdv_kernel<D, T, false>, threads, 0);
   if (e != hipSuccess) return e;
   *out = n < n2 ? n : n2;
   if (*out < 1) *out = 1;

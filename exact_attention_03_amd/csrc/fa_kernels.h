@@ -43,7 +43,9 @@ constexpr int kFwdQueries = 128;
 constexpr int fwd_keys(int D) { return D == 64 ? 64 : 32; }
 
 // Keys per dK/dV work unit and queries per staged tile of the dK/dV kernel.
-constexpr int kDkdvKeys = 128;
+// Waves per dK/dV workgroup (32 keys each) and keys per dK/dV work unit.
+constexpr int dkdv_waves(int /*D*/) { return 4; }
+constexpr int dkdv_keys(int D) { return 32 * dkdv_waves(D); }
 constexpr int dkdv_queries(int /*D*/) { return 32; }
 
 }  // namespace fa

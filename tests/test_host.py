@@ -126,10 +126,11 @@ def test_persistent_dealing_matches_page(fa):
 ])
 def test_schedule_covers_units_and_balances(fa, Z, H, N, D, causal, Pn):
     units, work, n = fa.dkdv_schedule(Z, H, N, D, causal, Pn)
-    assert sum(units) == n == Z * H * ((N + 127) // 128)
+    bk = 128  # keys per unit: 32 per wave, 4 waves
+    assert sum(units) == n == Z * H * ((N + bk - 1) // bk)
     bq = 32
     nq = (N + bq - 1) // bq
-    total = sum(nq - ((kt * 128) // bq if causal else 0) for kt in range((N + 127) // 128)) * Z * H
+    total = sum(nq - ((kt * bk) // bq if causal else 0) for kt in range((N + bk - 1) // bk)) * Z * H
     assert sum(work) == total
     if n >= 4 * Pn:
         mean = total / Pn
