@@ -215,8 +215,8 @@ FA_DEV u32x4 lds_read16(const char* base, int off) {
 template <int R>
 struct RowRead {
   int b0, b1;
-  FA_DEV RowRead(int row, int h) : b0(CmTile<R>::off(row, h)), b1(CmTile<R>::off(row, 2 + h)) {}
-  FA_DEV int at(int t) const { return ((t & 1) ? b1 : b0) + (t >> 1) * CmTile<R>::GB; }
+  FA_HD RowRead(int row, int h) : b0(CmTile<R>::off(row, h)), b1(CmTile<R>::off(row, 2 + h)) {}
+  FA_HD int at(int t) const { return ((t & 1) ? b1 : b0) + (t >> 1) * CmTile<R>::GB; }
 };
 constexpr int kRowBlockBytes = 32 * 64;  // one 32-row block of a tile
 
@@ -235,7 +235,7 @@ FA_DEV u32x2 lds_read_tr(const char* base, int off) {
 template <int R>
 struct TrRead {
   int lo, hi;
-  FA_DEV explicit TrRead(int lane) {
+  FA_HD explicit TrRead(int lane) {
     const int g = lane >> 4, h = lane >> 5, r = (lane & 15) >> 2, c = swap01(lane & 3);
     const int x = 2 * (g & 1) + (c >> 1);  // chunk within the 32-column block
     const int e = 4 * (c & 1);              // first element within the chunk
