@@ -128,7 +128,7 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = wave_id();
   const int h = lane >> 5;
   const int l32 = lane & 31;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
@@ -241,12 +241,23 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
         for (int i = 0; i < 8; ++i) {
           const int jj = 8 * t2 + i;
           const float l2 = (i < 4 ? la[i & 3] : lb[i & 3]) * kLog2e;
-          const float dl = i < 4 ? da[i & 3] : dbv[i & 3];
-          float p = fast_exp2(__builtin_fmaf(s[jj], c2, -l2));
-          if (need_mask) {
+          s[jj] = __builtin_fmaf(s[jj], c2, -l2);  // log2 of P
+        }
+        // Only the tile on the wave's diagonal and a ragged last tile are
+        // masked; the (uniform) branch keeps the selects off every other tile.
+        if (need_mask) {
+          keep_branch();
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
             const int query = qb0 + qi + i;
-            p = ((CAUSAL && key > query) || query >= N) ? 0.f : p;
+            if ((CAUSAL && key > query) || query >= N) s[8 * t2 + i] = -__builtin_inff();
           }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int jj = 8 * t2 + i;
+          const float dl = i < 4 ? da[i & 3] : dbv[i & 3];
+          const float p = fast_exp2(s[jj]);  // exp2(-inf) = 0
           s[jj] = p;
           dp[jj] = p * (dp[jj] - dl);
         }

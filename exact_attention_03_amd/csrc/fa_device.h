@@ -28,6 +28,16 @@ namespace fa {
 #define FA_DEV __device__ __forceinline__
 #define FA_HD __host__ __device__ __forceinline__
 
+// An empty statement the compiler must not execute speculatively: placed in a
+// rarely taken uniform branch it keeps the branch from being flattened into
+// per-element selects that every iteration would pay for.
+FA_DEV void keep_branch() { asm volatile("" ::: "memory"); }
+
+// Index of the calling wave in its workgroup, as a scalar: the compiler then
+// treats everything derived from it (per-wave key or query ranges, mask
+// decisions) as wave-uniform, keeping it in SGPRs and branching on it.
+FA_DEV int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));

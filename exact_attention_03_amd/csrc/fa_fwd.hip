@@ -82,7 +82,7 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = wave_id();
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
