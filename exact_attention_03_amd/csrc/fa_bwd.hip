@@ -326,12 +326,6 @@ struct DqTile {
   static constexpr bool PAIRS = D <= 128;
 };
 
-// Workgroups per head of the dQ pass (see the kernel).
-template <bool CAUSAL>
-FA_HD int dq_groups(int n_qtiles) {
-  return CAUSAL ? (n_qtiles + 1) / 2 : n_qtiles;
-}
-
 template <int D, typename T, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqTile<D>::OCC, DqTile<D>::OCC)))
 void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -351,21 +345,20 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  // The same index as a scalar, for the LDS destinations of the tile copies
+  // (kept separate from w: the divergent form gives better register use for
+  // the rest of this kernel).
+  const int ws = wave_id();
   const int h = lane >> 5;
   const int l32 = lane & 31;
-  // With the causal mask a workgroup takes two query tiles of one head, n-1-i
-  // and i, one after the other: a long and a short one, so every workgroup
-  // has the same work (with an odd tile count the middle tile is alone).
-  // Without the mask every workgroup takes one tile.
-  const int n_groups = dq_groups<CAUSAL>(n_qtiles);
-  int64_t head64, slot64;
-  xcd_tile(blockIdx.x, n_groups, &head64, &slot64);
+  // Query tiles of this workgroup: one, or with the causal mask a long and a
+  // short one of the same head.
+  int64_t head64, slot64, qt_a64, qt_b64;
+  xcd_tile(blockIdx.x, paired_groups(n_qtiles, CAUSAL), &head64, &slot64);
   if (head64 >= ZH) return;  // padding block
   const int head = (int)head64;
-  const int pr = (int)slot64;
-  const int qt_a = CAUSAL ? n_qtiles - 1 - pr : pr;
-  const int qt_b = CAUSAL ? pr : pr;
-  const int n_items = (CAUSAL && qt_b != qt_a) ? 2 : 1;
+  const int n_items = paired_items(slot64, n_qtiles, CAUSAL, &qt_a64, &qt_b64);
+  const int qt_a = (int)qt_a64, qt_b = (int)qt_b64;
   const size_t hoff = (size_t)head * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc(q + hoff, head_bytes);
@@ -384,7 +377,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     const int kv0 = j * C::BN;
 #pragma unroll
     for (int i = 0; i < C::DMA; ++i) {
-      const int blk = w * C::DMA + i;
+      const int blk = ws * C::DMA + i;
       const int sl = blk * 64 + lane;
       const int row = Tile::slot_row(sl), chunk = Tile::slot_chunk(sl);
       const uint32_t off = (uint32_t)(((kv0 + row) * D + 8 * chunk) * 2);
@@ -465,16 +458,25 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       if (!active) return;
       const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > wq0) || (kv0 + C::BN > N);
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb) {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) s[kb][jj] = __builtin_fmaf(s[kb][jj], c2, -l2c);  // log2 of P
+        // Only tiles on the wave's diagonal and a ragged last tile are
+        // masked; the (uniform) branch keeps the selects off every other tile.
+        if (need_mask) {
+          keep_branch();
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) {
+            const int key = kv0 + 32 * kb + 16 * (jj >> 3) + 8 * h + (jj & 7);
+            if ((CAUSAL && key > query) || key >= N) s[kb][jj] = -__builtin_inff();
+          }
+        }
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
-          float p = fast_exp2(__builtin_fmaf(s[kb][jj], c2, -l2c));
-          if (need_mask) {
-            const int key = kv0 + 32 * kb + 16 * (jj >> 3) + 8 * h + (jj & 7);
-            p = ((CAUSAL && key > query) || key >= N) ? 0.f : p;
-          }
+          const float p = fast_exp2(s[kb][jj]);  // exp2(-inf) = 0
           dp[kb][jj] = p * (dp[kb][jj] - dlc);
         }
+      }
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
@@ -594,7 +596,7 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
   using C = DqTile<D>;
   const int ZH = (int)(a.Z * a.H);
   const int n_qt = (int)((a.N + C::BM - 1) / C::BM);
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, T, CAUSAL>), dim3((unsigned)xcd_grid(ZH, dq_groups<CAUSAL>(n_qt))),
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, T, CAUSAL>), dim3((unsigned)xcd_grid(ZH, paired_groups(n_qt, CAUSAL))),
                      dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, (int)a.N, ZH, n_qt,

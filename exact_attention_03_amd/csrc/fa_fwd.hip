@@ -10,9 +10,12 @@
 // tile straddles the diagonal, and a single write of O.
 //
 // Work decomposition on gfx950
-//   * one workgroup = 4 waves = one Q tile of BM = 128 queries of one head;
-//     wave w owns 32 consecutive queries and keeps them in registers as the
-//     B operand of the score MFMA for the whole kernel;
+//   * one workgroup = 4 waves working on a Q tile of BM = 128 queries of one
+//     head; wave w owns 32 consecutive queries and keeps them in registers as
+//     the B operand of the score MFMA.  With the causal mask a workgroup takes
+//     two tiles of the head, a long and a short one, so every workgroup has
+//     the same work; the second tile's Q rows and first K/V tile are fetched
+//     during the first tile's last step;
 //   * several workgroups share a compute unit (3 at D = 128, 4 at D = 64, with
 //     registers and LDS sized for that), so one wave's softmax arithmetic and
 //     memory waits overlap other waves' matrix instructions on the same SIMD;
@@ -45,7 +48,7 @@ namespace fa {
 template <int D>
 struct FwdTile {
   static constexpr int NW = 4;                               // waves per workgroup
-  static constexpr int BM = kFwdQueries;                     // queries per workgroup
+  static constexpr int BM = kFwdQueries;                     // queries per tile
   static constexpr int BN = fwd_keys(D);                     // keys per tile
   static constexpr int KB = BN / 32;                         // 32-key blocks per tile
   static_assert(BM == NW * 32, "32 queries per wave");
@@ -86,22 +89,19 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  int64_t head64, slot64;
-  xcd_tile(blockIdx.x, n_qtiles, &head64, &slot64);
+  // Query tiles of this workgroup: one, or with the causal mask a long and a
+  // short one of the same head (the longest pairs go first).
+  int64_t head64, slot64, qt_a64, qt_b64;
+  xcd_tile(blockIdx.x, paired_groups(n_qtiles, CAUSAL), &head64, &slot64);
   if (head64 >= ZH) return;  // padding block
+  const int n_items = paired_items(slot64, n_qtiles, CAUSAL, &qt_a64, &qt_b64);
+  const int qt_a = (int)qt_a64, qt_b = (int)qt_b64;
   const int head = (int)head64;
-  // With the causal mask the longest tiles of a head go first.
-  const int qt = CAUSAL ? (n_qtiles - 1 - (int)slot64) : (int)slot64;
-  const int q0 = qt * C::BM;
-  const int wq0 = q0 + 32 * w;  // first query of this wave
   const size_t hoff = (size_t)head * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc(q + hoff, head_bytes);
   const auto rk = make_rsrc(k + hoff, head_bytes);
   const auto rv = make_rsrc(v + hoff, head_bytes);
-
-  const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
-  const int nt = (kv_end + C::BN - 1) / C::BN;
 
   // Copy K/V tile j into a ring stage (chunk-major layout, see CmTile).
   auto issue_tile = [&](int j, char* kdst, char* vdst) {
@@ -116,146 +116,176 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       dma16(rv, vdst + blk * 1024, off);
     }
   };
-  issue_tile(0, k0s, v0s);
-
-  // Q tile -> registers, B-operand layout: lane owns query wq0 + l32, k = d.
+  // This wave's Q rows of tile qt -> registers, B-operand layout: lane owns
+  // query qt BM + 32 w + l32, k = d.
   u32x4 qf[C::KSTEPS];
+  auto load_q = [&](int qt) {
 #pragma unroll
-  for (int t = 0; t < C::KSTEPS; ++t)
-    qf[t] = gload16(rq, (uint32_t)(((wq0 + l32) * D + 16 * t + 8 * h) * 2));
+    for (int t = 0; t < C::KSTEPS; ++t)
+      qf[t] = gload16(rq, (uint32_t)(((qt * C::BM + 32 * w + l32) * D + 16 * t + 8 * h) * 2));
+  };
 
   // Per-lane LDS read bases: K rows 32 kb + sigma(l32) as the A operand of
   // the score product, V^T through transposing reads.
   const RowRead<C::BN> krd(sigma32(l32), h);
   const TrRead<C::BN> vrd(lane);
 
-  float m_run = -1e30f;  // running max, exp2 units
-  float l_run = 0.f;     // running denominator (this lane half's keys)
-  f32x16 acc[C::DB];
-#pragma unroll
-  for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+  issue_tile(0, k0s, v0s);
+  load_q(qt_a);
+  bool first_tile_issued = true;
+  for (int it = 0; it < n_items; ++it) {
+    const int qt = it == 0 ? qt_a : qt_b;
+    const int q0 = qt * C::BM;
+    const int wq0 = q0 + 32 * w;  // first query of this wave
+    const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
+    const int nt = (kv_end + C::BN - 1) / C::BN;
+    const bool more = it + 1 < n_items;
+    // With an even tile count the next item's first tile lands in stage 0 of
+    // the ring: copy it during this item's last tile.
+    const bool chain = more && (nt % 2 == 0);
+    if (!first_tile_issued) issue_tile(0, k0s, v0s);
 
-  // Tile j, read from kt/vt; the copy of tile j+1 goes to kn/vn.
-  auto tile = [&](int j, const char* kt, const char* vt, char* kn, char* vn) {
-    // Tile j has landed for every wave, and every wave is done with tile j-1,
-    // whose stage the copy of tile j+1 now overwrites.
-    wait_vmem();
-    __syncthreads();
-    if (j + 1 < nt) issue_tile(j + 1, kn, vn);
-    const int kv0 = j * C::BN;
-    // With the causal mask a wave whose last query precedes the tile skips it.
-    const bool active = !CAUSAL || kv0 <= wq0 + 31;
-    if (!active) return;
-    // ---- S^T = K Q^T : rows = keys (sigma order), columns = this wave's queries
-    f32x16 s[C::KB];
+    float m_run = -1e30f;  // running max, exp2 units
+    float l_run = 0.f;     // running denominator (this lane half's keys)
+    f32x16 acc[C::DB];
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) s[kb] = f32x16{};
+    for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
+
+    // Tile j, read from kt/vt; the copy of tile j+1 goes to kn/vn.
+    auto tile = [&](int j, const char* kt, const char* vt, char* kn, char* vn) {
+      // Tile j has landed for every wave, and every wave is done with tile
+      // j-1, whose stage the copy of tile j+1 now overwrites.
+      wait_vmem();
+      __syncthreads();
+      if (j + 1 < nt)
+        issue_tile(j + 1, kn, vn);
+      else if (chain)
+        issue_tile(0, kn, vn);
+      const int kv0 = j * C::BN;
+      // With the causal mask a wave whose last query precedes the tile skips it.
+      const bool active = !CAUSAL || kv0 <= wq0 + 31;
+      // ---- S^T = K Q^T : rows = keys (sigma order), columns = this wave's queries
+      f32x16 s[C::KB];
+      if (active) {
 #pragma unroll
-    for (int t = 0; t < C::KSTEPS; ++t) {
+        for (int kb = 0; kb < C::KB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        const u32x4 a = lds_read16(kt, krd.at(t) + kRowBlockBytes * kb);
-        s[kb] = mfma32<T>(a, qf[t], s[kb]);
+        for (int t = 0; t < C::KSTEPS; ++t) {
+#pragma unroll
+          for (int kb = 0; kb < C::KB; ++kb) {
+            const u32x4 a = lds_read16(kt, krd.at(t) + kRowBlockBytes * kb);
+            s[kb] = mfma32<T>(a, qf[t], s[kb]);
+          }
+        }
       }
-    }
-    // ---- masks: causal diagonal tile and ragged last tile only
-    const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > wq0) || (kv0 + C::BN > N);
-    if (need_mask) {
-      const int query = wq0 + l32;
+      // The Q rows are not needed any more: load the next item's.
+      if (j == nt - 1 && more) load_q(qt_b);
+      if (!active) return;
+      // ---- masks: causal diagonal tile and ragged last tile only
+      const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > wq0) || (kv0 + C::BN > N);
+      if (need_mask) {
+        const int query = wq0 + l32;
+#pragma unroll
+        for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) {
+            const int key = kv0 + 32 * kb + 16 * (jj >> 3) + 8 * h + (jj & 7);
+            s[kb][jj] = ((CAUSAL && key > query) || key >= N) ? -INFINITY : s[kb][jj];
+          }
+      }
+      // ---- online softmax, exp2 units
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s[kb][jj]);
+      mx = half_swap_max(mx);
+      const float m_new = fmaxf(m_run, mx * c2);
+      if (wave_any(m_new > m_run + kRescaleSlack<T>)) {
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+        m_run = m_new;
+      }
+      // p = exp2(s c - m), packed to the 16-bit type for the PV product;
+      // l_run sums the fp32 p.
+      float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
-          const int key = kv0 + 32 * kb + 16 * (jj >> 3) + 8 * h + (jj & 7);
-          s[kb][jj] = ((CAUSAL && key > query) || key >= N) ? -INFINITY : s[kb][jj];
+          const float p = fast_exp2(__builtin_fmaf(s[kb][jj], c2, -m_run));
+          s[kb][jj] = p;
+          rs += p;
         }
-    }
-    // ---- online softmax, exp2 units
-    float mx = -INFINITY;
+      l_run += rs;
+      // ---- O^T += V^T P^T : A = V^T from the V tile (transposing reads), B = P
 #pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
+      for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) mx = fmaxf(mx, s[kb][jj]);
-    mx = half_swap_max(mx);
-    const float m_new = fmaxf(m_run, mx * c2);
-    if (wave_any(m_new > m_run + kRescaleSlack<T>)) {
-      const float alpha = fast_exp2(m_run - m_new);
-      l_run *= alpha;
+        for (int t2 = 0; t2 < 2; ++t2) {
+          const u32x4 pk = pack8<T>(s[kb], 8 * t2);
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
-      m_run = m_new;
-    }
-    // p = exp2(s c - m), packed to the 16-bit type for the PV product; l_run
-    // sums the fp32 p.
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const float p = fast_exp2(__builtin_fmaf(s[kb][jj], c2, -m_run));
-        s[kb][jj] = p;
-        rs += p;
-      }
-    l_run += rs;
-    // ---- O^T += V^T P^T : A = V^T from the V tile (transposing reads), B = P
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const u32x4 pk = pack8<T>(s[kb], 8 * t2);
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const u32x4 a = lds_read_tr_operand<C::BN>(vt, vrd, 32 * kb + 16 * t2, db);
-          acc[db] = mfma32<T>(a, pk, acc[db]);
+          for (int db = 0; db < C::DB; ++db) {
+            const u32x4 a = lds_read_tr_operand<C::BN>(vt, vrd, 32 * kb + 16 * t2, db);
+            acc[db] = mfma32<T>(a, pk, acc[db]);
+          }
         }
       }
+    };
+    for (int j = 0; j < nt; j += 2) {
+      tile(j, k0s, v0s, k1s, v1s);
+      if (j + 1 < nt) tile(j + 1, k1s, v1s, k0s, v0s);
     }
-  };
-  for (int j = 0; j < nt; j += 2) {
-    tile(j, k0s, v0s, k1s, v1s);
-    if (j + 1 < nt) tile(j + 1, k1s, v1s, k0s, v0s);
-  }
 
-  // ---- epilogue: O = acc / l written once; lse = ln(sum exp(S)) per query
-  const float lsum = half_swap_sum(l_run);
-  const float inv = 1.0f / lsum;
-  const int query = wq0 + l32;
-  if constexpr (sizeof(OT) == 4) {
-    const auto ro = make_rsrc((float*)o + hoff, (uint32_t)N * D * 4);
+    // ---- epilogue: O = acc / l written once; lse = ln(sum exp(S)) per query
+    const float lsum = half_swap_sum(l_run);
+    const float inv = 1.0f / lsum;
+    const int query = wq0 + l32;
+    if constexpr (sizeof(OT) == 4) {
+      const auto ro = make_rsrc((float*)o + hoff, (uint32_t)N * D * 4);
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+      for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int d = 32 * db + 16 * half + 8 * h;
-        const int j0 = 8 * half;
-        u32x4 lo, hi;
-        lo.x = __float_as_uint(acc[db][j0 + 0] * inv);
-        lo.y = __float_as_uint(acc[db][j0 + 1] * inv);
-        lo.z = __float_as_uint(acc[db][j0 + 2] * inv);
-        lo.w = __float_as_uint(acc[db][j0 + 3] * inv);
-        hi.x = __float_as_uint(acc[db][j0 + 4] * inv);
-        hi.y = __float_as_uint(acc[db][j0 + 5] * inv);
-        hi.z = __float_as_uint(acc[db][j0 + 6] * inv);
-        hi.w = __float_as_uint(acc[db][j0 + 7] * inv);
-        const uint32_t off = (uint32_t)((query * D + d) * 4);
-        gstore16(ro, off, lo);
-        gstore16(ro, off + 16, hi);
-      }
-  } else {
-    const auto ro = make_rsrc((uint16_t*)o + hoff, (uint32_t)N * D * 2);
+        for (int half = 0; half < 2; ++half) {
+          const int d = 32 * db + 16 * half + 8 * h;
+          const int j0 = 8 * half;
+          u32x4 lo, hi;
+          lo.x = __float_as_uint(acc[db][j0 + 0] * inv);
+          lo.y = __float_as_uint(acc[db][j0 + 1] * inv);
+          lo.z = __float_as_uint(acc[db][j0 + 2] * inv);
+          lo.w = __float_as_uint(acc[db][j0 + 3] * inv);
+          hi.x = __float_as_uint(acc[db][j0 + 4] * inv);
+          hi.y = __float_as_uint(acc[db][j0 + 5] * inv);
+          hi.z = __float_as_uint(acc[db][j0 + 6] * inv);
+          hi.w = __float_as_uint(acc[db][j0 + 7] * inv);
+          const uint32_t off = (uint32_t)((query * D + d) * 4);
+          gstore16(ro, off, lo);
+          gstore16(ro, off + 16, hi);
+        }
+    } else {
+      const auto ro = make_rsrc((uint16_t*)o + hoff, (uint32_t)N * D * 2);
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) {
-      f32x16 y = acc[db] * inv;
+      for (int db = 0; db < C::DB; ++db) {
+        f32x16 y = acc[db] * inv;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int d = 32 * db + 16 * half + 8 * h;
-        gstore16(ro, (uint32_t)((query * D + d) * 2), pack8<T>(y, 8 * half));
+        for (int half = 0; half < 2; ++half) {
+          const int d = 32 * db + 16 * half + 8 * h;
+          gstore16(ro, (uint32_t)((query * D + d) * 2), pack8<T>(y, 8 * half));
+        }
       }
     }
-  }
-  if (h == 0) {
-    const auto rl = make_rsrc(lse + (size_t)head * N, (uint32_t)N * 4);
-    gstore_f32(rl, (uint32_t)query * 4, (m_run + __log2f(lsum)) * kLn2);
+    if (h == 0) {
+      const auto rl = make_rsrc(lse + (size_t)head * N, (uint32_t)N * 4);
+      gstore_f32(rl, (uint32_t)query * 4, (m_run + __log2f(lsum)) * kLn2);
+    }
+    first_tile_issued = chain;
+    if (more && !chain) {
+      // The ring restarts at stage 0 for the next item; every wave must be
+      // done with this item's last tile before it is overwritten.
+      __syncthreads();
+    }
   }
 }
 
@@ -264,7 +294,7 @@ hipError_t launch_fwd_t(const FwdArgs& a) {
   using C = FwdTile<D>;
   const int n_qtiles = (int)((a.N + C::BM - 1) / C::BM);
   const int ZH = (int)(a.Z * a.H);
-  const dim3 grid((unsigned)xcd_grid(ZH, n_qtiles));
+  const dim3 grid((unsigned)xcd_grid(ZH, paired_groups(n_qtiles, CAUSAL)));
   hipLaunchKernelGGL((fa_fwd_kernel<D, T, CAUSAL, OT>), grid, dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.lse,
                      (int)a.N, ZH, n_qtiles, a.scale * kLog2e);

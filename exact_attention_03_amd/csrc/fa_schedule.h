@@ -64,6 +64,26 @@ FA_SCHED_HD int64_t sched_first_qtile(int64_t key_tile, int64_t keys_per_unit,
   return causal ? (key_tile * keys_per_unit) / queries_per_tile : 0;
 }
 
+// Causal pairing of query tiles (forward and dQ passes).  With the causal
+// mask the cost of query tile i grows with i, so a workgroup takes tiles
+// n-1-p and p of one head, one after the other: every workgroup has the same
+// work (with an odd count the middle tile is alone), and the second tile's
+// start overlaps the end of the first.  Without the mask a workgroup takes one
+// tile.  paired_groups is the number of workgroups per head; paired_items
+// returns how many tiles workgroup slot p takes and which.
+FA_SCHED_HD int64_t paired_groups(int64_t n_qtiles, int causal) {
+  return causal ? (n_qtiles + 1) / 2 : n_qtiles;
+}
+FA_SCHED_HD int paired_items(int64_t p, int64_t n_qtiles, int causal, int64_t* first, int64_t* second) {
+  if (!causal) {
+    *first = *second = p;
+    return 1;
+  }
+  *first = n_qtiles - 1 - p;
+  *second = p;
+  return *first != *second ? 2 : 1;
+}
+
 // Query-tile grids (forward and dQ passes) laid out so that the tiles of one
 // head run on one XCD, back to back, and share its L2 copy of K and V.
 // Workgroups are dealt to the XCDs round-robin by block index, so block b runs
