@@ -61,7 +61,8 @@ def kernel_work(w, o_bytes: int):
       dO V^T, P^T dO, dS^T Q), 8 N^2 D per head (x 1/2 causal).
     fa_bwd_dq: the fifth (dS K), 2 N^2 D per head (x 1/2 causal); its two
       recomputed GEMMs are not counted.
-    fa_bwd_pre: HBM bytes, read O and dO rows and write one fp32 per row.
+    fa_bwd_pre: HBM bytes, read O and dO rows and lse, write two fp32 per row
+    (Delta and lse * log2 e).
     """
     hf = fwd_flops(w)  # = 4 N^2 D per head, halved when causal
     rows = w.Z * w.H * w.N
@@ -69,7 +70,7 @@ def kernel_work(w, o_bytes: int):
         "fa_fwd": ("mfma", hf, "flop"),
         "fa_bwd_dkdv": ("mfma", 2.0 * hf, "flop"),
         "fa_bwd_dq": ("mfma", 0.5 * hf, "flop"),
-        "fa_bwd_pre": ("hbm", float(rows * (w.D * o_bytes + w.D * 2 + 4)), "byte"),
+        "fa_bwd_pre": ("hbm", float(rows * (w.D * o_bytes + w.D * 2 + 12)), "byte"),
     }
 
 
@@ -177,7 +178,7 @@ def run(args):
     o = torch.empty_like(q)
     lse = torch.empty((Z, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    delta = torch.empty((Z, H, N), dtype=torch.float32, device=dev)
+    stats = torch.empty((2, Z, H, N), dtype=torch.float32, device=dev)
     L = fa.lib()
     code = fa._dtype_code(q)
     causal = int(w.causal)
@@ -196,14 +197,14 @@ def run(args):
         call(L.fa_fwd(Z, H, N, D, code, code, P(q), P(k), P(v), P(o), P(lse), scale, causal, sp), "fa_fwd")
         if ev is not None:
             ev[1].record(stream)
-        call(L.fa_bwd_preprocess(Z, H, N, D, code, code, P(o), P(do), P(delta), sp), "fa_bwd_preprocess")
+        call(L.fa_bwd_preprocess(Z, H, N, D, code, code, P(o), P(do), P(lse), P(stats), sp), "fa_bwd_preprocess")
         if ev is not None:
             ev[2].record(stream)
-        call(L.fa_bwd_dkdv(Z, H, N, D, code, P(q), P(k), P(v), P(do), P(lse), P(delta), P(dk), P(dv),
+        call(L.fa_bwd_dkdv(Z, H, N, D, code, P(q), P(k), P(v), P(do), P(stats), P(dk), P(dv),
                            scale, causal, 0, sp), "fa_bwd_dkdv")
         if ev is not None:
             ev[3].record(stream)
-        call(L.fa_bwd_dq(Z, H, N, D, code, P(q), P(k), P(v), P(do), P(lse), P(delta), P(dq), scale, causal, sp),
+        call(L.fa_bwd_dq(Z, H, N, D, code, P(q), P(k), P(v), P(do), P(stats), P(dq), scale, causal, sp),
              "fa_bwd_dq")
         if ev is not None:
             ev[4].record(stream)

@@ -104,7 +104,8 @@ def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None):
         dk = torch.empty_like(k)
         dv = torch.empty_like(v)
         if workspace is None:
-            workspace = torch.empty((max(1, Z * H * N),), dtype=torch.float32, device=q.device)
+            nbytes = lib().fa_bwd_workspace_bytes(Z, H, N, D)
+            workspace = torch.empty((max(1, nbytes // 4),), dtype=torch.float32, device=q.device)
         st = lib().fa_bwd(Z, H, N, D, _dtype_code(q), _dtype_code(o), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                           _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _scale(scale, D),
                           int(bool(causal)), _ptr(workspace), workspace.numel() * 4, _stream(q))
@@ -112,20 +113,23 @@ def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None):
     return dq, dk, dv
 
 
-def bwd_preprocess(o, do):
-    """Delta = rowsum(O * dO) in float32, shape (Z, H, N)."""
+def bwd_preprocess(o, do, lse):
+    """Backward row statistics, float32 (2, Z, H, N): [0] = Delta = rowsum(O * dO),
+    [1] = lse * log2(e)."""
     torch = _torch()
     _check_qkv(do, o, names=("do", "o"))
     Z, H, N, D = do.shape
+    if lse.shape != (Z, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (Z, H, N) tensor")
     with torch.cuda.device(do.device):
-        delta = torch.empty((Z, H, N), dtype=torch.float32, device=do.device)
+        stats = torch.empty((2, Z, H, N), dtype=torch.float32, device=do.device)
         st = lib().fa_bwd_preprocess(Z, H, N, D, _dtype_code(do), _dtype_code(o), _ptr(o), _ptr(do),
-                                     _ptr(delta), _stream(do))
+                                     _ptr(lse), _ptr(stats), _stream(do))
     check(st, "fa_bwd_preprocess")
-    return delta
+    return stats
 
 
-def bwd_dkdv(q, k, v, do, lse, delta, causal=False, scale=None, num_programs=0):
+def bwd_dkdv(q, k, v, do, stats, causal=False, scale=None, num_programs=0):
     """dK, dV from the persistent key-tile pass (num_programs 0 = device default)."""
     torch = _torch()
     _check_qkv(q, k, v, do, names=("q", "k", "v", "do"))
@@ -133,24 +137,32 @@ def bwd_dkdv(q, k, v, do, lse, delta, causal=False, scale=None, num_programs=0):
     with torch.cuda.device(q.device):
         dk = torch.empty_like(k)
         dv = torch.empty_like(v)
-        st = lib().fa_bwd_dkdv(Z, H, N, D, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
-                               _ptr(delta), _ptr(dk), _ptr(dv), _scale(scale, D), int(bool(causal)),
-                               int(num_programs), _stream(q))
+        _check_stats(stats, Z, H, N)
+        st = lib().fa_bwd_dkdv(Z, H, N, D, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(stats),
+                               _ptr(dk), _ptr(dv), _scale(scale, D), int(bool(causal)), int(num_programs),
+                               _stream(q))
     check(st, "fa_bwd_dkdv")
     return dk, dv
 
 
-def bwd_dq(q, k, v, do, lse, delta, causal=False, scale=None):
+def bwd_dq(q, k, v, do, stats, causal=False, scale=None):
     """dQ from the query-tile pass."""
     torch = _torch()
     _check_qkv(q, k, v, do, names=("q", "k", "v", "do"))
     Z, H, N, D = q.shape
     with torch.cuda.device(q.device):
         dq = torch.empty_like(q)
-        st = lib().fa_bwd_dq(Z, H, N, D, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
-                             _ptr(delta), _ptr(dq), _scale(scale, D), int(bool(causal)), _stream(q))
+        _check_stats(stats, Z, H, N)
+        st = lib().fa_bwd_dq(Z, H, N, D, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(stats),
+                             _ptr(dq), _scale(scale, D), int(bool(causal)), _stream(q))
     check(st, "fa_bwd_dq")
     return dq
+
+
+def _check_stats(stats, Z, H, N):
+    torch = _torch()
+    if stats.shape != (2, Z, H, N) or stats.dtype != torch.float32 or not stats.is_contiguous():
+        raise ValueError("stats must be the contiguous float32 (2, Z, H, N) output of bwd_preprocess")
 
 
 def device_info(D=128, dtype_code=FA_DTYPE_F16):

@@ -144,7 +144,7 @@ int finish(hipError_t launch_err, hipStream_t stream, const char* what) {
 }
 
 int validate_bwd_common(const Shape& s, int dtype, const void* q, const void* k, const void* v,
-                        const void* dout, const float* lse, const float* delta, float scale, int causal) {
+                        const void* dout, const float* stats, float scale, int causal) {
   FA_TRY(check_shape(s));
   FA_TRY(check_dtypes(dtype, dtype, false));
   FA_TRY(check_scale(scale, causal));
@@ -153,8 +153,7 @@ int validate_bwd_common(const Shape& s, int dtype, const void* q, const void* k,
   FA_TRY(check_ptr(k, "k"));
   FA_TRY(check_ptr(v, "v"));
   FA_TRY(check_ptr(dout, "dout"));
-  FA_TRY(check_ptr(lse, "lse"));
-  FA_TRY(check_ptr(delta, "delta"));
+  FA_TRY(check_ptr(stats, "stats"));
   return FA_OK;
 }
 
@@ -179,7 +178,7 @@ const char* fa_last_error(void) { return g_last_error.c_str(); }
 size_t fa_bwd_workspace_bytes(int64_t Z, int64_t H, int64_t N, int64_t D) {
   (void)D;
   if (Z <= 0 || H <= 0 || N <= 0) return 0;
-  return (size_t)(Z * H * N) * sizeof(float);
+  return 2 * (size_t)(Z * H * N) * sizeof(float);
 }
 
 int fa_fwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, const void* q, const void* k,
@@ -200,7 +199,7 @@ int fa_fwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, c
 }
 
 int fa_bwd_preprocess(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, const void* o,
-                      const void* dout, float* delta, hipStream_t stream) {
+                      const void* dout, const float* lse, float* stats, hipStream_t stream) {
   g_last_error.clear();
   const Shape s{Z, H, N, D};
   FA_TRY(check_shape(s));
@@ -208,19 +207,20 @@ int fa_bwd_preprocess(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int
   if (s.empty()) return FA_OK;
   FA_TRY(check_ptr(o, "o"));
   FA_TRY(check_ptr(dout, "dout"));
-  FA_TRY(check_ptr(delta, "delta"));
+  FA_TRY(check_ptr(lse, "lse"));
+  FA_TRY(check_ptr(stats, "stats"));
   fa::BwdArgs a{};
   a.Z = Z; a.H = H; a.N = N; a.D = D; a.dtype = dtype; a.o_dtype = o_dtype;
-  a.o = o; a.dout = dout; a.delta = delta; a.stream = stream;
+  a.o = o; a.dout = dout; a.lse = lse; a.stats = stats; a.stream = stream;
   return finish(fa::launch_bwd_pre(a), stream, "fa_bwd_preprocess launch");
 }
 
 int fa_bwd_dkdv(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, const void* q, const void* k,
-                const void* v, const void* dout, const float* lse, const float* delta, void* dk, void* dv,
-                float scale, int causal, int num_programs, hipStream_t stream) {
+                const void* v, const void* dout, const float* stats, void* dk, void* dv, float scale,
+                int causal, int num_programs, hipStream_t stream) {
   g_last_error.clear();
   const Shape s{Z, H, N, D};
-  FA_TRY(validate_bwd_common(s, dtype, q, k, v, dout, lse, delta, scale, causal));
+  FA_TRY(validate_bwd_common(s, dtype, q, k, v, dout, stats, scale, causal));
   if (num_programs < 0) return fail(FA_ERR_INVALID_ARGUMENT, "num_programs must be >= 0 (got %d)", num_programs);
   if (s.empty()) return FA_OK;
   FA_TRY(check_ptr(dk, "dk"));
@@ -232,22 +232,22 @@ int fa_bwd_dkdv(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, const voi
   }
   fa::BwdArgs a{};
   a.Z = Z; a.H = H; a.N = N; a.D = D; a.dtype = dtype;
-  a.q = q; a.k = k; a.v = v; a.dout = dout; a.lse = lse; a.delta = const_cast<float*>(delta);
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.stats = const_cast<float*>(stats);
   a.dk = dk; a.dv = dv; a.scale = scale; a.causal = causal; a.num_programs = num_programs; a.stream = stream;
   return finish(fa::launch_bwd_dkdv(a), stream, "fa_bwd_dkdv launch");
 }
 
 int fa_bwd_dq(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, const void* q, const void* k,
-              const void* v, const void* dout, const float* lse, const float* delta, void* dq, float scale,
-              int causal, hipStream_t stream) {
+              const void* v, const void* dout, const float* stats, void* dq, float scale, int causal,
+              hipStream_t stream) {
   g_last_error.clear();
   const Shape s{Z, H, N, D};
-  FA_TRY(validate_bwd_common(s, dtype, q, k, v, dout, lse, delta, scale, causal));
+  FA_TRY(validate_bwd_common(s, dtype, q, k, v, dout, stats, scale, causal));
   if (s.empty()) return FA_OK;
   FA_TRY(check_ptr(dq, "dq"));
   fa::BwdArgs a{};
   a.Z = Z; a.H = H; a.N = N; a.D = D; a.dtype = dtype;
-  a.q = q; a.k = k; a.v = v; a.dout = dout; a.lse = lse; a.delta = const_cast<float*>(delta);
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.stats = const_cast<float*>(stats);
   a.dq = dq; a.scale = scale; a.causal = causal; a.stream = stream;
   return finish(fa::launch_bwd_dq(a), stream, "fa_bwd_dq launch");
 }
@@ -275,10 +275,10 @@ int fa_bwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, c
   if (workspace_bytes < need)
     return fail(FA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu bytes needed",
                 workspace_bytes, need);
-  float* delta = static_cast<float*>(workspace);
-  FA_TRY(fa_bwd_preprocess(Z, H, N, D, dtype, o_dtype, o, dout, delta, stream));
-  FA_TRY(fa_bwd_dkdv(Z, H, N, D, dtype, q, k, v, dout, lse, delta, dk, dv, scale, causal, 0, stream));
-  FA_TRY(fa_bwd_dq(Z, H, N, D, dtype, q, k, v, dout, lse, delta, dq, scale, causal, stream));
+  float* stats = static_cast<float*>(workspace);
+  FA_TRY(fa_bwd_preprocess(Z, H, N, D, dtype, o_dtype, o, dout, lse, stats, stream));
+  FA_TRY(fa_bwd_dkdv(Z, H, N, D, dtype, q, k, v, dout, stats, dk, dv, scale, causal, 0, stream));
+  FA_TRY(fa_bwd_dq(Z, H, N, D, dtype, q, k, v, dout, stats, dq, scale, causal, stream));
   return FA_OK;
 }
 

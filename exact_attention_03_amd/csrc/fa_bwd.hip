@@ -24,19 +24,26 @@
 namespace fa {
 
 // ============================================================ Delta pass
-// delta[row] = sum_d O[row, d] * dO[row, d] in fp32.  HBM-bound: each thread
-// reads one 16-byte chunk of dO (8 elements) and the matching O elements; the
-// D/8 threads of a row combine their partial sums with lane shuffles.
+// delta[row] = sum_d O[row, d] * dO[row, d] in fp32, and lse2[row] =
+// lse[row] * log2(e), the row statistic in the exp2 units the gradient passes
+// use (so they need no per-element conversion).  HBM-bound: each thread reads
+// one 16-byte chunk of dO (8 elements) and the matching O elements; the D/8
+// threads of a row combine their partial sums with lane shuffles.
 template <int D, typename T, bool O32>
 __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const void* __restrict__ o,
                                                          const uint16_t* __restrict__ dout,
-                                                         float* __restrict__ delta, int64_t rows) {
+                                                         const float* __restrict__ lse,
+                                                         float* __restrict__ delta, float* __restrict__ lse2,
+                                                         int64_t rows) {
   constexpr int TPR = D / 8;             // threads per row
   constexpr int RPB = 256 / TPR;         // rows per block
   const int tid = threadIdx.x;
   const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;
   const int c = tid % TPR;
   float acc = 0.f;
+  // The row's lse is loaded first, unconditionally (a clamped, in-bounds
+  // index), so that its latency overlaps the O / dO loads.
+  const float l = lse[row < rows ? row : rows - 1];
   if (row < rows) {
     const u32x4 g = *reinterpret_cast<const u32x4*>(dout + row * D + 8 * c);
     float ov[8];
@@ -61,7 +68,10 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const void* __restrict_
   }
 #pragma unroll
   for (int s = TPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s, 64);
-  if (row < rows && c == 0) delta[row] = acc;
+  if (row < rows && c == 0) {
+    delta[row] = acc;
+    lse2[row] = l * kLog2e;
+  }
 }
 
 // ============================================================ dK / dV pass
@@ -69,7 +79,7 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(const void* __restrict_
 // owns keys kw0 = k0 + 32w .. kw0+31, keeps their K rows in registers (and
 // their V rows too at D = 64; at D >= 128 the unit's V rows stay in LDS, which
 // frees the registers for two waves per SIMD at D = 128), and accumulates its
-// dK and dV rows in fp32 registers.  Query tiles of 32 rows (Q, dO, lse, Delta) stream through a
+// dK and dV rows in fp32 registers.  Query tiles of 32 rows (Q, dO, lse2, Delta) stream through a
 // two-stage LDS ring filled by direct global -> LDS copies.  Per query tile
 // the wave computes
 //     S  = Q K^T        (A = Q rows from LDS, B = K from registers)
@@ -87,7 +97,7 @@ struct DkdvTile {
   static_assert(BQ == 32, "one 32-query MFMA block per stage");
   static constexpr bool V_LDS = D >= 128;        // V rows in LDS instead of registers
   static constexpr int QT_BYTES = BQ * D * 2;    // one Q (or dO) tile
-  static constexpr int STAT_OFF = 2 * QT_BYTES;  // 64 lse values, then 64 Delta values
+  static constexpr int STAT_OFF = 2 * QT_BYTES;  // 64 lse2 values, then 64 Delta values
   static constexpr int STAGE_BYTES = 2 * QT_BYTES + 512;
   static constexpr int V_BYTES = V_LDS ? BK * D * 2 : 0;
   static constexpr int KSTEPS = D / 16;
@@ -112,13 +122,13 @@ __global__ __launch_bounds__(DkdvTile<D>::NW * 64)
 __attribute__((amdgpu_waves_per_eu(DkdvTile<D>::OCC, DkdvTile<D>::OCC)))
 void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                         const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-                        const float* __restrict__ lse, const float* __restrict__ delta, uint16_t* __restrict__ dk,
+                        const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
                         uint16_t* __restrict__ dv, int N, int ZH, int n_ktiles, int n_qtiles, float c2, float scale,
                         int P) {
   using C = DkdvTile<D>;
   using QTile = CmTile<C::BQ>;
   using VTile = CmTile<C::BK>;
-  // One LDS object per ring stage (Q tile, dO tile, lse and Delta) and one
+  // One LDS object per ring stage (Q tile, dO tile, lse2 and Delta) and one
   // for the unit's V rows, accessed with compile-time stages (query tiles in
   // pairs), so that the copy of the next query tile provably does not alias
   // the reads of the current one and does not hold them up.
@@ -144,12 +154,12 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     const auto rk = make_rsrc(k + hoff, head_bytes);
     const auto rv = make_rsrc(v + hoff, head_bytes);
     const auto rdo = make_rsrc(dout + hoff, head_bytes);
-    const auto rl = make_rsrc(lse + (size_t)head * N, (uint32_t)N * 4);
+    const auto rl = make_rsrc(lse2 + (size_t)head * N, (uint32_t)N * 4);
     const auto rd = make_rsrc(delta + (size_t)head * N, (uint32_t)N * 4);
     const int i0 = (int)sched_first_qtile(kt, C::BK, C::BQ, CAUSAL);
     const int nq = n_qtiles - i0;
 
-    // Copy query tile i (Q, dO, and the lse / Delta values from its first
+    // Copy query tile i (Q, dO, and the lse2 / Delta values from its first
     // query on) into ring stage st.
     auto issue_qtile = [&](int i, char* base) {
       const int qq0 = i * C::BQ;
@@ -240,7 +250,7 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int jj = 8 * t2 + i;
-          const float l2 = (i < 4 ? la[i & 3] : lb[i & 3]) * kLog2e;
+          const float l2 = i < 4 ? la[i & 3] : lb[i & 3];
           s[jj] = __builtin_fmaf(s[jj], c2, -l2);  // log2 of P
         }
         // Only the tile on the wave's diagonal and a ragged last tile are
@@ -298,7 +308,7 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
 
 // ============================================================ dQ pass
 // A workgroup of 4 waves owns a query tile of 128 queries of one head (32 per
-// wave, kept in registers together with their dO rows, lse and Delta); two
+// wave, kept in registers together with their dO rows, lse2 and Delta); two
 // (D = 128) or three (D = 64) workgroups share a compute unit.  With the
 // causal mask a workgroup owns two tiles, a long and a short one, so every
 // workgroup has the same work, and finishes them one after the other; the
@@ -330,7 +340,7 @@ template <int D, typename T, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqTile<D>::OCC, DqTile<D>::OCC)))
 void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                       const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-                      const float* __restrict__ lse, const float* __restrict__ delta, uint16_t* __restrict__ dq,
+                      const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dq,
                       int N, int ZH, int n_qtiles, float c2, float scale) {
   using C = DqTile<D>;
   using Tile = CmTile<C::BN>;
@@ -365,7 +375,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const auto rk = make_rsrc(k + hoff, head_bytes);
   const auto rv = make_rsrc(v + hoff, head_bytes);
   const auto rdo = make_rsrc(dout + hoff, head_bytes);
-  const auto rl = make_rsrc(lse + (size_t)head * N, (uint32_t)N * 4);
+  const auto rl = make_rsrc(lse2 + (size_t)head * N, (uint32_t)N * 4);
   const auto rdl = make_rsrc(delta + (size_t)head * N, (uint32_t)N * 4);
   const auto rdq = make_rsrc(dq + hoff, head_bytes);
   auto n_tiles = [&](int qt) {
@@ -386,7 +396,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     }
   };
   // The wave's query rows of tile qt: Q and dO in B-operand layout (lane =
-  // query, k = d), lse (as lse * log2 e) and Delta.
+  // query, k = d), lse2 and Delta.
   u32x4 qf[C::KSTEPS], dof[C::KSTEPS];
   float l2 = 0.f, dl = 0.f;
   auto load_rows = [&](int qt) {
@@ -397,7 +407,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       qf[t] = gload16(rq, off);
       dof[t] = gload16(rdo, off);
     }
-    l2 = gload_f32(rl, (uint32_t)query * 4) * kLog2e;
+    l2 = gload_f32(rl, (uint32_t)query * 4);
     dl = gload_f32(rdl, (uint32_t)query * 4);
   };
 
@@ -522,7 +532,7 @@ static hipError_t launch_pre_t(const BwdArgs& a) {
   const int64_t rows = a.Z * a.H * a.N;
   const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
   hipLaunchKernelGGL((fa_bwd_pre_kernel<D, T, O32>), grid, dim3(256), 0, a.stream, a.o,
-                     (const uint16_t*)a.dout, a.delta, rows);
+                     (const uint16_t*)a.dout, a.lse, a.stats, a.stats + rows, rows);
   return hipGetLastError();
 }
 template <int D, typename T>
@@ -549,7 +559,7 @@ static hipError_t launch_dkdv_t(const BwdArgs& a) {
   const int n_qt = (int)((a.N + C::BQ - 1) / C::BQ);
   hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, T, CAUSAL>), dim3((unsigned)a.num_programs), dim3(C::NW * 64), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, (int)a.N,
+                     (const uint16_t*)a.dout, a.stats + a.Z * a.H * a.N, a.stats, (uint16_t*)a.dk, (uint16_t*)a.dv, (int)a.N,
                      ZH, n_kt, n_qt, a.scale * kLog2e, a.scale, a.num_programs);
   return hipGetLastError();
 }
@@ -599,7 +609,7 @@ static hipError_t launch_dq_t(const BwdArgs& a) {
   hipLaunchKernelGGL((fa_bwd_dq_kernel<D, T, CAUSAL>), dim3((unsigned)xcd_grid(ZH, paired_groups(n_qt, CAUSAL))),
                      dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, (int)a.N, ZH, n_qt,
+                     (const uint16_t*)a.dout, a.stats + a.Z * a.H * a.N, a.stats, (uint16_t*)a.dq, (int)a.N, ZH, n_qt,
                      a.scale * kLog2e, a.scale);
   return hipGetLastError();
 }

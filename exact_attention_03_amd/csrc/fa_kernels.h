@@ -21,8 +21,10 @@ struct BwdArgs {
   int64_t Z, H, N, D;
   int dtype, o_dtype;
   const void *q, *k, *v, *o, *dout;
-  const float* lse;
-  float* delta;
+  const float* lse;  // preprocess input
+  // (2, Z, H, N) float32 written by the preprocess and read by the gradient
+  // passes: plane 0 = Delta, plane 1 = lse * log2(e).
+  float* stats;
   void *dq, *dk, *dv;
   float scale;
   int causal;

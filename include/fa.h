@@ -14,7 +14,8 @@
  * ---------------------------------------
  * - Tensors Q, K, V, O, dO, dQ, dK, dV are dense, contiguous, row-major
  *   (Z, H, N, D) arrays: Z batch, H heads, N sequence length (queries and keys
- *   alike), D head dimension.  lse and Delta are contiguous (Z, H, N) float32.
+ *   alike), D head dimension.  lse is contiguous (Z, H, N) float32 and the
+ *   backward row statistics are contiguous (2, Z, H, N) float32.
  * - Every tensor pointer is a DEVICE pointer owned by the caller; the library
  *   never allocates, frees or retains device memory.  Pointers must be 16-byte
  *   aligned.  Outputs must not alias inputs.
@@ -90,7 +91,8 @@ int fa_fwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype,
            const void* q, const void* k, const void* v, void* o, float* lse,
            float scale, int causal, hipStream_t stream);
 
-/* Bytes of device workspace fa_bwd needs: Z*H*N*sizeof(float) (Delta). */
+/* Bytes of device workspace fa_bwd needs: 2*Z*H*N*sizeof(float) (the row
+ * statistics written by fa_bwd_preprocess). */
 size_t fa_bwd_workspace_bytes(int64_t Z, int64_t H, int64_t N, int64_t D);
 
 /*
@@ -100,8 +102,8 @@ size_t fa_bwd_workspace_bytes(int64_t Z, int64_t H, int64_t N, int64_t D);
  *   dout            : (Z,H,N,D) dtype, the incoming gradient dO.
  *   dq, dk, dv      : (Z,H,N,D) dtype, written (overwritten, not accumulated).
  *   workspace       : device buffer of at least fa_bwd_workspace_bytes();
- *                     holds Delta between the stages; contents on return are
- *                     Delta = rowsum(O * dO) in float32.
+ *                     holds the row statistics between the stages; contents
+ *                     on return are those of fa_bwd_preprocess's `stats`.
  * Runs fa_bwd_preprocess, then fa_bwd_dkdv, then fa_bwd_dq on `stream`.
  */
 int fa_bwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype,
@@ -111,13 +113,17 @@ int fa_bwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype,
            hipStream_t stream);
 
 /*
- * Stage 1 of the backward: delta[z,h,i] = sum_d O[z,h,i,d] * dO[z,h,i,d]
- * accumulated in float32 ([FA-Ascend] §二, first line).  o is o_dtype, dout
- * is dtype, delta is (Z,H,N) float32 (written).
+ * Stage 1 of the backward: the per-row statistics of the gradient stages.
+ *   o     : (Z,H,N,D) o_dtype;  dout : (Z,H,N,D) dtype;
+ *   lse   : (Z,H,N) float32 from fa_fwd (read);
+ *   stats : (2,Z,H,N) float32 (written): stats[0] = Delta, with
+ *           Delta[z,h,i] = sum_d O[z,h,i,d] * dO[z,h,i,d] accumulated in
+ *           float32 ([FA-Ascend] §二, first line), and stats[1] = lse * log2(e),
+ *           the log-sum-exp in the exp2 units in which P is recomputed.
  */
 int fa_bwd_preprocess(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype,
                       int o_dtype, const void* o, const void* dout,
-                      float* delta, hipStream_t stream);
+                      const float* lse, float* stats, hipStream_t stream);
 
 /*
  * Stage 2: dK and dV.  A persistent grid of `num_programs` workgroups (0 =
@@ -125,23 +131,23 @@ int fa_bwd_preprocess(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype,
  * walks a static schedule of (head, key-tile) units; each workgroup owns whole
  * key tiles, recomputes P from lse for every query tile, and writes each dK/dV
  * tile exactly once: no atomics and no N*N scratch ([FA-Ascend] §二 three
- * principles, §五 persistent programs).  delta comes from fa_bwd_preprocess.
+ * principles, §五 persistent programs).  stats comes from fa_bwd_preprocess.
  * The result does not depend on num_programs (bitwise).
  */
 int fa_bwd_dkdv(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype,
                 const void* q, const void* k, const void* v, const void* dout,
-                const float* lse, const float* delta, void* dk, void* dv,
-                float scale, int causal, int num_programs, hipStream_t stream);
+                const float* stats, void* dk, void* dv, float scale, int causal,
+                int num_programs, hipStream_t stream);
 
 /*
  * Stage 3: dQ.  One workgroup per (head, query tile) owns its dQ tile and
  * writes it exactly once ([FA-Ascend] §二: a query tile can finish dQ by
- * itself).
+ * itself).  stats comes from fa_bwd_preprocess.
  */
 int fa_bwd_dq(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype,
               const void* q, const void* k, const void* v, const void* dout,
-              const float* lse, const float* delta, void* dq, float scale,
-              int causal, hipStream_t stream);
+              const float* stats, void* dq, float scale, int causal,
+              hipStream_t stream);
 
 /*
  * Device facts used for launch sizing, for the current device: compute

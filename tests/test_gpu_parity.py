@@ -116,19 +116,20 @@ def test_dkdv_bitwise_independent_of_grid_size():
     cpu, gpu = device_inputs(w)
     q, k, v, do = gpu
     o, lse = fa.forward(q, k, v, causal=True, scale=w.scale)
-    delta = fa.bwd_preprocess(o, do)
+    stats = fa.bwd_preprocess(o, do, lse)
     cus, default = fa.device_info(128, fa.FA_DTYPE_F16)
     log(f"device: {cus} CUs, default dK/dV grid {default}")
-    ref = fa.bwd_dkdv(q, k, v, do, lse, delta, causal=True, scale=w.scale, num_programs=0)
+    ref = fa.bwd_dkdv(q, k, v, do, stats, causal=True, scale=w.scale, num_programs=0)
     for P in (1, 7, cus, 3 * cus + 1):
-        dk, dv = fa.bwd_dkdv(q, k, v, do, lse, delta, causal=True, scale=w.scale, num_programs=P)
+        dk, dv = fa.bwd_dkdv(q, k, v, do, stats, causal=True, scale=w.scale, num_programs=P)
         torch.cuda.synchronize()
         assert torch.equal(dk.view(torch.int16), ref[0].view(torch.int16)), f"dk differs at P={P}"
         assert torch.equal(dv.view(torch.int16), ref[1].view(torch.int16)), f"dv differs at P={P}"
 
 
 def test_stages_match_fused_backward():
-    """fa_bwd == preprocess + dkdv + dq called one by one; Delta matches the oracle."""
+    """fa_bwd == preprocess + dkdv + dq called one by one; the row statistics
+    are Delta (checked in fp64 against the stored O and dO) and lse * log2(e)."""
     import torch
 
     fa = _fa()
@@ -137,15 +138,17 @@ def test_stages_match_fused_backward():
     q, k, v, do = gpu
     o, lse = fa.forward(q, k, v, causal=False, scale=w.scale)
     dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal=False, scale=w.scale)
-    delta = fa.bwd_preprocess(o, do)
-    dk2, dv2 = fa.bwd_dkdv(q, k, v, do, lse, delta, causal=False, scale=w.scale)
-    dq2 = fa.bwd_dq(q, k, v, do, lse, delta, causal=False, scale=w.scale)
+    stats = fa.bwd_preprocess(o, do, lse)
+    dk2, dv2 = fa.bwd_dkdv(q, k, v, do, stats, causal=False, scale=w.scale)
+    dq2 = fa.bwd_dq(q, k, v, do, stats, causal=False, scale=w.scale)
     torch.cuda.synchronize()
     for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     # Delta from the stored 16-bit O, in fp64 on the host
     want = np.sum(to_f64(o) * to_f64(do), axis=-1)
-    assert max_abs(to_f64(delta), want) <= 1e-4 * max(1.0, float(np.max(np.abs(want))))
+    assert max_abs(to_f64(stats[0]), want) <= 1e-4 * max(1.0, float(np.max(np.abs(want))))
+    lse2 = to_f64(lse) * np.log2(np.e)
+    assert max_abs(to_f64(stats[1]), lse2) <= 1e-6 * max(1.0, float(np.max(np.abs(lse2))))
 
 
 def test_negative_controls_fail_the_check():

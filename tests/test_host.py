@@ -79,7 +79,7 @@ def test_empty_problem_is_ok_without_pointers(fa):
 
 def test_bwd_workspace_rules(fa):
     lib = fa.lib()
-    assert lib.fa_bwd_workspace_bytes(128, 8, 1024, 128) == 128 * 8 * 1024 * 4
+    assert lib.fa_bwd_workspace_bytes(128, 8, 1024, 128) == 2 * 128 * 8 * 1024 * 4
     need = lib.fa_bwd_workspace_bytes(1, 2, 100, 64)
     st = lib.fa_bwd(1, 2, 100, 64, 0, 0, *([P] * 9), 0.125, 0, P, need - 4, None)
     assert st == 1 and "workspace" in fa.last_error()
@@ -89,10 +89,12 @@ def test_bwd_workspace_rules(fa):
 
 def test_stage_argument_errors(fa):
     lib = fa.lib()
-    assert lib.fa_bwd_preprocess(1, 1, 64, 64, 0, 1, P, P, P, None) == 1       # o_dtype bf16 with f16
-    assert lib.fa_bwd_dkdv(1, 1, 64, 64, 0, *([P] * 8), 0.125, 0, -1, None) == 1  # negative grid
-    assert lib.fa_bwd_dq(1, 1, 64, 32, 0, *([P] * 7), 0.125, 0, None) == 2      # D = 32
-    assert lib.fa_bwd_dq(1, 1, 64, 64, 0, *([P] * 6), MIS, 0.125, 0, None) == 1  # misaligned dq
+    assert lib.fa_bwd_preprocess(1, 1, 64, 64, 0, 1, P, P, P, P, None) == 1    # o_dtype bf16 with f16
+    assert lib.fa_bwd_preprocess(1, 1, 64, 64, 0, 0, P, P, None, P, None) == 1  # no lse
+    assert lib.fa_bwd_dkdv(1, 1, 64, 64, 0, *([P] * 7), 0.125, 0, -1, None) == 1  # negative grid
+    assert lib.fa_bwd_dkdv(1, 1, 64, 64, 0, *([P] * 4), None, P, P, 0.125, 0, 0, None) == 1  # no stats
+    assert lib.fa_bwd_dq(1, 1, 64, 32, 0, *([P] * 6), 0.125, 0, None) == 2      # D = 32
+    assert lib.fa_bwd_dq(1, 1, 64, 64, 0, *([P] * 5), MIS, 0.125, 0, None) == 1  # misaligned dq
 
 
 def test_causal_tile_count_matches_page(fa):
@@ -142,4 +144,4 @@ def test_workspace_versus_page_full_scratch(fa):
     full = g["Z"] * g["H"] * g["N"] * g["N"] * g["bytes_per_element"]
     assert full == g["one_copy_bytes"]
     ours = fa.workspace_bytes(g["Z"], g["H"], g["N"], 128)
-    assert ours == g["Z"] * g["H"] * g["N"] * 4 and ours * 512 == full
+    assert ours == 2 * g["Z"] * g["H"] * g["N"] * 4 and ours * 256 == full
