@@ -41,10 +41,10 @@ KERNELS = ("fa_fwd", "fa_bwd_pre", "fa_bwd_dkdv", "fa_bwd_dq")
 # Source files each kernel is built from; a stored traffic measurement is only
 # reported while these are unchanged.
 KERNEL_SOURCES = {
-    "fa_fwd": ("fa_fwd.hip", "fa_device.h", "fa_kernels.h"),
+    "fa_fwd": ("fa_fwd.hip", "fa_device.h", "fa_kernels.h", "fa_schedule.h"),
     "fa_bwd_pre": ("fa_bwd.hip", "fa_device.h", "fa_kernels.h"),
     "fa_bwd_dkdv": ("fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_schedule.h"),
-    "fa_bwd_dq": ("fa_bwd.hip", "fa_device.h", "fa_kernels.h"),
+    "fa_bwd_dq": ("fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_schedule.h"),
 }
 
 
