@@ -184,7 +184,13 @@ FA_DEV void dma4(__amdgpu_buffer_rsrc_t r, char* lds_base, uint32_t voff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds_base, 4, voff, 0, 0, 0);
 }
 // Wait until every global load of this wave (including LDS copies) is done.
-FA_DEV void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Emitted through the builtin (s_waitcnt with vmcnt 0 and the other counters
+// at their maximum), not inline assembly, so that the compiler's own wait
+// insertion knows every earlier load has completed and adds no further waits
+// for registers loaded before this point.  The builtin does not order memory
+// accesses for the compiler: every use is followed by __syncthreads(), which
+// does, before any LDS read of the copied data.
+FA_DEV void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ----------------------------------------------------------------- LDS tiles
 // A tile of R rows x D 16-bit elements (D a multiple of 32) is stored in LDS

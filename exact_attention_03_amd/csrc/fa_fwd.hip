@@ -147,6 +147,7 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 
     float m_run = -1e30f;  // running max, exp2 units
     float l_run = 0.f;     // running denominator (this lane half's keys)
+    bool fresh = true;     // no tile processed yet: acc and l_run are zero
     f32x16 acc[C::DB];
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[db] = f32x16{};
@@ -202,12 +203,17 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       mx = half_swap_max(mx);
       const float m_new = fmaxf(m_run, mx * c2);
       if (wave_any(m_new > m_run + kRescaleSlack<T>)) {
-        const float alpha = fast_exp2(m_run - m_new);
-        l_run *= alpha;
+        // Before the first tile the accumulator and denominator are zero and
+        // need no rescaling.
+        if (!fresh) {
+          const float alpha = fast_exp2(m_run - m_new);
+          l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+          for (int db = 0; db < C::DB; ++db) acc[db] *= alpha;
+        }
         m_run = m_new;
       }
+      fresh = false;
       // p = exp2(s c - m), packed to the 16-bit type for the PV product;
       // l_run sums the fp32 p.
       float rs = 0.f;
