@@ -1,9 +1,9 @@
 """FlashAttention forward + backward throughput on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-fa_fwd (O in the input dtype, lse), then the backward's three stages
-(fa_bwd_preprocess -> fa_bwd_dkdv -> fa_bwd_dq, exactly what fa_bwd runs),
-all through the library's C ABI on torch's current stream.
+fa_fwd (O in the input dtype, lse), then the backward's two stages
+(fa_bwd_dq_and_stats -> fa_bwd_dkdv, exactly what fa_bwd runs), all through
+the library's C ABI on torch's current stream.
 
 Default workload: Z=128, H=8, N=1024, D=128, fp16, causal, scale=1/sqrt(128)
 (seeded i.i.d. N(0,1) Q/K/V/dO).  Prints ONE JSON line with:
@@ -37,7 +37,7 @@ import workloads  # noqa: E402  (seeded inputs only; no attention arithmetic)
 PEAK_MFMA_F16_TFLOPS = 2516.6   # fp16 / bf16 dense MFMA
 PEAK_HBM_GBS = 8000.0           # HBM3E
 DEFAULT_WORKLOAD = "d128_causal"
-KERNELS = ("fa_fwd", "fa_bwd_pre", "fa_bwd_dkdv", "fa_bwd_dq")
+KERNELS = ("fa_fwd", "fa_bwd_dq", "fa_bwd_dkdv")  # the step, in launch order
 # Source files each kernel is built from; a stored traffic measurement is only
 # reported while these are unchanged.
 KERNEL_SOURCES = {
@@ -60,9 +60,10 @@ def kernel_work(w, o_bytes: int):
     fa_bwd_dkdv: four of the five counted backward GEMMs (QK^T recompute,
       dO V^T, P^T dO, dS^T Q), 8 N^2 D per head (x 1/2 causal).
     fa_bwd_dq: the fifth (dS K), 2 N^2 D per head (x 1/2 causal); its two
-      recomputed GEMMs are not counted.
-    fa_bwd_pre: HBM bytes, read O and dO rows and lse, write two fp32 per row
-    (Delta and lse * log2 e).
+      recomputed GEMMs, and the row statistics (Delta, lse * log2 e) it
+      computes for the dK/dV pass, are not counted.
+    fa_bwd_pre (the standalone statistics pass, not part of the step): HBM
+      bytes, read O and dO rows and lse, write two fp32 per row.
     """
     hf = fwd_flops(w)  # = 4 N^2 D per head, halved when causal
     rows = w.Z * w.H * w.N
@@ -197,17 +198,14 @@ def run(args):
         call(L.fa_fwd(Z, H, N, D, code, code, P(q), P(k), P(v), P(o), P(lse), scale, causal, sp), "fa_fwd")
         if ev is not None:
             ev[1].record(stream)
-        call(L.fa_bwd_preprocess(Z, H, N, D, code, code, P(o), P(do), P(lse), P(stats), sp), "fa_bwd_preprocess")
+        call(L.fa_bwd_dq_and_stats(Z, H, N, D, code, code, P(q), P(k), P(v), P(o), P(do), P(lse), P(stats),
+                                   P(dq), scale, causal, sp), "fa_bwd_dq_and_stats")
         if ev is not None:
             ev[2].record(stream)
         call(L.fa_bwd_dkdv(Z, H, N, D, code, P(q), P(k), P(v), P(do), P(stats), P(dk), P(dv),
                            scale, causal, 0, sp), "fa_bwd_dkdv")
         if ev is not None:
             ev[3].record(stream)
-        call(L.fa_bwd_dq(Z, H, N, D, code, P(q), P(k), P(v), P(do), P(stats), P(dq), scale, causal, sp),
-             "fa_bwd_dq")
-        if ev is not None:
-            ev[4].record(stream)
 
     if args.calib_copy_mib > 0:
         # A plain device copy of known size, for scaling HBM counters.
@@ -223,7 +221,7 @@ def run(args):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -242,7 +240,7 @@ def run(args):
 
     ff = fwd_flops(w)
     fwd_ms = avg["fa_fwd"]
-    bwd_ms = avg["fa_bwd_pre"] + avg["fa_bwd_dkdv"] + avg["fa_bwd_dq"]
+    bwd_ms = avg["fa_bwd_dq"] + avg["fa_bwd_dkdv"]
     value = 3.5 * ff / (ms_step * 1e-3) / 1e12
     work = kernel_work(w, o.element_size())
     kern = {}

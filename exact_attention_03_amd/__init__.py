@@ -16,7 +16,7 @@ import math
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32, FAError, check, last_error, lib,  # noqa: F401
                    status_name)
 
-__all__ = ["forward", "backward", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "workspace_bytes",
+__all__ = ["forward", "backward", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_dq_and_stats", "workspace_bytes",
            "device_info", "dkdv_schedule", "fwd_tile_pairs", "FAError", "lib"]
 
 
@@ -157,6 +157,23 @@ def bwd_dq(q, k, v, do, stats, causal=False, scale=None):
                              _ptr(dq), _scale(scale, D), int(bool(causal)), _stream(q))
     check(st, "fa_bwd_dq")
     return dq
+
+
+def bwd_dq_and_stats(q, k, v, o, do, lse, causal=False, scale=None):
+    """dQ and the backward row statistics from one pass: (dq, stats)."""
+    torch = _torch()
+    _check_qkv(q, k, v, do, names=("q", "k", "v", "do"))
+    Z, H, N, D = q.shape
+    if lse.shape != (Z, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (Z, H, N) tensor")
+    with torch.cuda.device(q.device):
+        dq = torch.empty_like(q)
+        stats = torch.empty((2, Z, H, N), dtype=torch.float32, device=q.device)
+        st = lib().fa_bwd_dq_and_stats(Z, H, N, D, _dtype_code(q), _dtype_code(o), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(o), _ptr(do), _ptr(lse), _ptr(stats), _ptr(dq), _scale(scale, D),
+                                       int(bool(causal)), _stream(q))
+    check(st, "fa_bwd_dq_and_stats")
+    return dq, stats
 
 
 def _check_stats(stats, Z, H, N):

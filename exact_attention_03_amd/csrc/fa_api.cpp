@@ -252,6 +252,30 @@ int fa_bwd_dq(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, const void*
   return finish(fa::launch_bwd_dq(a), stream, "fa_bwd_dq launch");
 }
 
+int fa_bwd_dq_and_stats(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, const void* q,
+                        const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                        float* stats, void* dq, float scale, int causal, hipStream_t stream) {
+  g_last_error.clear();
+  const Shape s{Z, H, N, D};
+  FA_TRY(check_shape(s));
+  FA_TRY(check_dtypes(dtype, o_dtype, true));
+  FA_TRY(check_scale(scale, causal));
+  if (s.empty()) return FA_OK;
+  FA_TRY(check_ptr(q, "q"));
+  FA_TRY(check_ptr(k, "k"));
+  FA_TRY(check_ptr(v, "v"));
+  FA_TRY(check_ptr(o, "o"));
+  FA_TRY(check_ptr(dout, "dout"));
+  FA_TRY(check_ptr(lse, "lse"));
+  FA_TRY(check_ptr(stats, "stats"));
+  FA_TRY(check_ptr(dq, "dq"));
+  fa::BwdArgs a{};
+  a.Z = Z; a.H = H; a.N = N; a.D = D; a.dtype = dtype; a.o_dtype = o_dtype;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.stats = stats;
+  a.dq = dq; a.scale = scale; a.causal = causal; a.dq_stats = true; a.stream = stream;
+  return finish(fa::launch_bwd_dq(a), stream, "fa_bwd_dq_and_stats launch");
+}
+
 int fa_bwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, const void* q, const void* k,
            const void* v, const void* o, const void* dout, const float* lse, void* dq, void* dk, void* dv,
            float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
@@ -276,9 +300,8 @@ int fa_bwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, c
     return fail(FA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu bytes needed",
                 workspace_bytes, need);
   float* stats = static_cast<float*>(workspace);
-  FA_TRY(fa_bwd_preprocess(Z, H, N, D, dtype, o_dtype, o, dout, lse, stats, stream));
+  FA_TRY(fa_bwd_dq_and_stats(Z, H, N, D, dtype, o_dtype, q, k, v, o, dout, lse, stats, dq, scale, causal, stream));
   FA_TRY(fa_bwd_dkdv(Z, H, N, D, dtype, q, k, v, dout, stats, dk, dv, scale, causal, 0, stream));
-  FA_TRY(fa_bwd_dq(Z, H, N, D, dtype, q, k, v, dout, stats, dq, scale, causal, stream));
   return FA_OK;
 }
 

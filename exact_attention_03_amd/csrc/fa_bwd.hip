@@ -336,12 +336,19 @@ struct DqTile {
   static constexpr bool PAIRS = D <= 128;
 };
 
-template <int D, typename T, bool CAUSAL>
+// Where the dQ pass gets its row statistics: kStatsIn reads lse2 and Delta
+// from the preprocess pass; kStatsO16 / kStatsO32 compute them itself from
+// lse and the O rows (16-bit or fp32 O) and dO rows it loads anyway, and
+// write them for the dK/dV pass, which then needs no preprocess pass.
+enum DqStats { kStatsIn = 0, kStatsO16 = 1, kStatsO32 = 2 };
+
+template <int D, typename T, bool CAUSAL, int STATS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqTile<D>::OCC, DqTile<D>::OCC)))
 void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                       const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                       const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dq,
-                      int N, int ZH, int n_qtiles, float c2, float scale) {
+                      int N, int ZH, int n_qtiles, float c2, float scale, const void* __restrict__ o,
+                      const float* __restrict__ lse, float* __restrict__ stats_out) {
   using C = DqTile<D>;
   using Tile = CmTile<C::BN>;
   // One LDS object per ring stage and operand, accessed with compile-time
@@ -375,7 +382,8 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const auto rk = make_rsrc(k + hoff, head_bytes);
   const auto rv = make_rsrc(v + hoff, head_bytes);
   const auto rdo = make_rsrc(dout + hoff, head_bytes);
-  const auto rl = make_rsrc(lse2 + (size_t)head * N, (uint32_t)N * 4);
+  const auto rl = STATS == kStatsIn ? make_rsrc(lse2 + (size_t)head * N, (uint32_t)N * 4)
+                                    : make_rsrc(lse + (size_t)head * N, (uint32_t)N * 4);
   const auto rdl = make_rsrc(delta + (size_t)head * N, (uint32_t)N * 4);
   const auto rdq = make_rsrc(dq + hoff, head_bytes);
   auto n_tiles = [&](int qt) {
@@ -407,8 +415,69 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       qf[t] = gload16(rq, off);
       dof[t] = gload16(rdo, off);
     }
-    l2 = gload_f32(rl, (uint32_t)query * 4);
-    dl = gload_f32(rdl, (uint32_t)query * 4);
+    if constexpr (STATS == kStatsIn) {
+      l2 = gload_f32(rl, (uint32_t)query * 4);
+      dl = gload_f32(rdl, (uint32_t)query * 4);
+    } else {
+      l2 = gload_f32(rl, (uint32_t)query * 4) * kLog2e;
+    }
+  };
+  // Row statistics of tile qt computed here (STATS != kStatsIn), once its dO
+  // rows are in registers: Delta = sum_d O * dO, in the exact order of the
+  // preprocess pass (there D/8 threads each sum one 8-element chunk c of the
+  // row with an fma chain and combine the chunks with an xor butterfly over c;
+  // here lane half h holds the chunks c = 2t + h, so every butterfly level
+  // but the last pairs chunks inside a lane and the last pairs the halves),
+  // so that both paths give the same bits.  lse2 and Delta are then written
+  // for the dK/dV pass.
+  auto finish_rows = [&](int qt) {
+    if constexpr (STATS != kStatsIn) {
+      const int query = qt * C::BM + 32 * w + l32;
+      float part[C::KSTEPS];
+#pragma unroll
+      for (int t = 0; t < C::KSTEPS; ++t) {
+        float ov[8];
+        if constexpr (STATS == kStatsO32) {
+          const auto ro = make_rsrc((const float*)o + hoff, (uint32_t)N * D * 4);
+          const uint32_t off = (uint32_t)((query * D + 16 * t + 8 * h) * 4);
+          const u32x4 a = gload16(ro, off), b = gload16(ro, off + 16);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ov[i] = __uint_as_float(a[i]);
+            ov[4 + i] = __uint_as_float(b[i]);
+          }
+        } else {
+          const auto ro = make_rsrc((const uint16_t*)o + hoff, head_bytes);
+          const u32x4 a = gload16(ro, (uint32_t)((query * D + 16 * t + 8 * h) * 2));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ov[2 * i] = lo16_to_f32<T>(a[i]);
+            ov[2 * i + 1] = hi16_to_f32<T>(a[i]);
+          }
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc = __builtin_fmaf(ov[2 * i], lo16_to_f32<T>(dof[t][i]), acc);
+          acc = __builtin_fmaf(ov[2 * i + 1], hi16_to_f32<T>(dof[t][i]), acc);
+        }
+        part[t] = acc;
+      }
+#pragma unroll
+      for (int sx = C::KSTEPS / 2; sx >= 1; sx >>= 1) {
+        float nxt[C::KSTEPS];
+#pragma unroll
+        for (int t = 0; t < C::KSTEPS; ++t) nxt[t] = part[t] + part[t ^ sx];
+#pragma unroll
+        for (int t = 0; t < C::KSTEPS; ++t) part[t] = nxt[t];
+      }
+      dl = half_swap_sum(part[0]);
+      if (h == 0) {
+        const size_t plane = (size_t)ZH * (size_t)N;
+        gstore_f32(make_rsrc(stats_out + (size_t)head * N, (uint32_t)N * 4), (uint32_t)query * 4, dl);
+        gstore_f32(make_rsrc(stats_out + plane + (size_t)head * N, (uint32_t)N * 4), (uint32_t)query * 4, l2);
+      }
+    }
   };
 
   // Per-lane LDS read bases: K / V rows 32 kb + sigma(l32) as A operands,
@@ -431,6 +500,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     // during this item's last tile.
     const bool chain = more && (nt % 2 == 0);
     if (!first_tile_issued) issue_tile(0, k0s, v0s);
+    finish_rows(qt);
 
     f32x16 dqa[C::DB];
 #pragma unroll
@@ -601,21 +671,26 @@ hipError_t dkdv_blocks_per_cu(int D, int dtype, int* out) {
   }
 }
 
-template <int D, typename T, bool CAUSAL>
+template <int D, typename T, bool CAUSAL, int STATS>
 static hipError_t launch_dq_t(const BwdArgs& a) {
   using C = DqTile<D>;
   const int ZH = (int)(a.Z * a.H);
   const int n_qt = (int)((a.N + C::BM - 1) / C::BM);
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, T, CAUSAL>), dim3((unsigned)xcd_grid(ZH, paired_groups(n_qt, CAUSAL))),
-                     dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, T, CAUSAL, STATS>),
+                     dim3((unsigned)xcd_grid(ZH, paired_groups(n_qt, CAUSAL))), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.stats + a.Z * a.H * a.N, a.stats, (uint16_t*)a.dq, (int)a.N, ZH, n_qt,
-                     a.scale * kLog2e, a.scale);
+                     a.scale * kLog2e, a.scale, a.o, a.lse, a.stats);
   return hipGetLastError();
+}
+template <int D, typename T, int STATS>
+static hipError_t launch_dq_s(const BwdArgs& a) {
+  return a.causal ? launch_dq_t<D, T, true, STATS>(a) : launch_dq_t<D, T, false, STATS>(a);
 }
 template <int D, typename T>
 static hipError_t launch_dq_d(const BwdArgs& a) {
-  return a.causal ? launch_dq_t<D, T, true>(a) : launch_dq_t<D, T, false>(a);
+  if (!a.dq_stats) return launch_dq_s<D, T, kStatsIn>(a);
+  return a.o_dtype == F32::code ? launch_dq_s<D, T, kStatsO32>(a) : launch_dq_s<D, T, kStatsO16>(a);
 }
 template <typename T>
 static hipError_t launch_dq_dt(const BwdArgs& a) {

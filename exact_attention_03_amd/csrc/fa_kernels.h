@@ -29,6 +29,9 @@ struct BwdArgs {
   float scale;
   int causal;
   int num_programs;  // persistent dK/dV grid; resolved by the caller (> 0)
+  // dQ pass: compute the row statistics from o and lse and write them to
+  // stats (instead of reading them from the preprocess pass).
+  bool dq_stats;
   hipStream_t stream;
 };
 

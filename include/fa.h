@@ -104,7 +104,8 @@ size_t fa_bwd_workspace_bytes(int64_t Z, int64_t H, int64_t N, int64_t D);
  *   workspace       : device buffer of at least fa_bwd_workspace_bytes();
  *                     holds the row statistics between the stages; contents
  *                     on return are those of fa_bwd_preprocess's `stats`.
- * Runs fa_bwd_preprocess, then fa_bwd_dkdv, then fa_bwd_dq on `stream`.
+ * Runs fa_bwd_dq_and_stats, then fa_bwd_dkdv on `stream`.  The result is
+ * bitwise that of fa_bwd_preprocess, fa_bwd_dkdv, fa_bwd_dq run one by one.
  */
 int fa_bwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype,
            const void* q, const void* k, const void* v, const void* o,
@@ -148,6 +149,20 @@ int fa_bwd_dq(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype,
               const void* q, const void* k, const void* v, const void* dout,
               const float* stats, void* dq, float scale, int causal,
               hipStream_t stream);
+
+/*
+ * dQ together with the row statistics ([FA-Ascend] §二): the dQ pass computes
+ * Delta for its own query rows from o and dout (with the summation order of
+ * fa_bwd_preprocess, so the values are bitwise the same) and lse * log2(e)
+ * from lse, uses them, and writes both to `stats` ((2,Z,H,N) float32, the
+ * layout fa_bwd_preprocess writes) for a following fa_bwd_dkdv.  This saves
+ * the separate pass over O and dO.  Arguments as in fa_bwd.
+ */
+int fa_bwd_dq_and_stats(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype,
+                        int o_dtype, const void* q, const void* k, const void* v,
+                        const void* o, const void* dout, const float* lse,
+                        float* stats, void* dq, float scale, int causal,
+                        hipStream_t stream);
 
 /*
  * Device facts used for launch sizing, for the current device: compute

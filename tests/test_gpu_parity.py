@@ -127,24 +127,35 @@ def test_dkdv_bitwise_independent_of_grid_size():
         assert torch.equal(dv.view(torch.int16), ref[1].view(torch.int16)), f"dv differs at P={P}"
 
 
-def test_stages_match_fused_backward():
-    """fa_bwd == preprocess + dkdv + dq called one by one; the row statistics
-    are Delta (checked in fp64 against the stored O and dO) and lse * log2(e)."""
+@pytest.mark.parametrize("shape,dtype,causal,o32", [
+    ((1, 3, 333, 64), "bf16", False, False),
+    ((2, 2, 300, 128), "f16", True, True),
+    ((1, 2, 200, 256), "bf16", True, False),
+])
+def test_stages_match_fused_backward(shape, dtype, causal, o32):
+    """fa_bwd (dQ with the row statistics, then dK/dV) == preprocess + dK/dV +
+    dQ called one by one, bit for bit; the statistics the dQ pass computes
+    equal the preprocess pass's bit for bit (Delta is checked in fp64 against
+    the stored O and dO, lse * log2 e against lse)."""
     import torch
 
     fa = _fa()
-    w = workloads.Workload("stages", 91, 1, 3, 333, 64, "bf16", False)
+    Z, H, N, D = shape
+    w = workloads.Workload("stages", 91 + D, Z, H, N, D, dtype, causal)
     cpu, gpu = device_inputs(w)
     q, k, v, do = gpu
-    o, lse = fa.forward(q, k, v, causal=False, scale=w.scale)
-    dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal=False, scale=w.scale)
+    log(f"case shape={shape} dtype={dtype} causal={causal} o32={o32}")
+    o, lse = fa.forward(q, k, v, causal=causal, scale=w.scale, out_dtype=torch.float32 if o32 else None)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal=causal, scale=w.scale)
     stats = fa.bwd_preprocess(o, do, lse)
-    dk2, dv2 = fa.bwd_dkdv(q, k, v, do, stats, causal=False, scale=w.scale)
-    dq2 = fa.bwd_dq(q, k, v, do, stats, causal=False, scale=w.scale)
+    dk2, dv2 = fa.bwd_dkdv(q, k, v, do, stats, causal=causal, scale=w.scale)
+    dq2 = fa.bwd_dq(q, k, v, do, stats, causal=causal, scale=w.scale)
+    dq3, stats3 = fa.bwd_dq_and_stats(q, k, v, o, do, lse, causal=causal, scale=w.scale)
     torch.cuda.synchronize()
-    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
-        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
-    # Delta from the stored 16-bit O, in fp64 on the host
+    for a, b, n in ((dq, dq2, "dq"), (dk, dk2, "dk"), (dv, dv2, "dv"), (dq3, dq2, "dq (fused stats)")):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), n
+    assert torch.equal(stats3.view(torch.int32), stats.view(torch.int32)), "statistics differ"
+    # Delta from the stored O, in fp64 on the host
     want = np.sum(to_f64(o) * to_f64(do), axis=-1)
     assert max_abs(to_f64(stats[0]), want) <= 1e-4 * max(1.0, float(np.max(np.abs(want))))
     lse2 = to_f64(lse) * np.log2(np.e)

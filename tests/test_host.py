@@ -95,6 +95,11 @@ def test_stage_argument_errors(fa):
     assert lib.fa_bwd_dkdv(1, 1, 64, 64, 0, *([P] * 4), None, P, P, 0.125, 0, 0, None) == 1  # no stats
     assert lib.fa_bwd_dq(1, 1, 64, 32, 0, *([P] * 6), 0.125, 0, None) == 2      # D = 32
     assert lib.fa_bwd_dq(1, 1, 64, 64, 0, *([P] * 5), MIS, 0.125, 0, None) == 1  # misaligned dq
+    assert lib.fa_bwd_dq_and_stats(1, 1, 64, 64, 0, 1, *([P] * 8), 0.125, 0, None) == 1  # o bf16 with f16
+    assert lib.fa_bwd_dq_and_stats(1, 1, 64, 64, 0, 0, *([P] * 5), None, P, P, 0.125, 0, None) == 1  # no lse
+    assert lib.fa_bwd_dq_and_stats(1, 1, 64, 64, 0, 0, *([P] * 7), MIS, 0.125, 0, None) == 1  # misaligned dq
+    assert lib.fa_bwd_dq_and_stats(1, 1, 64, 48, 0, 0, *([P] * 8), 0.125, 0, None) == 2  # D = 48
+    assert lib.fa_bwd_dq_and_stats(0, 1, 64, 64, 0, 0, *([None] * 8), 0.125, 0, None) == 0  # empty
 
 
 def test_causal_tile_count_matches_page(fa):
