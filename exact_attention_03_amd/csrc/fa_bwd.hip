@@ -358,6 +358,12 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   __shared__ __attribute__((aligned(1024))) char v0s[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char k1s[C::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v1s[C::TILE_BYTES];
+  // With 16-bit O and the statistics computed here, the O rows of a query
+  // tile are copied into LDS ahead of use (see finish_rows).
+  constexpr bool O_LDS = STATS == kStatsO16;
+  using OTile = CmTile<C::BM>;
+  constexpr int O_BYTES = C::BM * D * 2;
+  __shared__ __attribute__((aligned(1024))) char osm[O_LDS ? O_BYTES : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -429,10 +435,25 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   // here lane half h holds the chunks c = 2t + h, so every butterfly level
   // but the last pairs chunks inside a lane and the last pairs the halves),
   // so that both paths give the same bits.  lse2 and Delta are then written
-  // for the dK/dV pass.
+  // for the dK/dV pass.  16-bit O rows come from LDS, copied there one item
+  // ahead (issue_o), so their latency is hidden; fp32 O rows are loaded here.
+  auto issue_o = [&](int qt) {
+    if constexpr (O_LDS) {
+      const auto ro = make_rsrc((const uint16_t*)o + hoff, head_bytes);
+      const int q0 = qt * C::BM;
+#pragma unroll
+      for (int x = 0; x < O_BYTES / 1024 / C::NW; ++x) {
+        const int blk = ws * (O_BYTES / 1024 / C::NW) + x;
+        const int sl = blk * 64 + lane;
+        const int row = OTile::slot_row(sl), chunk = OTile::slot_chunk(sl);
+        dma16(ro, osm + blk * 1024, (uint32_t)(((q0 + row) * D + 8 * chunk) * 2));
+      }
+    }
+  };
   auto finish_rows = [&](int qt) {
     if constexpr (STATS != kStatsIn) {
       const int query = qt * C::BM + 32 * w + l32;
+      const RowRead<C::BM> ord(32 * w + l32, h);
       float part[C::KSTEPS];
 #pragma unroll
       for (int t = 0; t < C::KSTEPS; ++t) {
@@ -447,8 +468,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
             ov[4 + i] = __uint_as_float(b[i]);
           }
         } else {
-          const auto ro = make_rsrc((const uint16_t*)o + hoff, head_bytes);
-          const u32x4 a = gload16(ro, (uint32_t)((query * D + 16 * t + 8 * h) * 2));
+          const u32x4 a = lds_read16(osm, ord.at(t));
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             ov[2 * i] = lo16_to_f32<T>(a[i]);
@@ -486,8 +506,10 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const TrRead<C::BN> trd(lane);
 
   issue_tile(0, k0s, v0s);
+  issue_o(qt_a);
   load_rows(qt_a);
   bool first_tile_issued = true;
+  bool o_issued = true;  // the current item's O rows are on their way to osm
   for (int it = 0; it < n_items; ++it) {
     const int qt = it == 0 ? qt_a : qt_b;
     const int q0 = qt * C::BM;
@@ -500,7 +522,10 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     // during this item's last tile.
     const bool chain = more && (nt % 2 == 0);
     if (!first_tile_issued) issue_tile(0, k0s, v0s);
-    finish_rows(qt);
+    if (!o_issued) issue_o(qt);  // (an item of one key tile came before)
+    // fp32 O: the statistics right away; 16-bit O: in the first key step,
+    // once the copy into osm has landed.
+    if constexpr (!O_LDS) finish_rows(qt);
 
     f32x16 dqa[C::DB];
 #pragma unroll
@@ -514,6 +539,11 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         issue_tile(j + 1, kn, vn);
       else if (chain)
         issue_tile(0, kn, vn);
+      if constexpr (O_LDS) {
+        if (j == 0) finish_rows(qt);
+        // Every wave has read osm (in step 0): copy the next item's O rows.
+        if (j == 1 && more) issue_o(qt_b);
+      }
       const int kv0 = j * C::BN;
       const bool active = !CAUSAL || kv0 <= wq0 + 31;
       f32x16 s[C::KB], dp[C::KB];
@@ -587,6 +617,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         gstore16(rdq, (uint32_t)((query * D + 32 * db + 16 * half + 8 * h) * 2), pack8<T>(y, 8 * half));
     }
     first_tile_issued = chain;
+    o_issued = nt > 1;
     if (more && !chain) {
       // The ring restarts at stage 0 for the next item; every wave must be
       // done with this item's last tile before it is overwritten.
