@@ -360,7 +360,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   __shared__ __attribute__((aligned(1024))) char v1s[C::TILE_BYTES];
   // With 16-bit O and the statistics computed here, the O rows of a query
   // tile are copied into LDS ahead of use (see finish_rows).
-  constexpr bool O_LDS = STATS == kStatsO16;
+  constexpr bool O_LDS = STATS == kStatsO16 && D <= 128;
   using OTile = CmTile<C::BM>;
   constexpr int O_BYTES = C::BM * D * 2;
   __shared__ __attribute__((aligned(1024))) char osm[O_LDS ? O_BYTES : 16];
@@ -435,8 +435,9 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   // here lane half h holds the chunks c = 2t + h, so every butterfly level
   // but the last pairs chunks inside a lane and the last pairs the halves),
   // so that both paths give the same bits.  lse2 and Delta are then written
-  // for the dK/dV pass.  16-bit O rows come from LDS, copied there one item
-  // ahead (issue_o), so their latency is hidden; fp32 O rows are loaded here.
+  // for the dK/dV pass.  16-bit O rows at D <= 128 come from LDS, copied there
+  // one item ahead (issue_o), so their latency is hidden; fp32 O rows, and
+  // the 64 KiB of a D = 256 tile, are loaded here.
   auto issue_o = [&](int qt) {
     if constexpr (O_LDS) {
       const auto ro = make_rsrc((const uint16_t*)o + hoff, head_bytes);
@@ -468,7 +469,13 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
             ov[4 + i] = __uint_as_float(b[i]);
           }
         } else {
-          const u32x4 a = lds_read16(osm, ord.at(t));
+          u32x4 a;
+          if constexpr (O_LDS) {
+            a = lds_read16(osm, ord.at(t));
+          } else {
+            const auto ro = make_rsrc((const uint16_t*)o + hoff, head_bytes);
+            a = gload16(ro, (uint32_t)((query * D + 16 * t + 8 * h) * 2));
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             ov[2 * i] = lo16_to_f32<T>(a[i]);
