@@ -8,7 +8,9 @@ library (no kernels, headers, helpers, tables or pre/post-processing).
 Every function follows the page titled "把 FlashAttention 搬上昇腾：Triton-Ascend
 CV Pipeline 优化实战" ("Porting FlashAttention to Ascend: CV-pipeline
 optimisation with Triton-Ascend", BiumBiu, 2026-08-30), cited below as
-[FA-Ascend] with the section it comes from.
+[FA-Ascend] with the section it comes from; the grouped key/value heads follow
+the page "从算子到 Serving：昇腾推理评测链路实践" (BiumBiu, 2026-04-30), cited
+as [Serving-Ascend].
 
 Pinning: every function here is pinned by tests marked ``not gpu`` to facts
 other than itself (finite differences, closed forms, invariants, a library
@@ -20,4 +22,7 @@ from .attention import (  # noqa: F401
     attention_forward_full,
     attention_backward,
     loss_sum_o_do,
+    gqa_kv_head,
+    attention_forward_gqa,
+    attention_backward_gqa,
 )

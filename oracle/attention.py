@@ -24,7 +24,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["attention_forward", "attention_forward_full", "attention_backward", "loss_sum_o_do"]
+__all__ = ["attention_forward", "attention_forward_full", "attention_backward", "loss_sum_o_do",
+           "gqa_kv_head", "attention_forward_gqa", "attention_backward_gqa"]
 
 
 def _as_f64(x):
@@ -108,3 +109,65 @@ def loss_sum_o_do(q, k, v, do, scale, causal=False):
     backward pass above, which the finite-difference pin uses."""
     O, _ = attention_forward(q, k, v, scale, causal)
     return float(np.sum(O * _as_f64(do)))
+
+
+# ---------------------------------------------------------------- grouped KV heads
+# [Serving-Ascend] = the page "从算子到 Serving：昇腾推理评测链路实践" (BiumBiu),
+# section "GQA Paged Attention": the number of query heads is an integer
+# multiple of the number of key/value heads, and consecutive query heads share
+# one key/value head (grouped-query attention; one KV head for all query
+# heads is the multi-query case).  Reading of the grouping (listed in
+# DESIGN.md): with G = Hq / Hkv, query head h uses key/value head h // G, the
+# usual contiguous grouping.
+
+
+def gqa_kv_head(h, n_q_heads, n_kv_heads):
+    """Key/value head used by query head h: h // (Hq / Hkv)."""
+    if n_kv_heads <= 0 or n_q_heads % n_kv_heads != 0:
+        raise ValueError("query heads must be a whole multiple of key/value heads")
+    return h // (n_q_heads // n_kv_heads)
+
+
+def attention_forward_gqa(q, k, v, scale, causal=False):
+    """(O, lse) with grouped key/value heads.
+
+    q: (Z, Hq, N, D); k, v: (Z, Hkv, N, D).  Each query head is the plain
+    forward pass of [FA-Ascend] §一 against the key/value head it shares
+    ([Serving-Ascend], "GQA Paged Attention"); O is (Z, Hq, N, D), lse
+    (Z, Hq, N).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    Z, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    O = np.empty_like(q)
+    lse = np.empty(q.shape[:3])
+    for z in range(Z):
+        for h in range(Hq):
+            g = gqa_kv_head(h, Hq, Hkv)
+            O[z, h], lse[z, h] = attention_forward(q[z, h], k[z, g], v[z, g], scale, causal)
+    return O, lse
+
+
+def attention_backward_gqa(q, k, v, do, scale, causal=False):
+    """Backward pass with grouped key/value heads: (dq, dk, dv).
+
+    Each query head's gradients are those of [FA-Ascend] §二 against its
+    key/value head; a key/value head's dK and dV are the sums of the
+    contributions of all query heads that share it (the shared K and V enter
+    each of those heads' scores and outputs).  dq is (Z, Hq, N, D); dk, dv are
+    (Z, Hkv, N, D).
+    """
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    Z, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    dq = np.empty_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for z in range(Z):
+        for h in range(Hq):
+            g = gqa_kv_head(h, Hq, Hkv)
+            r = attention_backward(q[z, h], k[z, g], v[z, g], do[z, h], scale, causal)
+            dq[z, h] = r["dq"]
+            dk[z, g] += r["dk"]
+            dv[z, g] += r["dv"]
+    return dq, dk, dv

@@ -9,7 +9,8 @@ import math
 import numpy as np
 import pytest
 
-from oracle import attention_backward, attention_forward, attention_forward_full, loss_sum_o_do
+from oracle import (attention_backward, attention_backward_gqa, attention_forward, attention_forward_full,
+                    attention_forward_gqa, gqa_kv_head, loss_sum_o_do)
 
 RNG = np.random.default_rng(1234)
 
@@ -248,3 +249,80 @@ def test_closed_form_catches_wrong_causal_diagonal():
     wrong = P @ v
     want = np.cumsum(v, 0) / np.arange(1, n + 1)[:, None]
     assert np.max(np.abs(wrong - want)) > 1e-3
+
+
+# ---------------------------------------------------------------- grouped key/value heads
+# [Serving-Ascend] is the page "从算子到 Serving：昇腾推理评测链路实践" (BiumBiu),
+# section "GQA Paged Attention": query heads a whole multiple of key/value
+# heads, consecutive query heads sharing one.
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_gradient_matches_finite_differences(causal):
+    """dK and dV of a shared key/value head are the gradient of
+    L = sum(O * dO) over all the query heads that use it: central differences
+    over every element of Q, K and V (Z=1, Hq=4, Hkv=2, N=6, D=4)."""
+    rng = np.random.default_rng(43)
+    q = rng.standard_normal((1, 4, 6, 4))
+    k, v = (rng.standard_normal((1, 2, 6, 4)) for _ in range(2))
+    do = rng.standard_normal((1, 4, 6, 4))
+    scale = 0.41
+
+    def loss():
+        O, _ = attention_forward_gqa(q, k, v, scale, causal)
+        return float(np.sum(O * do))
+
+    dq, dk, dv = attention_backward_gqa(q, k, v, do, scale, causal)
+    for g, x in ((dq, q), (dk, k), (dv, v)):
+        fd = _fd_grad(loss, x)
+        assert np.max(np.abs(fd - g)) <= 1e-6 * max(1.0, np.max(np.abs(g)))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (6, 1), (3, 3)])
+def test_gqa_against_torch_sdpa(causal, hq, hkv):
+    """An independent library routine: torch's CPU scaled_dot_product_attention
+    with enable_gqa in float64, forward and autograd backward."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(47 + hq + hkv)
+    q = rng.standard_normal((2, hq, 20, 8))
+    k, v = (rng.standard_normal((2, hkv, 20, 8)) for _ in range(2))
+    do = rng.standard_normal((2, hq, 20, 8))
+    scale = 0.3
+    O, lse = attention_forward_gqa(q, k, v, scale, causal)
+    dq, dk, dv = attention_backward_gqa(q, k, v, do, scale, causal)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale,
+                                                         enable_gqa=True)
+    o.backward(torch.tensor(do))
+    assert np.max(np.abs(o.detach().numpy() - O)) <= 1e-12
+    for g, t in ((dq, tq), (dk, tk), (dv, tv)):
+        assert np.max(np.abs(t.grad.numpy() - g)) <= 1e-12
+
+
+def test_gqa_one_group_is_plain_attention():
+    """Hkv == Hq: every query head has its own key/value head, so the grouped
+    oracle equals the per-head oracle exactly."""
+    rng = np.random.default_rng(53)
+    q, k, v, do = (rng.standard_normal((1, 3, 12, 4)) for _ in range(4))
+    O, lse = attention_forward_gqa(q, k, v, 0.5, True)
+    dq, dk, dv = attention_backward_gqa(q, k, v, do, 0.5, True)
+    r = attention_backward(q, k, v, do, 0.5, True)
+    for a, b in ((O, r["O"]), (lse, r["lse"]), (dq, r["dq"]), (dk, r["dk"]), (dv, r["dv"])):
+        assert np.array_equal(a, b)
+
+
+def test_gqa_head_map_and_planted_interleaving():
+    """Consecutive query heads share a key/value head (h // G); an interleaved
+    map (h % Hkv), a plausible slip, disagrees with torch's grouping."""
+    assert [gqa_kv_head(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+    with pytest.raises(ValueError):
+        gqa_kv_head(0, 6, 4)
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(59)
+    q = rng.standard_normal((1, 4, 10, 4))
+    k, v = (rng.standard_normal((1, 2, 10, 4)) for _ in range(2))
+    o = torch.nn.functional.scaled_dot_product_attention(*(torch.tensor(x) for x in (q, k, v)), scale=0.5,
+                                                         enable_gqa=True).numpy()
+    wrong = np.stack([attention_forward(q[0, h], k[0, h % 2], v[0, h % 2], 0.5)[0] for h in range(4)])
+    assert np.max(np.abs(wrong - o[0])) > 1e-3
