@@ -132,7 +132,11 @@ def cpu_baseline(w, cpu_inputs, n_heads: int, workers: int):
     import numpy as np
 
     n_heads = min(n_heads, w.Z * w.H)
-    flat = [t.reshape(w.Z * w.H, w.N, w.D)[:n_heads].float().numpy() for t in cpu_inputs]
+    G = w.H // w.kv_heads
+    # Each query head with the key/value head it shares (the grouped oracle's
+    # per-head work; its sum of dK / dV over a group is not timed).
+    per_q = [t.repeat_interleave(G, dim=1) if t.shape[1] != w.H else t for t in cpu_inputs]
+    flat = [t.reshape(w.Z * w.H, w.N, w.D)[:n_heads].float().numpy() for t in per_q]
     workers = max(1, min(workers, n_heads))
     chunks = np.array_split(np.arange(n_heads), workers)
     jobs = [tuple(x[c[0]:c[-1] + 1] for x in flat) + (w.scale, w.causal) for c in chunks if len(c)]
@@ -175,7 +179,7 @@ def run(args):
     cpu_inputs = workloads.make_inputs(w)
     q, k, v, do = (t.to(dev) for t in cpu_inputs)
     Z, H, N, D = w.shape
-    tdt = q.dtype
+    Hkv = w.kv_heads
     o = torch.empty_like(q)
     lse = torch.empty((Z, H, N), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -193,17 +197,30 @@ def run(args):
             raise fa.FAError(st, name, fa.last_error())
 
     def step(ev=None):
+        # Grouped key/value heads go through the *_gqa forms of the same calls.
         if ev is not None:
             ev[0].record(stream)
-        call(L.fa_fwd(Z, H, N, D, code, code, P(q), P(k), P(v), P(o), P(lse), scale, causal, sp), "fa_fwd")
+        if Hkv == H:
+            call(L.fa_fwd(Z, H, N, D, code, code, P(q), P(k), P(v), P(o), P(lse), scale, causal, sp), "fa_fwd")
+        else:
+            call(L.fa_fwd_gqa(Z, H, Hkv, N, D, code, code, P(q), P(k), P(v), P(o), P(lse), scale, causal, sp),
+                 "fa_fwd_gqa")
         if ev is not None:
             ev[1].record(stream)
-        call(L.fa_bwd_dq_and_stats(Z, H, N, D, code, code, P(q), P(k), P(v), P(o), P(do), P(lse), P(stats),
-                                   P(dq), scale, causal, sp), "fa_bwd_dq_and_stats")
+        if Hkv == H:
+            call(L.fa_bwd_dq_and_stats(Z, H, N, D, code, code, P(q), P(k), P(v), P(o), P(do), P(lse), P(stats),
+                                       P(dq), scale, causal, sp), "fa_bwd_dq_and_stats")
+        else:
+            call(L.fa_bwd_dq_and_stats_gqa(Z, H, Hkv, N, D, code, code, P(q), P(k), P(v), P(o), P(do), P(lse),
+                                           P(stats), P(dq), scale, causal, sp), "fa_bwd_dq_and_stats_gqa")
         if ev is not None:
             ev[2].record(stream)
-        call(L.fa_bwd_dkdv(Z, H, N, D, code, P(q), P(k), P(v), P(do), P(stats), P(dk), P(dv),
-                           scale, causal, 0, sp), "fa_bwd_dkdv")
+        if Hkv == H:
+            call(L.fa_bwd_dkdv(Z, H, N, D, code, P(q), P(k), P(v), P(do), P(stats), P(dk), P(dv),
+                               scale, causal, 0, sp), "fa_bwd_dkdv")
+        else:
+            call(L.fa_bwd_dkdv_gqa(Z, H, Hkv, N, D, code, P(q), P(k), P(v), P(do), P(stats), P(dk), P(dv),
+                                   scale, causal, 0, sp), "fa_bwd_dkdv_gqa")
         if ev is not None:
             ev[3].record(stream)
 
@@ -282,9 +299,9 @@ def run(args):
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: Z={Z} H={H} N={N} D={D} {w.dtype} causal={bool(w.causal)} "
-                               f"scale={scale:.9g}", "Z": Z, "H": H, "N": N, "D": D, "causal": bool(w.causal),
-                   "seed": w.seed},
+        "config": {"workload": f"{w.name}: Z={Z} H={H}" + (f" Hkv={Hkv}" if Hkv != H else "") +
+                               f" N={N} D={D} {w.dtype} causal={bool(w.causal)} scale={scale:.9g}",
+                   "Z": Z, "H": H, "Hkv": Hkv, "N": N, "D": D, "causal": bool(w.causal), "seed": w.seed},
         "frac_of_peak": round(value / PEAK_MFMA_F16_TFLOPS, 4),
         "breakdown": {
             "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),

@@ -7,6 +7,10 @@ kernels; nothing here computes attention.
 
 The operations follow the page "把 FlashAttention 搬上昇腾：Triton-Ascend CV
 Pipeline 优化实战" (BiumBiu): §一 for the forward, §二 for the backward.
+``forward`` and ``backward`` also take fewer key/value heads than query heads
+(grouped-query attention, the page "从算子到 Serving：昇腾推理评测链路实践",
+section "GQA Paged Attention"): k and v of shape (Z, Hkv, N, D) with H a whole
+multiple of Hkv; query head h uses key/value head h // (H // Hkv).
 """
 from __future__ import annotations
 
@@ -49,6 +53,28 @@ def _check_qkv(*ts, names):
             raise ValueError(f"{n} is on {t.device}, expected {ref.device}")
 
 
+def _check_kv_group(q, k, v, names=("k", "v")):
+    """k, v: (Z, Hkv, N, D) with the batch, length and head dim of q and H a
+    whole multiple of Hkv.  Returns Hkv."""
+    for t, n in zip((k, v), names):
+        if not t.is_cuda:
+            raise ValueError(f"{n} must be a GPU tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{n} must be (Z, Hkv, N, D), got shape {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+        if t.device != q.device:
+            raise ValueError(f"{n} is on {t.device}, expected {q.device}")
+    if k.shape != v.shape:
+        raise ValueError(f"{names[0]} {tuple(k.shape)} and {names[1]} {tuple(v.shape)} differ")
+    Z, H, N, D = q.shape
+    Hkv = k.shape[1]
+    if (k.shape[0], k.shape[2], k.shape[3]) != (Z, N, D) or Hkv == 0 or H % Hkv != 0:
+        raise ValueError(f"{names[0]} has shape {tuple(k.shape)}; expected (Z, Hkv, N, D) = ({Z}, Hkv, {N}, {D}) "
+                         f"with {H} query heads a whole multiple of Hkv")
+    return Hkv
+
+
 def _stream(t):
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
@@ -63,13 +89,15 @@ def _scale(scale, D):
 
 
 def forward(q, k, v, causal=False, scale=None, out_dtype=None):
-    """O, lse = attention(q, k, v).  q, k, v: (Z, H, N, D) fp16/bf16 GPU tensors.
+    """O, lse = attention(q, k, v).  q: (Z, H, N, D), k, v: (Z, H, N, D) or
+    grouped (Z, Hkv, N, D); fp16/bf16 GPU tensors.
 
     out_dtype: dtype of O, either q.dtype (default) or torch.float32.
     Returns O (Z, H, N, D) and lse (Z, H, N) float32 (natural log).
     """
     torch = _torch()
-    _check_qkv(q, k, v, names=("q", "k", "v"))
+    _check_qkv(q, names=("q",))
+    Hkv = _check_kv_group(q, k, v)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k, v must share one dtype")
     Z, H, N, D = q.shape
@@ -77,9 +105,13 @@ def forward(q, k, v, causal=False, scale=None, out_dtype=None):
     with torch.cuda.device(q.device):
         o = torch.empty((Z, H, N, D), dtype=odt, device=q.device)
         lse = torch.empty((Z, H, N), dtype=torch.float32, device=q.device)
-        st = lib().fa_fwd(Z, H, N, D, _dtype_code(q), _dtype_code(o), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                          _ptr(lse), _scale(scale, D), int(bool(causal)), _stream(q))
-    check(st, "fa_fwd")
+        if Hkv == H:
+            st = lib().fa_fwd(Z, H, N, D, _dtype_code(q), _dtype_code(o), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                              _ptr(lse), _scale(scale, D), int(bool(causal)), _stream(q))
+        else:
+            st = lib().fa_fwd_gqa(Z, H, Hkv, N, D, _dtype_code(q), _dtype_code(o), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(o), _ptr(lse), _scale(scale, D), int(bool(causal)), _stream(q))
+    check(st, "fa_fwd" if Hkv == H else "fa_fwd_gqa")
     return o, lse
 
 
@@ -88,14 +120,17 @@ def workspace_bytes(Z, H, N, D):
 
 
 def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None):
-    """dq, dk, dv of attention given dO; o and lse from ``forward``.
+    """dq, dk, dv of attention given dO; o and lse from ``forward``.  k and v
+    may be grouped (Z, Hkv, N, D); dk and dv then have that shape.
 
-    workspace: optional float32 GPU tensor of >= Z*H*N elements (Delta); one
-    is allocated when omitted.
+    workspace: optional float32 GPU tensor of >= 2*Z*H*N elements (the row
+    statistics); one is allocated when omitted.
     """
     torch = _torch()
-    _check_qkv(q, k, v, do, names=("q", "k", "v", "do"))
-    _check_qkv(q, o, names=("q", "o"))
+    _check_qkv(q, do, o, names=("q", "do", "o"))
+    Hkv = _check_kv_group(q, k, v)
+    if k.dtype != q.dtype or v.dtype != q.dtype or do.dtype != q.dtype:
+        raise TypeError("q, k, v, do must share one dtype")
     Z, H, N, D = q.shape
     if lse.shape != (Z, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 (Z, H, N) tensor")
@@ -106,10 +141,16 @@ def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None):
         if workspace is None:
             nbytes = lib().fa_bwd_workspace_bytes(Z, H, N, D)
             workspace = torch.empty((max(1, nbytes // 4),), dtype=torch.float32, device=q.device)
-        st = lib().fa_bwd(Z, H, N, D, _dtype_code(q), _dtype_code(o), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                          _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _scale(scale, D),
-                          int(bool(causal)), _ptr(workspace), workspace.numel() * 4, _stream(q))
-    check(st, "fa_bwd")
+        if workspace.dtype != torch.float32 or not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous float32 GPU tensor")
+        common = (_dtype_code(q), _dtype_code(o), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                  _ptr(dq), _ptr(dk), _ptr(dv), _scale(scale, D), int(bool(causal)), _ptr(workspace),
+                  workspace.numel() * 4, _stream(q))
+        if Hkv == H:
+            st = lib().fa_bwd(Z, H, N, D, *common)
+        else:
+            st = lib().fa_bwd_gqa(Z, H, Hkv, N, D, *common)
+    check(st, "fa_bwd" if Hkv == H else "fa_bwd_gqa")
     return dq, dk, dv
 
 

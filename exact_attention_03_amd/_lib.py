@@ -35,6 +35,13 @@ SIGNATURES = {
     "fa_bwd_dq": (_int, [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _int, _vp]),
     "fa_bwd_dq_and_stats": (_int, [_i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    _f32, _int, _vp]),
+    "fa_fwd_gqa": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _f32, _int, _vp]),
+    "fa_bwd_gqa": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                          _f32, _int, _vp, _sz, _vp]),
+    "fa_bwd_dq_and_stats_gqa": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, _vp, _f32, _int, _vp]),
+    "fa_bwd_dkdv_gqa": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _int,
+                               _int, _vp]),
     "fa_device_info": (_int, [_i64, _int, _intp, _intp]),
     "fa_dkdv_schedule": (_int, [_i64, _i64, _i64, _i64, _int, _int, _i64p, _i64p, _i64p]),
     "fa_fwd_tile_pairs": (_int, [_i64, _i64, _int, _i64p, _i64p]),

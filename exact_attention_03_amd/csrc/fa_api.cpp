@@ -71,6 +71,26 @@ int check_shape(const Shape& s) {
   return FA_OK;
 }
 
+// Grouped key/value heads: H query heads over Hkv key/value heads, H a whole
+// multiple of Hkv.  The dK/dV pass indexes the G = H / Hkv query heads of a
+// group with one 32-bit byte offset.
+int check_groups(const Shape& s, int64_t Hkv) {
+  if (Hkv < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative Hkv=%lld", (long long)Hkv);
+  if (s.H == 0) return FA_OK;
+  if (Hkv == 0 || s.H % Hkv != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "H=%lld query heads must be a whole multiple of Hkv=%lld key/value heads",
+                (long long)s.H, (long long)Hkv);
+  const int64_t G = s.H / Hkv;
+  if (!s.empty() && G * (s.N + 256) * s.D * 2 > kMaxI32)
+    return fail(FA_ERR_UNSUPPORTED, "group too large (H/Hkv=%lld N=%lld D=%lld)", (long long)G, (long long)s.N,
+                (long long)s.D);
+  // Query-tile grids pad the key/value heads to a multiple of the XCD count.
+  if (!s.empty() && (s.Z * Hkv + fa::kXcds) * G * ((s.N + 63) / 64) > kMaxI32)
+    return fail(FA_ERR_UNSUPPORTED, "grid too large (Z*Hkv=%lld H/Hkv=%lld N=%lld)", (long long)(s.Z * Hkv),
+                (long long)G, (long long)s.N);
+  return FA_OK;
+}
+
 int check_dtypes(int dtype, int o_dtype, bool need_o) {
   if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
     return fail(FA_ERR_INVALID_ARGUMENT, "dtype %d must be FA_DTYPE_F16 or FA_DTYPE_BF16", dtype);
@@ -181,11 +201,16 @@ size_t fa_bwd_workspace_bytes(int64_t Z, int64_t H, int64_t N, int64_t D) {
   return 2 * (size_t)(Z * H * N) * sizeof(float);
 }
 
-int fa_fwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, const void* q, const void* k,
-           const void* v, void* o, float* lse, float scale, int causal, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int fwd_impl(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype, int o_dtype, const void* q,
+             const void* k, const void* v, void* o, float* lse, float scale, int causal, hipStream_t stream) {
   g_last_error.clear();
   const Shape s{Z, H, N, D};
   FA_TRY(check_shape(s));
+  FA_TRY(check_groups(s, Hkv));
   FA_TRY(check_dtypes(dtype, o_dtype, true));
   FA_TRY(check_scale(scale, causal));
   if (s.empty()) return FA_OK;
@@ -194,8 +219,22 @@ int fa_fwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, c
   FA_TRY(check_ptr(v, "v"));
   FA_TRY(check_ptr(o, "o"));
   FA_TRY(check_ptr(lse, "lse"));
-  fa::FwdArgs a{Z, H, N, D, dtype, o_dtype, q, k, v, o, lse, scale, causal, stream};
+  fa::FwdArgs a{Z, H, N, D, Hkv, dtype, o_dtype, q, k, v, o, lse, scale, causal, stream};
   return finish(fa::launch_fwd(a), stream, "fa_fwd launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, const void* q, const void* k,
+           const void* v, void* o, float* lse, float scale, int causal, hipStream_t stream) {
+  return fwd_impl(Z, H, H, N, D, dtype, o_dtype, q, k, v, o, lse, scale, causal, stream);
+}
+
+int fa_fwd_gqa(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype, int o_dtype, const void* q,
+               const void* k, const void* v, void* o, float* lse, float scale, int causal, hipStream_t stream) {
+  return fwd_impl(Z, H, Hkv, N, D, dtype, o_dtype, q, k, v, o, lse, scale, causal, stream);
 }
 
 int fa_bwd_preprocess(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, const void* o,
@@ -210,17 +249,22 @@ int fa_bwd_preprocess(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int
   FA_TRY(check_ptr(lse, "lse"));
   FA_TRY(check_ptr(stats, "stats"));
   fa::BwdArgs a{};
-  a.Z = Z; a.H = H; a.N = N; a.D = D; a.dtype = dtype; a.o_dtype = o_dtype;
+  a.Z = Z; a.H = H; a.Hkv = H; a.N = N; a.D = D; a.dtype = dtype; a.o_dtype = o_dtype;
   a.o = o; a.dout = dout; a.lse = lse; a.stats = stats; a.stream = stream;
   return finish(fa::launch_bwd_pre(a), stream, "fa_bwd_preprocess launch");
 }
 
-int fa_bwd_dkdv(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, const void* q, const void* k,
-                const void* v, const void* dout, const float* stats, void* dk, void* dv, float scale,
-                int causal, int num_programs, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int dkdv_impl(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype, const void* q, const void* k,
+              const void* v, const void* dout, const float* stats, void* dk, void* dv, float scale, int causal,
+              int num_programs, hipStream_t stream) {
   g_last_error.clear();
   const Shape s{Z, H, N, D};
   FA_TRY(validate_bwd_common(s, dtype, q, k, v, dout, stats, scale, causal));
+  FA_TRY(check_groups(s, Hkv));
   if (num_programs < 0) return fail(FA_ERR_INVALID_ARGUMENT, "num_programs must be >= 0 (got %d)", num_programs);
   if (s.empty()) return FA_OK;
   FA_TRY(check_ptr(dk, "dk"));
@@ -231,10 +275,20 @@ int fa_bwd_dkdv(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, const voi
     num_programs = f->cus * f->dkdv_per_cu[d_index(D)][dtype];
   }
   fa::BwdArgs a{};
-  a.Z = Z; a.H = H; a.N = N; a.D = D; a.dtype = dtype;
+  a.Z = Z; a.H = H; a.Hkv = Hkv; a.N = N; a.D = D; a.dtype = dtype;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.stats = const_cast<float*>(stats);
   a.dk = dk; a.dv = dv; a.scale = scale; a.causal = causal; a.num_programs = num_programs; a.stream = stream;
   return finish(fa::launch_bwd_dkdv(a), stream, "fa_bwd_dkdv launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_dkdv(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, const void* q, const void* k,
+                const void* v, const void* dout, const float* stats, void* dk, void* dv, float scale,
+                int causal, int num_programs, hipStream_t stream) {
+  return dkdv_impl(Z, H, H, N, D, dtype, q, k, v, dout, stats, dk, dv, scale, causal, num_programs, stream);
 }
 
 int fa_bwd_dq(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, const void* q, const void* k,
@@ -246,18 +300,23 @@ int fa_bwd_dq(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, const void*
   if (s.empty()) return FA_OK;
   FA_TRY(check_ptr(dq, "dq"));
   fa::BwdArgs a{};
-  a.Z = Z; a.H = H; a.N = N; a.D = D; a.dtype = dtype;
+  a.Z = Z; a.H = H; a.Hkv = H; a.N = N; a.D = D; a.dtype = dtype;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.stats = const_cast<float*>(stats);
   a.dq = dq; a.scale = scale; a.causal = causal; a.stream = stream;
   return finish(fa::launch_bwd_dq(a), stream, "fa_bwd_dq launch");
 }
 
-int fa_bwd_dq_and_stats(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, const void* q,
-                        const void* k, const void* v, const void* o, const void* dout, const float* lse,
-                        float* stats, void* dq, float scale, int causal, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int dq_and_stats_impl(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype, int o_dtype,
+                      const void* q, const void* k, const void* v, const void* o, const void* dout,
+                      const float* lse, float* stats, void* dq, float scale, int causal, hipStream_t stream) {
   g_last_error.clear();
   const Shape s{Z, H, N, D};
   FA_TRY(check_shape(s));
+  FA_TRY(check_groups(s, Hkv));
   FA_TRY(check_dtypes(dtype, o_dtype, true));
   FA_TRY(check_scale(scale, causal));
   if (s.empty()) return FA_OK;
@@ -270,18 +329,21 @@ int fa_bwd_dq_and_stats(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, i
   FA_TRY(check_ptr(stats, "stats"));
   FA_TRY(check_ptr(dq, "dq"));
   fa::BwdArgs a{};
-  a.Z = Z; a.H = H; a.N = N; a.D = D; a.dtype = dtype; a.o_dtype = o_dtype;
+  a.Z = Z; a.H = H; a.Hkv = Hkv; a.N = N; a.D = D; a.dtype = dtype; a.o_dtype = o_dtype;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.stats = stats;
   a.dq = dq; a.scale = scale; a.causal = causal; a.dq_stats = true; a.stream = stream;
   return finish(fa::launch_bwd_dq(a), stream, "fa_bwd_dq_and_stats launch");
 }
 
-int fa_bwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, const void* q, const void* k,
-           const void* v, const void* o, const void* dout, const float* lse, void* dq, void* dk, void* dv,
-           float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Both gradient passes: dQ with the row statistics into the workspace, then
+// dK / dV from them.
+int bwd_impl(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype, int o_dtype, const void* q,
+             const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq, void* dk,
+             void* dv, float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   g_last_error.clear();
   const Shape s{Z, H, N, D};
   FA_TRY(check_shape(s));
+  FA_TRY(check_groups(s, Hkv));
   FA_TRY(check_dtypes(dtype, o_dtype, true));
   FA_TRY(check_scale(scale, causal));
   if (s.empty()) return FA_OK;
@@ -300,9 +362,46 @@ int fa_bwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, c
     return fail(FA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu bytes needed",
                 workspace_bytes, need);
   float* stats = static_cast<float*>(workspace);
-  FA_TRY(fa_bwd_dq_and_stats(Z, H, N, D, dtype, o_dtype, q, k, v, o, dout, lse, stats, dq, scale, causal, stream));
-  FA_TRY(fa_bwd_dkdv(Z, H, N, D, dtype, q, k, v, dout, stats, dk, dv, scale, causal, 0, stream));
+  FA_TRY(dq_and_stats_impl(Z, H, Hkv, N, D, dtype, o_dtype, q, k, v, o, dout, lse, stats, dq, scale, causal,
+                           stream));
+  FA_TRY(dkdv_impl(Z, H, Hkv, N, D, dtype, q, k, v, dout, stats, dk, dv, scale, causal, 0, stream));
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd_dq_and_stats(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, const void* q,
+                        const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                        float* stats, void* dq, float scale, int causal, hipStream_t stream) {
+  return dq_and_stats_impl(Z, H, H, N, D, dtype, o_dtype, q, k, v, o, dout, lse, stats, dq, scale, causal, stream);
+}
+
+int fa_bwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, const void* q, const void* k,
+           const void* v, const void* o, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(Z, H, H, N, D, dtype, o_dtype, q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace,
+                  workspace_bytes, stream);
+}
+
+int fa_bwd_gqa(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype, int o_dtype, const void* q,
+               const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq, void* dk,
+               void* dv, float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(Z, H, Hkv, N, D, dtype, o_dtype, q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace,
+                  workspace_bytes, stream);
+}
+
+int fa_bwd_dq_and_stats_gqa(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype, int o_dtype,
+                            const void* q, const void* k, const void* v, const void* o, const void* dout,
+                            const float* lse, float* stats, void* dq, float scale, int causal, hipStream_t stream) {
+  return dq_and_stats_impl(Z, H, Hkv, N, D, dtype, o_dtype, q, k, v, o, dout, lse, stats, dq, scale, causal, stream);
+}
+
+int fa_bwd_dkdv_gqa(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype, const void* q,
+                    const void* k, const void* v, const void* dout, const float* stats, void* dk, void* dv,
+                    float scale, int causal, int num_programs, hipStream_t stream) {
+  return dkdv_impl(Z, H, Hkv, N, D, dtype, q, k, v, dout, stats, dk, dv, scale, causal, num_programs, stream);
 }
 
 int fa_device_info(int64_t D, int dtype, int* compute_units, int* dkdv_programs) {

@@ -123,8 +123,8 @@ __attribute__((amdgpu_waves_per_eu(DkdvTile<D>::OCC, DkdvTile<D>::OCC)))
 void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                         const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                         const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
-                        uint16_t* __restrict__ dv, int N, int ZH, int n_ktiles, int n_qtiles, float c2, float scale,
-                        int P) {
+                        uint16_t* __restrict__ dv, int N, int ZHkv, int G, int n_ktiles, int n_qtiles, float c2,
+                        float scale, int P) {
   using C = DkdvTile<D>;
   using QTile = CmTile<C::BQ>;
   using VTile = CmTile<C::BK>;
@@ -144,25 +144,31 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   const uint32_t head_bytes = (uint32_t)N * D * 2;
 
   for (int64_t round = 0;; ++round) {
-    int64_t head64, kt64;
-    if (!sched_unit(round, blockIdx.x, P, ZH, n_ktiles, &head64, &kt64)) break;  // uniform
-    const int kt = (int)kt64, head = (int)head64;
+    int64_t kvh64, kt64;
+    if (!sched_unit(round, blockIdx.x, P, ZHkv, n_ktiles, &kvh64, &kt64)) break;  // uniform
+    const int kt = (int)kt64, kvh = (int)kvh64;
     const int k0 = kt * C::BK;
     const int kw0 = k0 + 32 * w;  // first key of this wave
-    const size_t hoff = (size_t)head * (size_t)N * D;
-    const auto rq = make_rsrc(q + hoff, head_bytes);
-    const auto rk = make_rsrc(k + hoff, head_bytes);
-    const auto rv = make_rsrc(v + hoff, head_bytes);
-    const auto rdo = make_rsrc(dout + hoff, head_bytes);
-    const auto rl = make_rsrc(lse2 + (size_t)head * N, (uint32_t)N * 4);
-    const auto rd = make_rsrc(delta + (size_t)head * N, (uint32_t)N * 4);
+    // The unit's key/value head kvh serves query heads kvh*G .. kvh*G+G-1
+    // (G = 1 without grouping), which lie next to each other in Q, dO and
+    // the statistics: one buffer resource spans the G heads and a member's
+    // rows start at member * N.
+    const size_t kvoff = (size_t)kvh * (size_t)N * D;
+    const size_t goff = kvoff * (size_t)G;
+    const auto rq = make_rsrc(q + goff, head_bytes * (uint32_t)G);
+    const auto rk = make_rsrc(k + kvoff, head_bytes);
+    const auto rv = make_rsrc(v + kvoff, head_bytes);
+    const auto rdo = make_rsrc(dout + goff, head_bytes * (uint32_t)G);
+    const auto rl = make_rsrc(lse2 + (size_t)kvh * G * N, (uint32_t)(N * G) * 4);
+    const auto rd = make_rsrc(delta + (size_t)kvh * G * N, (uint32_t)(N * G) * 4);
     const int i0 = (int)sched_first_qtile(kt, C::BK, C::BQ, CAUSAL);
     const int nq = n_qtiles - i0;
+    const int n_items = nq * G;  // (member, query tile) pairs, member-major
 
-    // Copy query tile i (Q, dO, and the lse2 / Delta values from its first
-    // query on) into ring stage st.
-    auto issue_qtile = [&](int i, char* base) {
-      const int qq0 = i * C::BQ;
+    // Copy query tile i of member m (Q, dO, and the lse2 / Delta values from
+    // its first query on) into ring stage st.
+    auto issue_qtile = [&](int m, int i, char* base) {
+      const int qq0 = m * N + i * C::BQ;  // row in the group's stacked rows
 #pragma unroll(C::COPY_UNROLL)
       for (int x = 0; x < C::QCOPIES / C::NW; ++x) {
         const int blk = w * (C::QCOPIES / C::NW) + x;
@@ -187,7 +193,7 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
         dma16(rv, vsm + blk * 1024, (uint32_t)(((k0 + row) * D + 8 * chunk) * 2));
       }
     }
-    issue_qtile(i0, st0);
+    issue_qtile(0, i0, st0);
 
     // K (and V) rows of this wave's keys, B-operand layout (lane = key, k = d).
     u32x4 kf[C::KSTEPS];
@@ -212,12 +218,19 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     const char* vbase = vsm + kRowBlockBytes * w;
     const TrRead<C::BQ> trd(lane);
 
-    // Query tile it, read from stage cs; the copy of tile it+1 goes to ns.
-    auto qtile = [&](int it, const char* cs, char* ns) {
-      // Tile it has landed for every wave; every wave is done with tile it-1.
+    // Item (member cm, query tile i0 + cit), read from stage cs; the copy of
+    // the next item goes to ns.
+    int cm = 0, cit = 0;
+    auto qtile = [&](const char* cs, char* ns) {
+      // The item has landed for every wave; every wave is done with the last.
       wait_vmem();
       __syncthreads();
-      if (it + 1 < nq) issue_qtile(i0 + it + 1, ns);
+      const int it = cit;
+      const bool wrap = cit + 1 == nq;
+      const int nm = wrap ? cm + 1 : cm;
+      cit = wrap ? 0 : cit + 1;
+      if (nm < G) issue_qtile(nm, i0 + cit, ns);
+      cm = nm;
       const int qb0 = (i0 + it) * C::BQ;  // first query of the tile
       // Causal: a tile whose last query precedes the wave's first key is empty.
       if (CAUSAL && qb0 + 31 < kw0) return;
@@ -281,18 +294,18 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
       }
     };
     if constexpr (C::PAIRS) {
-      for (int it = 0; it < nq; it += 2) {
-        qtile(it, st0, st1);
-        if (it + 1 < nq) qtile(it + 1, st1, st0);
+      for (int f = 0; f < n_items; f += 2) {
+        qtile(st0, st1);
+        if (f + 1 < n_items) qtile(st1, st0);
       }
     } else {
-      for (int it = 0; it < nq; ++it) qtile(it, (it & 1) ? st1 : st0, (it & 1) ? st0 : st1);
+      for (int f = 0; f < n_items; ++f) qtile((f & 1) ? st1 : st0, (f & 1) ? st0 : st1);
     }
 
     // Single write of this wave's dK and dV rows.  Register jj of block db
     // holds d = 32db + 16(jj/8) + 8h + jj%8 of key kw0 + l32.
-    const auto rdk = make_rsrc(dk + hoff, head_bytes);
-    const auto rdv = make_rsrc(dv + hoff, head_bytes);
+    const auto rdk = make_rsrc(dk + kvoff, head_bytes);
+    const auto rdv = make_rsrc(dv + kvoff, head_bytes);
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
       const f32x16 ks = dka[db] * scale;
@@ -348,7 +361,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                       const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dq,
                       int N, int ZH, int n_qtiles, float c2, float scale, const void* __restrict__ o,
-                      const float* __restrict__ lse, float* __restrict__ stats_out) {
+                      const float* __restrict__ lse, float* __restrict__ stats_out, int ZHkv, int G) {
   using C = DqTile<D>;
   using Tile = CmTile<C::BN>;
   // One LDS object per ring stage and operand, accessed with compile-time
@@ -376,17 +389,19 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const int l32 = lane & 31;
   // Query tiles of this workgroup: one, or with the causal mask a long and a
   // short one of the same head.
-  int64_t head64, slot64, qt_a64, qt_b64;
-  xcd_tile(blockIdx.x, paired_groups(n_qtiles, CAUSAL), &head64, &slot64);
-  if (head64 >= ZH) return;  // padding block
+  // Query head `head` (of ZH) reads key/value head kvh = head / G (of ZHkv).
+  int64_t kvh64, head64, slot64, qt_a64, qt_b64;
+  xcd_tile_grouped(blockIdx.x, G, paired_groups(n_qtiles, CAUSAL), &kvh64, &head64, &slot64);
+  if (kvh64 >= ZHkv) return;  // padding block
   const int head = (int)head64;
   const int n_items = paired_items(slot64, n_qtiles, CAUSAL, &qt_a64, &qt_b64);
   const int qt_a = (int)qt_a64, qt_b = (int)qt_b64;
   const size_t hoff = (size_t)head * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const size_t kvoff = (size_t)kvh64 * (size_t)N * D;
   const auto rq = make_rsrc(q + hoff, head_bytes);
-  const auto rk = make_rsrc(k + hoff, head_bytes);
-  const auto rv = make_rsrc(v + hoff, head_bytes);
+  const auto rk = make_rsrc(k + kvoff, head_bytes);
+  const auto rv = make_rsrc(v + kvoff, head_bytes);
   const auto rdo = make_rsrc(dout + hoff, head_bytes);
   const auto rl = STATS == kStatsIn ? make_rsrc(lse2 + (size_t)head * N, (uint32_t)N * 4)
                                     : make_rsrc(lse + (size_t)head * N, (uint32_t)N * 4);
@@ -662,13 +677,14 @@ hipError_t launch_bwd_pre(const BwdArgs& a) {
 template <int D, typename T, bool CAUSAL>
 static hipError_t launch_dkdv_t(const BwdArgs& a) {
   using C = DkdvTile<D>;
-  const int ZH = (int)(a.Z * a.H);
+  const int ZHkv = (int)(a.Z * a.Hkv);
+  const int G = (int)(a.H / a.Hkv);
   const int n_kt = (int)((a.N + C::BK - 1) / C::BK);
   const int n_qt = (int)((a.N + C::BQ - 1) / C::BQ);
   hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, T, CAUSAL>), dim3((unsigned)a.num_programs), dim3(C::NW * 64), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.stats + a.Z * a.H * a.N, a.stats, (uint16_t*)a.dk, (uint16_t*)a.dv, (int)a.N,
-                     ZH, n_kt, n_qt, a.scale * kLog2e, a.scale, a.num_programs);
+                     ZHkv, G, n_kt, n_qt, a.scale * kLog2e, a.scale, a.num_programs);
   return hipGetLastError();
 }
 template <int D, typename T>
@@ -713,12 +729,14 @@ template <int D, typename T, bool CAUSAL, int STATS>
 static hipError_t launch_dq_t(const BwdArgs& a) {
   using C = DqTile<D>;
   const int ZH = (int)(a.Z * a.H);
+  const int ZHkv = (int)(a.Z * a.Hkv);
+  const int G = (int)(a.H / a.Hkv);
   const int n_qt = (int)((a.N + C::BM - 1) / C::BM);
   hipLaunchKernelGGL((fa_bwd_dq_kernel<D, T, CAUSAL, STATS>),
-                     dim3((unsigned)xcd_grid(ZH, paired_groups(n_qt, CAUSAL))), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     dim3((unsigned)xcd_grid_grouped(ZHkv, G, paired_groups(n_qt, CAUSAL))), dim3(256), 0,
+                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.stats + a.Z * a.H * a.N, a.stats, (uint16_t*)a.dq, (int)a.N, ZH, n_qt,
-                     a.scale * kLog2e, a.scale, a.o, a.lse, a.stats);
+                     a.scale * kLog2e, a.scale, a.o, a.lse, a.stats, ZHkv, G);
   return hipGetLastError();
 }
 template <int D, typename T, int STATS>

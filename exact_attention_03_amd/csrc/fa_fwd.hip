@@ -71,7 +71,7 @@ template <int D, typename T, bool CAUSAL, typename OT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdTile<D>::OCC, FwdTile<D>::OCC)))
 void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, void* __restrict__ o, float* __restrict__ lse, int N,
-                   int ZH, int n_qtiles, float c2) {
+                   int ZHkv, int G, int n_qtiles, float c2) {
   using C = FwdTile<D>;
   using Tile = CmTile<C::BN>;
   // One LDS object per ring stage and operand.  With the stage of every
@@ -91,17 +91,19 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 
   // Query tiles of this workgroup: one, or with the causal mask a long and a
   // short one of the same head (the longest pairs go first).
-  int64_t head64, slot64, qt_a64, qt_b64;
-  xcd_tile(blockIdx.x, paired_groups(n_qtiles, CAUSAL), &head64, &slot64);
-  if (head64 >= ZH) return;  // padding block
+  // Query head `head` reads key/value head `kvh` (head / G).
+  int64_t kvh64, head64, slot64, qt_a64, qt_b64;
+  xcd_tile_grouped(blockIdx.x, G, paired_groups(n_qtiles, CAUSAL), &kvh64, &head64, &slot64);
+  if (kvh64 >= ZHkv) return;  // padding block
   const int n_items = paired_items(slot64, n_qtiles, CAUSAL, &qt_a64, &qt_b64);
   const int qt_a = (int)qt_a64, qt_b = (int)qt_b64;
   const int head = (int)head64;
   const size_t hoff = (size_t)head * (size_t)N * D;
+  const size_t kvoff = (size_t)kvh64 * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc(q + hoff, head_bytes);
-  const auto rk = make_rsrc(k + hoff, head_bytes);
-  const auto rv = make_rsrc(v + hoff, head_bytes);
+  const auto rk = make_rsrc(k + kvoff, head_bytes);
+  const auto rv = make_rsrc(v + kvoff, head_bytes);
 
   // Copy K/V tile j into a ring stage (chunk-major layout, see CmTile).
   auto issue_tile = [&](int j, char* kdst, char* vdst) {
@@ -299,11 +301,12 @@ template <int D, typename T, bool CAUSAL, typename OT>
 hipError_t launch_fwd_t(const FwdArgs& a) {
   using C = FwdTile<D>;
   const int n_qtiles = (int)((a.N + C::BM - 1) / C::BM);
-  const int ZH = (int)(a.Z * a.H);
-  const dim3 grid((unsigned)xcd_grid(ZH, paired_groups(n_qtiles, CAUSAL)));
+  const int ZHkv = (int)(a.Z * a.Hkv);
+  const int G = (int)(a.H / a.Hkv);
+  const dim3 grid((unsigned)xcd_grid_grouped(ZHkv, G, paired_groups(n_qtiles, CAUSAL)));
   hipLaunchKernelGGL((fa_fwd_kernel<D, T, CAUSAL, OT>), grid, dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.lse,
-                     (int)a.N, ZH, n_qtiles, a.scale * kLog2e);
+                     (int)a.N, ZHkv, G, n_qtiles, a.scale * kLog2e);
   return hipGetLastError();
 }
 

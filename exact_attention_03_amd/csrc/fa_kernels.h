@@ -8,6 +8,7 @@ namespace fa {
 
 struct FwdArgs {
   int64_t Z, H, N, D;
+  int64_t Hkv;  // key/value heads (H a whole multiple of it; H for plain attention)
   int dtype, o_dtype;
   const void *q, *k, *v;
   void* o;
@@ -19,6 +20,7 @@ struct FwdArgs {
 
 struct BwdArgs {
   int64_t Z, H, N, D;
+  int64_t Hkv;  // key/value heads (H a whole multiple of it; H for plain attention)
   int dtype, o_dtype;
   const void *q, *k, *v, *o, *dout;
   const float* lse;  // preprocess input

@@ -100,4 +100,20 @@ FA_SCHED_HD void xcd_tile(int64_t b, int64_t n_qtiles, int64_t* head, int64_t* s
   *slot = s % n_qtiles;
 }
 
+// Grouped key/value heads (G query heads share one key/value head): the
+// forward and dQ grids deal (key/value head, member, slot) so that the G
+// query heads of a key/value head run on one XCD, back to back, and share its
+// K and V through that XCD's L2.  Query head = kv_head * G + member.  With
+// G = 1 this is xcd_tile over query heads.
+FA_SCHED_HD int64_t xcd_grid_grouped(int64_t ZHkv, int64_t G, int64_t n_slots) {
+  return xcd_grid(ZHkv, G * n_slots);
+}
+FA_SCHED_HD void xcd_tile_grouped(int64_t b, int64_t G, int64_t n_slots, int64_t* kv_head, int64_t* head,
+                                  int64_t* slot) {
+  int64_t s;
+  xcd_tile(b, G * n_slots, kv_head, &s);
+  *head = *kv_head * G + s / n_slots;
+  *slot = s % n_slots;
+}
+
 }  // namespace fa

@@ -165,6 +165,50 @@ int fa_bwd_dq_and_stats(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype,
                         hipStream_t stream);
 
 /*
+ * Grouped key/value heads (GQA; MQA when Hkv = 1).  The page "从算子到
+ * Serving：昇腾推理评测链路实践" (BiumBiu), section "GQA Paged Attention",
+ * cited as [Serving-Ascend], lets H query heads share Hkv key/value heads, H a
+ * whole multiple of Hkv: query head h attends with key/value head h / G,
+ * G = H / Hkv.  The operation per query head is that of fa_fwd / fa_bwd; the
+ * gradients of a shared key/value head are the sums over its G query heads.
+ *   q, o, dout, dq : (Z,H,N,D);  k, v, dk, dv : (Z,Hkv,N,D);  lse : (Z,H,N).
+ *   workspace      : fa_bwd_workspace_bytes(Z, H, N, D) (query heads).
+ * Other arguments, the result and the errors are those of fa_fwd and fa_bwd;
+ * in addition FA_ERR_INVALID_ARGUMENT if Hkv <= 0 (with H > 0) or H is not a
+ * multiple of Hkv, and FA_ERR_UNSUPPORTED if G * (N + 256) * D * 2 reaches
+ * 2^31 (one group is indexed with 32-bit offsets).  With Hkv = H these are
+ * fa_fwd and fa_bwd, bitwise.  The G query heads of one key/value head run on
+ * one XCD and share its K and V through that XCD's L2; dK / dV are written
+ * once per key tile by the workgroup that walks all G query heads of it (no
+ * atomics).
+ */
+int fa_fwd_gqa(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype,
+               int o_dtype, const void* q, const void* k, const void* v, void* o,
+               float* lse, float scale, int causal, hipStream_t stream);
+int fa_bwd_gqa(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype,
+               int o_dtype, const void* q, const void* k, const void* v,
+               const void* o, const void* dout, const float* lse, void* dq,
+               void* dk, void* dv, float scale, int causal, void* workspace,
+               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The two stages fa_bwd_gqa runs, for callers that schedule them (or time
+ * them) one by one: fa_bwd_dq_and_stats and fa_bwd_dkdv with Hkv key/value
+ * heads, arguments and shapes as above (stats: (2,Z,H,N) over query heads).
+ * fa_bwd_dkdv_gqa's persistent workgroups own (key/value head, key tile)
+ * units and walk the query tiles of all G query heads of their head.
+ */
+int fa_bwd_dq_and_stats_gqa(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D,
+                            int dtype, int o_dtype, const void* q, const void* k,
+                            const void* v, const void* o, const void* dout,
+                            const float* lse, float* stats, void* dq, float scale,
+                            int causal, hipStream_t stream);
+int fa_bwd_dkdv_gqa(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype,
+                    const void* q, const void* k, const void* v, const void* dout,
+                    const float* stats, void* dk, void* dv, float scale, int causal,
+                    int num_programs, hipStream_t stream);
+
+/*
  * Device facts used for launch sizing, for the current device: compute
  * units, and the persistent grid fa_bwd_dkdv uses for (D, dtype) when
  * num_programs is 0.  Either output pointer may be NULL.

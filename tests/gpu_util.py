@@ -98,3 +98,19 @@ ZERO_REF_MAX_ABS = 1e-3  # max-abs bound used when the exact gradient is zero
 O_MAX_ABS = 1e-2      # max-abs error of the fp32 O
 GRAD_NORMWISE = 2e-2  # normwise relative error of dQ, dK, dV
 LSE_MAX_ABS = 1e-3    # max-abs error of lse (natural log)
+
+
+def oracle_group(cpu, z, kvh, scale, causal):
+    """Oracle for key/value head (z, kvh) of a grouped-head input and every
+    query head that shares it: {"heads": [query heads], "O", "lse", "dq"
+    (stacked over those heads), "dk", "dv" (of the key/value head)}."""
+    q, k, v, do = cpu
+    H, Hkv = q.shape[1], k.shape[1]
+    G = H // Hkv
+    heads = list(range(kvh * G, (kvh + 1) * G))
+    sl = slice(heads[0], heads[-1] + 1)
+    qq, dd = to_f64(q[z:z + 1, sl]), to_f64(do[z:z + 1, sl])
+    kk, vv = to_f64(k[z:z + 1, kvh:kvh + 1]), to_f64(v[z:z + 1, kvh:kvh + 1])
+    O, lse = oracle.attention_forward_gqa(qq, kk, vv, scale, causal)
+    dq, dk, dv = oracle.attention_backward_gqa(qq, kk, vv, dd, scale, causal)
+    return {"heads": heads, "O": O[0], "lse": lse[0], "dq": dq[0], "dk": dk[0, 0], "dv": dv[0, 0]}

@@ -150,3 +150,23 @@ def test_workspace_versus_page_full_scratch(fa):
     assert full == g["one_copy_bytes"]
     ours = fa.workspace_bytes(g["Z"], g["H"], g["N"], 128)
     assert ours == 2 * g["Z"] * g["H"] * g["N"] * 4 and ours * 256 == full
+
+
+def test_grouped_head_argument_errors(fa):
+    lib = fa.lib()
+
+    def fwd(H, Hkv, N=128, D=64):
+        return lib.fa_fwd_gqa(1, H, Hkv, N, D, 0, 0, P, P, P, P, P, 0.125, 0, None)
+
+    def bwd(H, Hkv, N=128, D=64):
+        return lib.fa_bwd_gqa(1, H, Hkv, N, D, 0, 0, *([P] * 9), 0.125, 0, P, 1 << 30, None)
+
+    for f in (fwd, bwd):
+        assert f(6, 4) == 1 and "multiple" in fa.last_error()  # 6 query heads over 4
+        assert f(4, 0) == 1
+        assert f(4, -1) == 1
+        assert f(4, 8) == 1                                  # more key/value heads than query heads
+        assert f(1 << 14, 1, N=1 << 16, D=128) == 2          # one group beyond 32-bit offsets
+        assert "group" in fa.last_error()
+    assert lib.fa_fwd_gqa(1, 0, 0, 128, 64, 0, 0, *([None] * 5), 0.125, 0, None) == 0  # no heads: empty
+    assert lib.fa_bwd_gqa(0, 4, 2, 128, 64, 0, 0, *([None] * 9), 0.125, 0, None, 0, None) == 0

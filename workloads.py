@@ -8,7 +8,8 @@ Recipe (one generator per workload, PCG64 through ``numpy.random.default_rng``):
 
 * seed = the workload's index (1..5);
 * draw, in this order, ``q, k, v, do`` as ``standard_normal(shape, float32)``
-  with shape (Z, H, N, D);
+  with shape (Z, H, N, D) for q and do and (Z, Hkv, N, D) for k and v (Hkv =
+  H except for the grouped key/value head workload);
 * for the long-sequence workload only, multiply q and k by 2 in float32 (exact),
   which sharpens the softmax and exercises the running-max rescaling;
 * cast to the workload's dtype with round-to-nearest-even.
@@ -37,6 +38,7 @@ class Workload:
     dtype: str          # "f16" or "bf16"
     causal: bool
     qk_gain: float = 1.0  # multiplier applied to q and k in float32
+    Hkv: int = 0          # key/value heads (0 = H: one per query head)
 
     @property
     def scale(self) -> float:
@@ -45,6 +47,14 @@ class Workload:
     @property
     def shape(self):
         return (self.Z, self.H, self.N, self.D)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
+
+    @property
+    def kv_shape(self):
+        return (self.Z, self.kv_heads, self.N, self.D)
 
     @property
     def heads(self) -> int:
@@ -60,13 +70,16 @@ def f32_scale(D: int) -> float:
 
 
 # The five workloads: a tiny parity case, three Z=128 x H=8 x N=1024 cases at
-# head dims 64/128/256, and a long-sequence causal case with a peaked softmax.
+# head dims 64/128/256, and a long-sequence causal case with a peaked softmax;
+# then a grouped key/value head case: Z=4, 32 query heads over 8 key/value
+# heads (4 query heads per key/value head), N=4096, D=128, causal.
 WORKLOADS = {
     "tiny": Workload("tiny", 1, 1, 1, 128, 64, "f16", False),
     "d64": Workload("d64", 2, 128, 8, 1024, 64, "f16", False),
     "d128_causal": Workload("d128_causal", 3, 128, 8, 1024, 128, "f16", True),
     "d256_bf16": Workload("d256_bf16", 4, 128, 8, 1024, 256, "bf16", False),
     "long_causal_bf16": Workload("long_causal_bf16", 5, 16, 16, 8192, 128, "bf16", True, 2.0),
+    "gqa_causal_bf16": Workload("gqa_causal_bf16", 6, 4, 32, 4096, 128, "bf16", True, 1.0, 8),
 }
 
 
@@ -75,7 +88,8 @@ def by_name(name: str) -> Workload:
 
 
 def draw_f32(w: Workload, heads: slice | None = None):
-    """Return float32 (q, k, v, do) of shape (Z, H, N, D) drawn from the workload's seed.
+    """Return float32 (q, k, v, do) drawn from the workload's seed: q and do of
+    shape (Z, H, N, D), k and v of shape (Z, Hkv, N, D).
 
     ``heads`` is ignored for the draw itself (the stream must stay identical); it
     exists so that callers can document that they slice afterwards.
@@ -83,7 +97,7 @@ def draw_f32(w: Workload, heads: slice | None = None):
     rng = np.random.default_rng(w.seed)
     out = []
     for name in ("q", "k", "v", "do"):
-        x = rng.standard_normal(size=w.shape, dtype=np.float32)
+        x = rng.standard_normal(size=w.kv_shape if name in ("k", "v") else w.shape, dtype=np.float32)
         if name in ("q", "k") and w.qk_gain != 1.0:
             x *= np.float32(w.qk_gain)
         out.append(x)
@@ -98,7 +112,7 @@ def make_inputs(w: Workload):
     return tuple(torch.from_numpy(x).to(tdt) for x in draw_f32(w))
 
 
-def random_inputs(shape, dtype: str, seed: int, qk_gain: float = 1.0):
+def random_inputs(shape, dtype: str, seed: int, qk_gain: float = 1.0, kv_heads: int = 0):
     """Seeded (q, k, v, do) torch CPU tensors of an arbitrary shape, same recipe."""
-    w = Workload("adhoc", seed, *shape, dtype, False, qk_gain)
+    w = Workload("adhoc", seed, *shape, dtype, False, qk_gain, kv_heads)
     return make_inputs(w)
