@@ -92,14 +92,14 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   // Query tiles of this workgroup: one, or with the causal mask a long and a
   // short one of the same head (the longest pairs go first).
   // Query head `head` reads key/value head `kvh` (head / G).
-  int64_t kvh64, head64, slot64, qt_a64, qt_b64;
-  xcd_tile_grouped(blockIdx.x, G, paired_groups(n_qtiles, CAUSAL), &kvh64, &head64, &slot64);
-  if (kvh64 >= ZHkv) return;  // padding block
-  const int n_items = paired_items(slot64, n_qtiles, CAUSAL, &qt_a64, &qt_b64);
-  const int qt_a = (int)qt_a64, qt_b = (int)qt_b64;
-  const int head = (int)head64;
+  uint32_t kvh_u, head_u, slot_u, qt_a_u, qt_b_u;
+  xcd_tile_grouped(blockIdx.x, (uint32_t)G, (uint32_t)paired_groups(n_qtiles, CAUSAL), &kvh_u, &head_u, &slot_u);
+  if (kvh_u >= (uint32_t)ZHkv) return;  // padding block
+  const int n_items = paired_items(slot_u, n_qtiles, CAUSAL, &qt_a_u, &qt_b_u);
+  const int qt_a = (int)qt_a_u, qt_b = (int)qt_b_u;
+  const int head = (int)head_u;
   const size_t hoff = (size_t)head * (size_t)N * D;
-  const size_t kvoff = (size_t)kvh64 * (size_t)N * D;
+  const size_t kvoff = (size_t)kvh_u * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc(q + hoff, head_bytes);
   const auto rk = make_rsrc(k + kvoff, head_bytes);

@@ -74,7 +74,7 @@ FA_SCHED_HD int64_t sched_first_qtile(int64_t key_tile, int64_t keys_per_unit,
 FA_SCHED_HD int64_t paired_groups(int64_t n_qtiles, int causal) {
   return causal ? (n_qtiles + 1) / 2 : n_qtiles;
 }
-FA_SCHED_HD int paired_items(int64_t p, int64_t n_qtiles, int causal, int64_t* first, int64_t* second) {
+FA_SCHED_HD int paired_items(uint32_t p, uint32_t n_qtiles, int causal, uint32_t* first, uint32_t* second) {
   if (!causal) {
     *first = *second = p;
     return 1;
@@ -90,13 +90,15 @@ FA_SCHED_HD int paired_items(int64_t p, int64_t n_qtiles, int causal, int64_t* f
 // on XCD b % kXcds; the s-th block of XCD x (s = b / kXcds) takes head
 // x + kXcds * (s / n_qtiles) and tile slot s % n_qtiles.  The grid is padded to
 // kXcds * ceil(ZH / kXcds) * n_qtiles blocks; a block whose head is past the
-// last one has no work.
+// last one has no work.  The decode runs in 32-bit arithmetic (a 64-bit
+// division is a long instruction sequence on the GPU); callers keep the grid
+// below 2^31 blocks.
 FA_SCHED_HD int64_t xcd_grid(int64_t ZH, int64_t n_qtiles) {
   return ((ZH + kXcds - 1) / kXcds) * kXcds * n_qtiles;
 }
-FA_SCHED_HD void xcd_tile(int64_t b, int64_t n_qtiles, int64_t* head, int64_t* slot) {
-  const int64_t x = b % kXcds, s = b / kXcds;
-  *head = x + kXcds * (s / n_qtiles);
+FA_SCHED_HD void xcd_tile(uint32_t b, uint32_t n_qtiles, uint32_t* head, uint32_t* slot) {
+  const uint32_t x = b % (uint32_t)kXcds, s = b / (uint32_t)kXcds;
+  *head = x + (uint32_t)kXcds * (s / n_qtiles);
   *slot = s % n_qtiles;
 }
 
@@ -108,9 +110,9 @@ FA_SCHED_HD void xcd_tile(int64_t b, int64_t n_qtiles, int64_t* head, int64_t* s
 FA_SCHED_HD int64_t xcd_grid_grouped(int64_t ZHkv, int64_t G, int64_t n_slots) {
   return xcd_grid(ZHkv, G * n_slots);
 }
-FA_SCHED_HD void xcd_tile_grouped(int64_t b, int64_t G, int64_t n_slots, int64_t* kv_head, int64_t* head,
-                                  int64_t* slot) {
-  int64_t s;
+FA_SCHED_HD void xcd_tile_grouped(uint32_t b, uint32_t G, uint32_t n_slots, uint32_t* kv_head, uint32_t* head,
+                                  uint32_t* slot) {
+  uint32_t s;
   xcd_tile(b, G * n_slots, kv_head, &s);
   *head = *kv_head * G + s / n_slots;
   *slot = s % n_slots;
