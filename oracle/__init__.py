@@ -25,4 +25,6 @@ from .attention import (  # noqa: F401
     gqa_kv_head,
     attention_forward_gqa,
     attention_backward_gqa,
+    attention_forward_varlen,
+    attention_backward_varlen,
 )

@@ -25,7 +25,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["attention_forward", "attention_forward_full", "attention_backward", "loss_sum_o_do",
-           "gqa_kv_head", "attention_forward_gqa", "attention_backward_gqa"]
+           "gqa_kv_head", "attention_forward_gqa", "attention_backward_gqa", "attention_forward_varlen",
+           "attention_backward_varlen"]
 
 
 def _as_f64(x):
@@ -170,4 +171,63 @@ def attention_backward_gqa(q, k, v, do, scale, causal=False):
             dq[z, h] = r["dq"]
             dk[z, g] += r["dk"]
             dv[z, g] += r["dv"]
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------- variable-length batches
+# [Serving-Ascend], sections "GQA Paged Attention" and the integration
+# discussion before it: a batch holds sequences of different real lengths
+# (context_lens), and tokens past a sequence's length take no part.  Reading
+# (listed in the design doc): the sequences of a batch are packed one after the
+# other along the token axis, sequence b occupying tokens cu_seqlens[b] ..
+# cu_seqlens[b+1]-1 of every head (head-major packed layout: q is (H, T, D),
+# k and v are (Hkv, T, D), T = cu_seqlens[-1]); each sequence is an
+# independent self-attention problem of its own length, causal within itself
+# when causal is set, and query heads share key/value heads as above.
+
+
+def _check_cu_seqlens(cu_seqlens, T):
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    if cu.ndim != 1 or cu.size < 1 or cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at the token count")
+    return cu
+
+
+def attention_forward_varlen(q, k, v, cu_seqlens, scale, causal=False):
+    """(O, lse) of a packed variable-length batch.
+
+    q: (H, T, D); k, v: (Hkv, T, D); cu_seqlens: (B+1,) token offsets.  Each
+    sequence's tokens attend only to that sequence's tokens
+    ([Serving-Ascend], context_lens); per sequence this is the grouped forward
+    above.  O is (H, T, D), lse (H, T).
+    """
+    q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
+    cu = _check_cu_seqlens(cu_seqlens, q.shape[1])
+    O = np.zeros_like(q)
+    lse = np.zeros(q.shape[:2])
+    for b in range(cu.size - 1):
+        s, e = int(cu[b]), int(cu[b + 1])
+        if e == s:
+            continue
+        Ob, lb = attention_forward_gqa(q[None, :, s:e], k[None, :, s:e], v[None, :, s:e], scale, causal)
+        O[:, s:e] = Ob[0]
+        lse[:, s:e] = lb[0]
+    return O, lse
+
+
+def attention_backward_varlen(q, k, v, do, cu_seqlens, scale, causal=False):
+    """(dq, dk, dv) of a packed variable-length batch: per sequence the
+    grouped backward above; a token's gradients come only from its own
+    sequence.  dq is (H, T, D); dk, dv are (Hkv, T, D)."""
+    q, k, v, do = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(do)
+    cu = _check_cu_seqlens(cu_seqlens, q.shape[1])
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(cu.size - 1):
+        s, e = int(cu[b]), int(cu[b + 1])
+        if e == s:
+            continue
+        g = attention_backward_gqa(q[None, :, s:e], k[None, :, s:e], v[None, :, s:e], do[None, :, s:e], scale, causal)
+        dq[:, s:e], dk[:, s:e], dv[:, s:e] = g[0][0], g[1][0], g[2][0]
     return dq, dk, dv

@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 from oracle import (attention_backward, attention_backward_gqa, attention_forward, attention_forward_full,
-                    attention_forward_gqa, gqa_kv_head, loss_sum_o_do)
+                    attention_forward_gqa, gqa_kv_head, loss_sum_o_do, attention_forward_varlen,
+                    attention_backward_varlen)
 
 RNG = np.random.default_rng(1234)
 
@@ -326,3 +327,90 @@ def test_gqa_head_map_and_planted_interleaving():
                                                          enable_gqa=True).numpy()
     wrong = np.stack([attention_forward(q[0, h], k[0, h % 2], v[0, h % 2], 0.5)[0] for h in range(4)])
     assert np.max(np.abs(wrong - o[0])) > 1e-3
+
+
+# ---------------------------------------------------------------- variable-length batches
+# [Serving-Ascend]: sequences of different real lengths in one batch, tokens
+# past a sequence's end taking no part.  Packed head-major layout (H, T, D)
+# with cu_seqlens token offsets.
+
+
+def _varlen_inputs(rng, H, Hkv, cu, D):
+    T = int(cu[-1])
+    q = rng.standard_normal((H, T, D))
+    k, v = (rng.standard_normal((Hkv, T, D)) for _ in range(2))
+    do = rng.standard_normal((H, T, D))
+    return q, k, v, do
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_against_torch_sdpa_block_mask(causal):
+    """An independent library routine: torch's CPU SDPA in float64 over the
+    whole packed token axis with a block-diagonal (and causal) boolean mask,
+    enable_gqa, forward and autograd backward."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(61)
+    cu = np.array([0, 5, 5, 17, 18, 30])  # includes an empty and a one-token sequence
+    H, Hkv, D = 4, 2, 8
+    q, k, v, do = _varlen_inputs(rng, H, Hkv, cu, D)
+    T = int(cu[-1])
+    seg = np.repeat(np.arange(len(cu) - 1), np.diff(cu))
+    pos = np.arange(T) - cu[seg]
+    mask = seg[:, None] == seg[None, :]
+    if causal:
+        mask &= pos[None, :] <= pos[:, None]
+    scale = 0.37
+    O, lse = attention_forward_varlen(q, k, v, cu, scale, causal)
+    dq, dk, dv = attention_backward_varlen(q, k, v, do, cu, scale, causal)
+    tq, tk, tv = (torch.tensor(x[None], requires_grad=True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.tensor(mask), scale=scale,
+                                                         enable_gqa=True)
+    o.backward(torch.tensor(do[None]))
+    assert np.max(np.abs(o.detach().numpy()[0] - O)) <= 1e-12
+    for g, t in ((dq, tq), (dk, tk), (dv, tv)):
+        assert np.max(np.abs(t.grad.numpy()[0] - g)) <= 1e-12
+    # lse against a direct log-sum-exp over each token's visible keys (head 0)
+    G = H // Hkv
+    for h in range(H):
+        S = (q[h] @ k[h // G].T) * scale
+        want = np.log(np.sum(np.where(mask, np.exp(S), 0.0), axis=1))
+        assert np.max(np.abs(lse[h] - want)) <= 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_gradient_matches_finite_differences(causal):
+    rng = np.random.default_rng(67)
+    cu = np.array([0, 3, 7])
+    q, k, v, do = _varlen_inputs(rng, 2, 1, cu, 3)
+    scale = 0.53
+
+    def loss():
+        O, _ = attention_forward_varlen(q, k, v, cu, scale, causal)
+        return float(np.sum(O * do))
+
+    dq, dk, dv = attention_backward_varlen(q, k, v, do, cu, scale, causal)
+    for g, x in ((dq, q), (dk, k), (dv, v)):
+        fd = _fd_grad(loss, x)
+        assert np.max(np.abs(fd - g)) <= 1e-6 * max(1.0, np.max(np.abs(g)))
+
+
+def test_varlen_sequences_are_independent_and_planted_merge_fails():
+    """Changing one sequence's tokens leaves every other sequence's outputs
+    bit for bit; one-token sequences give O = v (closed form) and
+    lse = scale * q.k; treating the batch as one sequence (a plausible slip)
+    changes the result."""
+    rng = np.random.default_rng(71)
+    cu = np.array([0, 6, 7, 15])
+    q, k, v, do = _varlen_inputs(rng, 2, 2, cu, 4)
+    O, lse = attention_forward_varlen(q, k, v, cu, 0.5, True)
+    k2 = k.copy()
+    k2[:, 8:12] += 3.0  # inside the third sequence
+    O2, lse2 = attention_forward_varlen(q, k2, v, cu, 0.5, True)
+    assert np.array_equal(O[:, :7], O2[:, :7]) and np.array_equal(lse[:, :7], lse2[:, :7])
+    assert not np.array_equal(O[:, 7:], O2[:, 7:])
+    assert np.max(np.abs(O[:, 6] - v[:, 6])) <= 1e-15
+    assert np.max(np.abs(lse[:, 6] - 0.5 * np.sum(q[:, 6] * k[:, 6], axis=-1))) <= 1e-14
+    merged, _ = attention_forward_varlen(q, k, v, np.array([0, 15]), 0.5, True)
+    assert np.max(np.abs(merged[:, 7:] - O[:, 7:])) > 1e-3
+    with pytest.raises(ValueError):
+        attention_forward_varlen(q, k, v, np.array([0, 8, 7, 15]), 0.5, True)
