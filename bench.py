@@ -49,7 +49,12 @@ KERNEL_SOURCES = {
 
 
 def fwd_flops(w) -> float:
-    f = 4.0 * w.Z * w.H * w.N * w.N * w.D
+    """4 N^2 D per (sequence, query head), halved when causal; a variable-length
+    batch sums over its sequences."""
+    if w.varlen:
+        f = 4.0 * w.H * w.D * float(sum(n * n for n in w.lengths))
+    else:
+        f = 4.0 * w.Z * w.H * w.N * w.N * w.D
     return f / 2 if w.causal else f
 
 
@@ -66,7 +71,7 @@ def kernel_work(w, o_bytes: int):
       bytes, read O and dO rows and lse, write two fp32 per row.
     """
     hf = fwd_flops(w)  # = 4 N^2 D per head, halved when causal
-    rows = w.Z * w.H * w.N
+    rows = w.H * w.T if w.varlen else w.Z * w.H * w.N
     return {
         "fa_fwd": ("mfma", hf, "flop"),
         "fa_bwd_dkdv": ("mfma", 2.0 * hf, "flop"),
@@ -112,16 +117,44 @@ def stored_traffic(kernel: str, workload: str):
 
 # ------------------------------------------------------------------ CPU baseline
 def _oracle_heads(args):
-    """Worker: fp64 oracle forward + backward over a list of heads."""
+    """Worker: fp64 oracle forward + backward over a list of (q, k, v, do) problems."""
     import numpy as np
 
     import oracle
 
-    q, k, v, do, scale, causal = args
-    for i in range(q.shape[0]):
-        oracle.attention_backward(q[i].astype(np.float64), k[i].astype(np.float64),
-                                  v[i].astype(np.float64), do[i].astype(np.float64), scale, causal)
-    return q.shape[0]
+    problems, scale, causal = args
+    for q, k, v, do in problems:
+        oracle.attention_backward(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                                  do.astype(np.float64), scale, causal)
+    return len(problems)
+
+
+def _problems(w, cpu_inputs, n_heads: int):
+    """The first n_heads (sequence, query head) problems of the workload as
+    float32 (q, k, v, do) arrays, each query head with the key/value head it
+    shares (the grouped oracle's per-head work; its sum of dK / dV over a
+    group is not timed), and the lengths of their sequences."""
+    G = w.H // w.kv_heads
+    q, k, v, do = cpu_inputs
+    f = lambda t: t.float().numpy()  # noqa: E731  (one problem at a time)
+    out, lens = [], []
+    if w.varlen:
+        cu = w.cu_seqlens
+        for b in range(w.Z):
+            for h in range(w.H):
+                if len(out) == n_heads:
+                    return out, lens
+                s, e = int(cu[b]), int(cu[b + 1])
+                out.append((f(q[h, s:e]), f(k[h // G, s:e]), f(v[h // G, s:e]), f(do[h, s:e])))
+                lens.append(e - s)
+        return out, lens
+    for z in range(w.Z):
+        for h in range(w.H):
+            if len(out) == n_heads:
+                return out, lens
+            out.append((f(q[z, h]), f(k[z, h // G]), f(v[z, h // G]), f(do[z, h])))
+            lens.append(w.N)
+    return out, lens
 
 
 def cpu_baseline(w, cpu_inputs, n_heads: int, workers: int):
@@ -131,21 +164,16 @@ def cpu_baseline(w, cpu_inputs, n_heads: int, workers: int):
 
     import numpy as np
 
-    n_heads = min(n_heads, w.Z * w.H)
-    G = w.H // w.kv_heads
-    # Each query head with the key/value head it shares (the grouped oracle's
-    # per-head work; its sum of dK / dV over a group is not timed).
-    per_q = [t.repeat_interleave(G, dim=1) if t.shape[1] != w.H else t for t in cpu_inputs]
-    flat = [t.reshape(w.Z * w.H, w.N, w.D)[:n_heads].float().numpy() for t in per_q]
-    workers = max(1, min(workers, n_heads))
-    chunks = np.array_split(np.arange(n_heads), workers)
-    jobs = [tuple(x[c[0]:c[-1] + 1] for x in flat) + (w.scale, w.causal) for c in chunks if len(c)]
+    problems, lens = _problems(w, cpu_inputs, n_heads)
+    workers = max(1, min(workers, len(problems)))
+    chunks = np.array_split(np.arange(len(problems)), workers)
+    jobs = [([problems[i] for i in c], w.scale, w.causal) for c in chunks if len(c)]
     saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
     for k in saved:
         os.environ[k] = "1"  # one BLAS thread per worker process
     try:
         with cf.ProcessPoolExecutor(max_workers=len(jobs), mp_context=mp.get_context("spawn")) as ex:
-            list(ex.map(_oracle_heads, [tuple(x[:1] for x in j[:4]) + j[4:] for j in jobs]))  # warm import
+            list(ex.map(_oracle_heads, [(j[0][:1],) + j[1:] for j in jobs]))  # warm import
             t0 = time.perf_counter()
             done = sum(ex.map(_oracle_heads, jobs))
             dt = time.perf_counter() - t0
@@ -155,14 +183,15 @@ def cpu_baseline(w, cpu_inputs, n_heads: int, workers: int):
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = v
-    flops = 3.5 * fwd_flops(w) * done / (w.Z * w.H)
+    per = 4.0 * w.D * float(sum(n * n for n in lens[:done])) * (0.5 if w.causal else 1.0)
+    flops = 3.5 * per
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": len(jobs),
         "kind": "oracle",
         "sample": (f"fp64 numpy oracle, fwd+bwd (full N x N S and P, naive backward) on {done} of "
-                   f"{w.Z * w.H} heads of the same seeded workload, {len(jobs)} processes x 1 BLAS "
+                   f"{w.Z * w.H} (sequence, head) problems of the same seeded workload, {len(jobs)} processes x 1 BLAS "
                    f"thread, wall {dt:.2f} s; FLOPs counted with the same convention"),
     }
 
@@ -180,10 +209,12 @@ def run(args):
     q, k, v, do = (t.to(dev) for t in cpu_inputs)
     Z, H, N, D = w.shape
     Hkv = w.kv_heads
+    T = w.T
     o = torch.empty_like(q)
-    lse = torch.empty((Z, H, N), dtype=torch.float32, device=dev)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    stats = torch.empty((2, Z, H, N), dtype=torch.float32, device=dev)
+    stats = torch.empty((2,) + tuple(q.shape[:-1]), dtype=torch.float32, device=dev)
+    cu = torch.from_numpy(w.cu_seqlens).to(dev) if w.varlen else None
     L = fa.lib()
     code = fa._dtype_code(q)
     causal = int(w.causal)
@@ -196,8 +227,27 @@ def run(args):
         if st != 0:
             raise fa.FAError(st, name, fa.last_error())
 
+    def step_varlen(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        call(L.fa_fwd_varlen(Z, H, Hkv, T, N, D, code, code, P(cu), P(q), P(k), P(v), P(o), P(lse), scale, causal,
+                             sp), "fa_fwd_varlen")
+        if ev is not None:
+            ev[1].record(stream)
+        call(L.fa_bwd_dq_and_stats_varlen(Z, H, Hkv, T, N, D, code, code, P(cu), P(q), P(k), P(v), P(o), P(do),
+                                          P(lse), P(stats), P(dq), scale, causal, sp), "fa_bwd_dq_and_stats_varlen")
+        if ev is not None:
+            ev[2].record(stream)
+        call(L.fa_bwd_dkdv_varlen(Z, H, Hkv, T, N, D, code, P(cu), P(q), P(k), P(v), P(do), P(stats), P(dk), P(dv),
+                                  scale, causal, 0, sp), "fa_bwd_dkdv_varlen")
+        if ev is not None:
+            ev[3].record(stream)
+
     def step(ev=None):
-        # Grouped key/value heads go through the *_gqa forms of the same calls.
+        # Grouped key/value heads go through the *_gqa forms of the same calls,
+        # variable-length batches through the *_varlen forms.
+        if w.varlen:
+            return step_varlen(ev)
         if ev is not None:
             ev[0].record(stream)
         if Hkv == H:
@@ -299,8 +349,10 @@ def run(args):
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: Z={Z} H={H}" + (f" Hkv={Hkv}" if Hkv != H else "") +
-                               f" N={N} D={D} {w.dtype} causal={bool(w.causal)} scale={scale:.9g}",
+        "config": {"workload": f"{w.name}: " + (f"B={Z} sequences of {min(w.lengths)}..{N} tokens (T={T}) "
+                                                 if w.varlen else f"Z={Z} ") + f"H={H}" +
+                               (f" Hkv={Hkv}" if Hkv != H else "") + ("" if w.varlen else f" N={N}") +
+                               f" D={D} {w.dtype} causal={bool(w.causal)} scale={scale:.9g}",
                    "Z": Z, "H": H, "Hkv": Hkv, "N": N, "D": D, "causal": bool(w.causal), "seed": w.seed},
         "frac_of_peak": round(value / PEAK_MFMA_F16_TFLOPS, 4),
         "breakdown": {

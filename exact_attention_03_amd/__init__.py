@@ -20,7 +20,7 @@ import math
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32, FAError, check, last_error, lib,  # noqa: F401
                    status_name)
 
-__all__ = ["forward", "backward", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_dq_and_stats", "workspace_bytes",
+__all__ = ["forward", "backward", "forward_varlen", "backward_varlen", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_dq_and_stats", "workspace_bytes",
            "device_info", "dkdv_schedule", "fwd_tile_pairs", "FAError", "lib"]
 
 
@@ -151,6 +151,75 @@ def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None):
         else:
             st = lib().fa_bwd_gqa(Z, H, Hkv, N, D, *common)
     check(st, "fa_bwd" if Hkv == H else "fa_bwd_gqa")
+    return dq, dk, dv
+
+
+def _check_varlen(q, k, v, cu_seqlens, max_seqlen):
+    """q: (H, T, D); k, v: (Hkv, T, D); cu_seqlens: int32 GPU tensor (B+1,).
+    Returns (B, H, Hkv, T, D, max_seqlen)."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if not t.is_cuda or t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous 3-d GPU tensor, packed (heads, tokens, D)")
+        if t.device != q.device:
+            raise ValueError(f"{n} is on {t.device}, expected {q.device}")
+    H, T, D = q.shape
+    Hkv = k.shape[0]
+    if k.shape != v.shape or k.shape[1:] != (T, D) or Hkv == 0 or H % Hkv != 0:
+        raise ValueError(f"k {tuple(k.shape)} / v {tuple(v.shape)} must be (Hkv, {T}, {D}) with {H} a multiple of Hkv")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if (not cu_seqlens.is_cuda or cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1
+            or not cu_seqlens.is_contiguous() or cu_seqlens.numel() < 1 or cu_seqlens.device != q.device):
+        raise ValueError("cu_seqlens must be a contiguous int32 GPU tensor of B+1 token offsets")
+    B = cu_seqlens.numel() - 1
+    if max_seqlen is None:
+        # One host read of the offsets (a synchronisation); pass max_seqlen to avoid it.
+        lens = (cu_seqlens[1:] - cu_seqlens[:-1]).cpu()
+        max_seqlen = int(lens.max()) if B > 0 else 0
+    return B, H, Hkv, T, D, int(max_seqlen)
+
+
+def forward_varlen(q, k, v, cu_seqlens, max_seqlen=None, causal=False, scale=None, out_dtype=None):
+    """Attention over a packed batch of variable-length sequences.
+
+    q: (H, T, D); k, v: (Hkv, T, D) (H a multiple of Hkv); sequence b is
+    tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of every head and attends only
+    within itself.  max_seqlen: at least the longest sequence (read from
+    cu_seqlens when omitted).  Returns O (H, T, D) and lse (H, T).
+    """
+    torch = _torch()
+    B, H, Hkv, T, D, mx = _check_varlen(q, k, v, cu_seqlens, max_seqlen)
+    odt = q.dtype if out_dtype is None else out_dtype
+    with torch.cuda.device(q.device):
+        o = torch.empty((H, T, D), dtype=odt, device=q.device)
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+        st = lib().fa_fwd_varlen(B, H, Hkv, T, mx, D, _dtype_code(q), _dtype_code(o), _ptr(cu_seqlens), _ptr(q),
+                                 _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _scale(scale, D), int(bool(causal)),
+                                 _stream(q))
+    check(st, "fa_fwd_varlen")
+    return o, lse
+
+
+def backward_varlen(q, k, v, o, do, lse, cu_seqlens, max_seqlen=None, causal=False, scale=None):
+    """dq (H, T, D), dk, dv (Hkv, T, D) of ``forward_varlen`` given dO."""
+    torch = _torch()
+    B, H, Hkv, T, D, mx = _check_varlen(q, k, v, cu_seqlens, max_seqlen)
+    for t, n in ((o, "o"), (do, "do")):
+        if not t.is_cuda or t.shape != q.shape or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{n} must be a contiguous GPU tensor of shape {tuple(q.shape)}")
+    if do.dtype != q.dtype:
+        raise TypeError("do must have q's dtype")
+    if lse.shape != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 (H, T) tensor")
+    with torch.cuda.device(q.device):
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        nbytes = lib().fa_bwd_workspace_bytes(1, H, T, D)
+        ws = torch.empty((max(1, nbytes // 4),), dtype=torch.float32, device=q.device)
+        st = lib().fa_bwd_varlen(B, H, Hkv, T, mx, D, _dtype_code(q), _dtype_code(o), _ptr(cu_seqlens), _ptr(q),
+                                 _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _scale(scale, D), int(bool(causal)), _ptr(ws), ws.numel() * 4, _stream(q))
+    check(st, "fa_bwd_varlen")
     return dq, dk, dv
 
 

@@ -42,6 +42,14 @@ SIGNATURES = {
                                        _vp, _vp, _f32, _int, _vp]),
     "fa_bwd_dkdv_gqa": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _int,
                                _int, _vp]),
+    "fa_fwd_varlen": (_int, [_i64, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _f32,
+                             _int, _vp]),
+    "fa_bwd_varlen": (_int, [_i64, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _vp, _vp, _f32, _int, _vp, _sz, _vp]),
+    "fa_bwd_dq_and_stats_varlen": (_int, [_i64, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp,
+                                          _vp, _vp, _vp, _vp, _f32, _int, _vp]),
+    "fa_bwd_dkdv_varlen": (_int, [_i64, _i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _f32, _int, _int, _vp]),
     "fa_device_info": (_int, [_i64, _int, _intp, _intp]),
     "fa_dkdv_schedule": (_int, [_i64, _i64, _i64, _i64, _int, _int, _i64p, _i64p, _i64p]),
     "fa_fwd_tile_pairs": (_int, [_i64, _i64, _int, _i64p, _i64p]),

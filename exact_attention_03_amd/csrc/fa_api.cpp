@@ -91,6 +91,30 @@ int check_groups(const Shape& s, int64_t Hkv) {
   return FA_OK;
 }
 
+// Variable-length batches: Z sequences packed head-major, (H, T, D), at the
+// token offsets cu (device int32, Z+1 entries), N = the longest sequence.
+// Dense batches have cu == nullptr.
+struct Packing {
+  const int* cu = nullptr;
+  int64_t T = 0;
+  bool packed() const { return cu != nullptr; }
+};
+
+int check_packing(const Shape& s, int64_t Hkv, const Packing& pk) {
+  if (!pk.packed()) return FA_OK;
+  if (pk.T < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative token count T=%lld", (long long)pk.T);
+  if (reinterpret_cast<uintptr_t>(pk.cu) % 4 != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "cu_seqlens is not 4-byte aligned");
+  if (s.empty() || pk.T == 0 || Hkv == 0) return FA_OK;
+  // Row offsets of one group of query heads (G heads T rows apart) and of one
+  // head's T rows stay 32-bit; the offsets array is read as int32.
+  const int64_t G = s.H / Hkv;
+  if (G * (pk.T + 256) * s.D * 2 > kMaxI32 || (pk.T + 256) * s.D * 4 > kMaxI32 || pk.T > kMaxI32)
+    return fail(FA_ERR_UNSUPPORTED, "packed batch too large (T=%lld H/Hkv=%lld D=%lld)", (long long)pk.T,
+                (long long)G, (long long)s.D);
+  return FA_OK;
+}
+
 int check_dtypes(int dtype, int o_dtype, bool need_o) {
   if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16)
     return fail(FA_ERR_INVALID_ARGUMENT, "dtype %d must be FA_DTYPE_F16 or FA_DTYPE_BF16", dtype);
@@ -206,20 +230,22 @@ size_t fa_bwd_workspace_bytes(int64_t Z, int64_t H, int64_t N, int64_t D) {
 namespace {
 
 int fwd_impl(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype, int o_dtype, const void* q,
-             const void* k, const void* v, void* o, float* lse, float scale, int causal, hipStream_t stream) {
+             const void* k, const void* v, void* o, float* lse, float scale, int causal, hipStream_t stream,
+             const Packing& pk = Packing{}) {
   g_last_error.clear();
   const Shape s{Z, H, N, D};
   FA_TRY(check_shape(s));
   FA_TRY(check_groups(s, Hkv));
+  FA_TRY(check_packing(s, Hkv, pk));
   FA_TRY(check_dtypes(dtype, o_dtype, true));
   FA_TRY(check_scale(scale, causal));
-  if (s.empty()) return FA_OK;
+  if (s.empty() || (pk.packed() && pk.T == 0)) return FA_OK;
   FA_TRY(check_ptr(q, "q"));
   FA_TRY(check_ptr(k, "k"));
   FA_TRY(check_ptr(v, "v"));
   FA_TRY(check_ptr(o, "o"));
   FA_TRY(check_ptr(lse, "lse"));
-  fa::FwdArgs a{Z, H, N, D, Hkv, dtype, o_dtype, q, k, v, o, lse, scale, causal, stream};
+  fa::FwdArgs a{Z, H, N, D, Hkv, dtype, o_dtype, q, k, v, o, lse, scale, causal, stream, pk.cu, pk.T};
   return finish(fa::launch_fwd(a), stream, "fa_fwd launch");
 }
 
@@ -260,13 +286,14 @@ namespace {
 
 int dkdv_impl(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype, const void* q, const void* k,
               const void* v, const void* dout, const float* stats, void* dk, void* dv, float scale, int causal,
-              int num_programs, hipStream_t stream) {
+              int num_programs, hipStream_t stream, const Packing& pk = Packing{}) {
   g_last_error.clear();
   const Shape s{Z, H, N, D};
   FA_TRY(validate_bwd_common(s, dtype, q, k, v, dout, stats, scale, causal));
   FA_TRY(check_groups(s, Hkv));
+  FA_TRY(check_packing(s, Hkv, pk));
   if (num_programs < 0) return fail(FA_ERR_INVALID_ARGUMENT, "num_programs must be >= 0 (got %d)", num_programs);
-  if (s.empty()) return FA_OK;
+  if (s.empty() || (pk.packed() && pk.T == 0)) return FA_OK;
   FA_TRY(check_ptr(dk, "dk"));
   FA_TRY(check_ptr(dv, "dv"));
   if (num_programs == 0) {
@@ -278,6 +305,7 @@ int dkdv_impl(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype
   a.Z = Z; a.H = H; a.Hkv = Hkv; a.N = N; a.D = D; a.dtype = dtype;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.stats = const_cast<float*>(stats);
   a.dk = dk; a.dv = dv; a.scale = scale; a.causal = causal; a.num_programs = num_programs; a.stream = stream;
+  a.cu_seqlens = pk.cu; a.T = pk.T;
   return finish(fa::launch_bwd_dkdv(a), stream, "fa_bwd_dkdv launch");
 }
 
@@ -312,14 +340,16 @@ namespace {
 
 int dq_and_stats_impl(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype, int o_dtype,
                       const void* q, const void* k, const void* v, const void* o, const void* dout,
-                      const float* lse, float* stats, void* dq, float scale, int causal, hipStream_t stream) {
+                      const float* lse, float* stats, void* dq, float scale, int causal, hipStream_t stream,
+                      const Packing& pk = Packing{}) {
   g_last_error.clear();
   const Shape s{Z, H, N, D};
   FA_TRY(check_shape(s));
   FA_TRY(check_groups(s, Hkv));
+  FA_TRY(check_packing(s, Hkv, pk));
   FA_TRY(check_dtypes(dtype, o_dtype, true));
   FA_TRY(check_scale(scale, causal));
-  if (s.empty()) return FA_OK;
+  if (s.empty() || (pk.packed() && pk.T == 0)) return FA_OK;
   FA_TRY(check_ptr(q, "q"));
   FA_TRY(check_ptr(k, "k"));
   FA_TRY(check_ptr(v, "v"));
@@ -332,6 +362,7 @@ int dq_and_stats_impl(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, i
   a.Z = Z; a.H = H; a.Hkv = Hkv; a.N = N; a.D = D; a.dtype = dtype; a.o_dtype = o_dtype;
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse = lse; a.stats = stats;
   a.dq = dq; a.scale = scale; a.causal = causal; a.dq_stats = true; a.stream = stream;
+  a.cu_seqlens = pk.cu; a.T = pk.T;
   return finish(fa::launch_bwd_dq(a), stream, "fa_bwd_dq_and_stats launch");
 }
 
@@ -339,14 +370,16 @@ int dq_and_stats_impl(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, i
 // dK / dV from them.
 int bwd_impl(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype, int o_dtype, const void* q,
              const void* k, const void* v, const void* o, const void* dout, const float* lse, void* dq, void* dk,
-             void* dv, float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+             void* dv, float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream,
+             const Packing& pk = Packing{}) {
   g_last_error.clear();
   const Shape s{Z, H, N, D};
   FA_TRY(check_shape(s));
   FA_TRY(check_groups(s, Hkv));
+  FA_TRY(check_packing(s, Hkv, pk));
   FA_TRY(check_dtypes(dtype, o_dtype, true));
   FA_TRY(check_scale(scale, causal));
-  if (s.empty()) return FA_OK;
+  if (s.empty() || (pk.packed() && pk.T == 0)) return FA_OK;
   FA_TRY(check_ptr(q, "q"));
   FA_TRY(check_ptr(k, "k"));
   FA_TRY(check_ptr(v, "v"));
@@ -357,14 +390,14 @@ int bwd_impl(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype,
   FA_TRY(check_ptr(dk, "dk"));
   FA_TRY(check_ptr(dv, "dv"));
   FA_TRY(check_ptr(workspace, "workspace"));
-  const size_t need = fa_bwd_workspace_bytes(Z, H, N, D);
+  const size_t need = pk.packed() ? fa_bwd_workspace_bytes(1, H, pk.T, D) : fa_bwd_workspace_bytes(Z, H, N, D);
   if (workspace_bytes < need)
     return fail(FA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu bytes needed",
                 workspace_bytes, need);
   float* stats = static_cast<float*>(workspace);
   FA_TRY(dq_and_stats_impl(Z, H, Hkv, N, D, dtype, o_dtype, q, k, v, o, dout, lse, stats, dq, scale, causal,
-                           stream));
-  FA_TRY(dkdv_impl(Z, H, Hkv, N, D, dtype, q, k, v, dout, stats, dk, dv, scale, causal, 0, stream));
+                           stream, pk));
+  FA_TRY(dkdv_impl(Z, H, Hkv, N, D, dtype, q, k, v, dout, stats, dk, dv, scale, causal, 0, stream, pk));
   return FA_OK;
 }
 
@@ -402,6 +435,45 @@ int fa_bwd_dkdv_gqa(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int
                     const void* k, const void* v, const void* dout, const float* stats, void* dk, void* dv,
                     float scale, int causal, int num_programs, hipStream_t stream) {
   return dkdv_impl(Z, H, Hkv, N, D, dtype, q, k, v, dout, stats, dk, dv, scale, causal, num_programs, stream);
+}
+
+int fa_fwd_varlen(int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t max_seqlen, int64_t D, int dtype,
+                  int o_dtype, const int32_t* cu_seqlens, const void* q, const void* k, const void* v, void* o,
+                  float* lse, float scale, int causal, hipStream_t stream) {
+  if (cu_seqlens == nullptr && B > 0 && H > 0 && max_seqlen > 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
+  return fwd_impl(B, H, Hkv, max_seqlen, D, dtype, o_dtype, q, k, v, o, lse, scale, causal, stream,
+                  Packing{cu_seqlens, T});
+}
+
+int fa_bwd_varlen(int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t max_seqlen, int64_t D, int dtype,
+                  int o_dtype, const int32_t* cu_seqlens, const void* q, const void* k, const void* v,
+                  const void* o, const void* dout, const float* lse, void* dq, void* dk, void* dv, float scale,
+                  int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (cu_seqlens == nullptr && B > 0 && H > 0 && max_seqlen > 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
+  return bwd_impl(B, H, Hkv, max_seqlen, D, dtype, o_dtype, q, k, v, o, dout, lse, dq, dk, dv, scale, causal,
+                  workspace, workspace_bytes, stream, Packing{cu_seqlens, T});
+}
+
+int fa_bwd_dq_and_stats_varlen(int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t max_seqlen, int64_t D,
+                               int dtype, int o_dtype, const int32_t* cu_seqlens, const void* q, const void* k,
+                               const void* v, const void* o, const void* dout, const float* lse, float* stats,
+                               void* dq, float scale, int causal, hipStream_t stream) {
+  if (cu_seqlens == nullptr && B > 0 && H > 0 && max_seqlen > 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
+  return dq_and_stats_impl(B, H, Hkv, max_seqlen, D, dtype, o_dtype, q, k, v, o, dout, lse, stats, dq, scale,
+                           causal, stream, Packing{cu_seqlens, T});
+}
+
+int fa_bwd_dkdv_varlen(int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t max_seqlen, int64_t D, int dtype,
+                       const int32_t* cu_seqlens, const void* q, const void* k, const void* v, const void* dout,
+                       const float* stats, void* dk, void* dv, float scale, int causal, int num_programs,
+                       hipStream_t stream) {
+  if (cu_seqlens == nullptr && B > 0 && H > 0 && max_seqlen > 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "cu_seqlens is NULL");
+  return dkdv_impl(B, H, Hkv, max_seqlen, D, dtype, q, k, v, dout, stats, dk, dv, scale, causal, num_programs,
+                   stream, Packing{cu_seqlens, T});
 }
 
 int fa_device_info(int64_t D, int dtype, int* compute_units, int* dkdv_programs) {

@@ -123,8 +123,8 @@ __attribute__((amdgpu_waves_per_eu(DkdvTile<D>::OCC, DkdvTile<D>::OCC)))
 void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                         const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                         const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
-                        uint16_t* __restrict__ dv, int N, int ZHkv, int G, int n_ktiles, int n_qtiles, float c2,
-                        float scale, int P) {
+                        uint16_t* __restrict__ dv, int N_max, int ZHkv, int Hkv, int G, int n_ktiles_max,
+                        float c2, float scale, int P, const int* __restrict__ cu, int64_t n_tokens) {
   using C = DkdvTile<D>;
   using QTile = CmTile<C::BQ>;
   using VTile = CmTile<C::BK>;
@@ -141,26 +141,40 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
   const int w = wave_id();
   const int h = lane >> 5;
   const int l32 = lane & 31;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-
   for (int64_t round = 0;; ++round) {
     int64_t kvh64, kt64;
-    if (!sched_unit(round, blockIdx.x, P, ZHkv, n_ktiles, &kvh64, &kt64)) break;  // uniform
-    const int kt = (int)kt64, kvh = (int)kvh64;
+    if (cu != nullptr) {
+      // Packed variable-length batch: one unit per workgroup, key-tile major
+      // (the first key tiles, which carry the most query tiles, go first), so
+      // that the dispatcher balances units of very different sizes.
+      if (round > 0) break;
+      kvh64 = blockIdx.x % (uint32_t)ZHkv;
+      kt64 = blockIdx.x / (uint32_t)ZHkv;
+    } else if (!sched_unit(round, blockIdx.x, P, ZHkv, n_ktiles_max, &kvh64, &kt64)) {
+      break;  // uniform
+    }
+    const int kt = (int)kt64;
     const int k0 = kt * C::BK;
     const int kw0 = k0 + 32 * w;  // first key of this wave
-    // The unit's key/value head kvh serves query heads kvh*G .. kvh*G+G-1
-    // (G = 1 without grouping), which lie next to each other in Q, dO and
-    // the statistics: one buffer resource spans the G heads and a member's
-    // rows start at member * N.
-    const size_t kvoff = (size_t)kvh * (size_t)N * D;
-    const size_t goff = kvoff * (size_t)G;
-    const auto rq = make_rsrc(q + goff, head_bytes * (uint32_t)G);
+    // The unit's (batch) key/value head serves G query heads (G = 1 without
+    // grouping), whose rows lie q_stride rows apart in Q, dO and the
+    // statistics: one buffer resource spans the G heads' rows of this
+    // problem and member m's rows start at m * q_stride.
+    const HeadRows hr = head_rows((uint32_t)kvh64, 0, (uint32_t)Hkv, (uint32_t)G, N_max, cu, n_tokens);
+    const int N = hr.n;  // this problem's sequence length
+    if (k0 >= N) continue;  // key tile past this sequence (uniform)
+    const int q_stride = (int)hr.q_stride;
+    const uint32_t head_bytes = (uint32_t)N * D * 2;
+    const uint32_t group_rows = (uint32_t)((G - 1) * q_stride + N);
+    const size_t kvoff = (size_t)hr.kv_row0 * D;
+    const size_t goff = (size_t)hr.q_row0 * D;
+    const auto rq = make_rsrc(q + goff, group_rows * D * 2);
     const auto rk = make_rsrc(k + kvoff, head_bytes);
     const auto rv = make_rsrc(v + kvoff, head_bytes);
-    const auto rdo = make_rsrc(dout + goff, head_bytes * (uint32_t)G);
-    const auto rl = make_rsrc(lse2 + (size_t)kvh * G * N, (uint32_t)(N * G) * 4);
-    const auto rd = make_rsrc(delta + (size_t)kvh * G * N, (uint32_t)(N * G) * 4);
+    const auto rdo = make_rsrc(dout + goff, group_rows * D * 2);
+    const auto rl = make_rsrc(lse2 + hr.q_row0, group_rows * 4);
+    const auto rd = make_rsrc(delta + hr.q_row0, group_rows * 4);
+    const int n_qtiles = (N + C::BQ - 1) / C::BQ;
     const int i0 = (int)sched_first_qtile(kt, C::BK, C::BQ, CAUSAL);
     const int nq = n_qtiles - i0;
     const int n_items = nq * G;  // (member, query tile) pairs, member-major
@@ -168,7 +182,7 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     // Copy query tile i of member m (Q, dO, and the lse2 / Delta values from
     // its first query on) into ring stage st.
     auto issue_qtile = [&](int m, int i, char* base) {
-      const int qq0 = m * N + i * C::BQ;  // row in the group's stacked rows
+      const int qq0 = m * q_stride + i * C::BQ;  // row in the group's rows
 #pragma unroll(C::COPY_UNROLL)
       for (int x = 0; x < C::QCOPIES / C::NW; ++x) {
         const int blk = w * (C::QCOPIES / C::NW) + x;
@@ -360,8 +374,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqTile<D>::
 void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                       const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                       const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dq,
-                      int N, int ZH, int n_qtiles, float c2, float scale, const void* __restrict__ o,
-                      const float* __restrict__ lse, float* __restrict__ stats_out, int ZHkv, int G) {
+                      int N_max, int64_t plane, int n_qtiles_max, float c2, float scale,
+                      const void* __restrict__ o, const float* __restrict__ lse, float* __restrict__ stats_out,
+                      int ZHkv, int Hkv, int G, const int* __restrict__ cu, int64_t n_tokens) {
   using C = DqTile<D>;
   using Tile = CmTile<C::BN>;
   // One LDS object per ring stage and operand, accessed with compile-time
@@ -388,24 +403,28 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const int h = lane >> 5;
   const int l32 = lane & 31;
   // Query tiles of this workgroup: one, or with the causal mask a long and a
-  // short one of the same head.
-  // Query head `head` (of ZH) reads key/value head kvh = head / G (of ZHkv).
+  // short one of the same head.  The grid is dealt over (batch key/value
+  // head, member, slot) for the longest sequence; blocks past their own
+  // sequence's tiles have no work.
   uint32_t kvh_u, head_u, slot_u, qt_a_u, qt_b_u;
-  xcd_tile_grouped(blockIdx.x, (uint32_t)G, (uint32_t)paired_groups(n_qtiles, CAUSAL), &kvh_u, &head_u, &slot_u);
+  xcd_tile_grouped(blockIdx.x, (uint32_t)G, (uint32_t)paired_groups(n_qtiles_max, CAUSAL), &kvh_u, &head_u, &slot_u);
   if (kvh_u >= (uint32_t)ZHkv) return;  // padding block
-  const int head = (int)head_u;
+  const HeadRows hr = head_rows(kvh_u, head_u - kvh_u * (uint32_t)G, (uint32_t)Hkv, (uint32_t)G, N_max, cu, n_tokens);
+  const int N = hr.n;  // this problem's sequence length
+  const int n_qtiles = (N + C::BM - 1) / C::BM;
+  if (slot_u >= (uint32_t)paired_groups(n_qtiles, CAUSAL)) return;  // past this sequence (uniform)
   const int n_items = paired_items(slot_u, n_qtiles, CAUSAL, &qt_a_u, &qt_b_u);
   const int qt_a = (int)qt_a_u, qt_b = (int)qt_b_u;
-  const size_t hoff = (size_t)head * (size_t)N * D;
+  const size_t hoff = (size_t)hr.q_row0 * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const size_t kvoff = (size_t)kvh_u * (size_t)N * D;
+  const size_t kvoff = (size_t)hr.kv_row0 * D;
   const auto rq = make_rsrc(q + hoff, head_bytes);
   const auto rk = make_rsrc(k + kvoff, head_bytes);
   const auto rv = make_rsrc(v + kvoff, head_bytes);
   const auto rdo = make_rsrc(dout + hoff, head_bytes);
-  const auto rl = STATS == kStatsIn ? make_rsrc(lse2 + (size_t)head * N, (uint32_t)N * 4)
-                                    : make_rsrc(lse + (size_t)head * N, (uint32_t)N * 4);
-  const auto rdl = make_rsrc(delta + (size_t)head * N, (uint32_t)N * 4);
+  const auto rl = STATS == kStatsIn ? make_rsrc(lse2 + hr.q_row0, (uint32_t)N * 4)
+                                    : make_rsrc(lse + hr.q_row0, (uint32_t)N * 4);
+  const auto rdl = make_rsrc(delta + hr.q_row0, (uint32_t)N * 4);
   const auto rdq = make_rsrc(dq + hoff, head_bytes);
   auto n_tiles = [&](int qt) {
     const int kv_end = CAUSAL ? min(N, (qt + 1) * C::BM) : N;
@@ -515,9 +534,8 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       }
       dl = half_swap_sum(part[0]);
       if (h == 0) {
-        const size_t plane = (size_t)ZH * (size_t)N;
-        gstore_f32(make_rsrc(stats_out + (size_t)head * N, (uint32_t)N * 4), (uint32_t)query * 4, dl);
-        gstore_f32(make_rsrc(stats_out + plane + (size_t)head * N, (uint32_t)N * 4), (uint32_t)query * 4, l2);
+        gstore_f32(make_rsrc(stats_out + hr.q_row0, (uint32_t)N * 4), (uint32_t)query * 4, dl);
+        gstore_f32(make_rsrc(stats_out + plane + hr.q_row0, (uint32_t)N * 4), (uint32_t)query * 4, l2);
       }
     }
   };
@@ -652,7 +670,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 template <int D, typename T, bool O32>
 static hipError_t launch_pre_t(const BwdArgs& a) {
   constexpr int RPB = 256 / (D / 8);
-  const int64_t rows = a.Z * a.H * a.N;
+  const int64_t rows = a.rows();
   const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
   hipLaunchKernelGGL((fa_bwd_pre_kernel<D, T, O32>), grid, dim3(256), 0, a.stream, a.o,
                      (const uint16_t*)a.dout, a.lse, a.stats, a.stats + rows, rows);
@@ -680,11 +698,14 @@ static hipError_t launch_dkdv_t(const BwdArgs& a) {
   const int ZHkv = (int)(a.Z * a.Hkv);
   const int G = (int)(a.H / a.Hkv);
   const int n_kt = (int)((a.N + C::BK - 1) / C::BK);
-  const int n_qt = (int)((a.N + C::BQ - 1) / C::BQ);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, T, CAUSAL>), dim3((unsigned)a.num_programs), dim3(C::NW * 64), 0,
+  // Packed batches: one workgroup per (sequence key/value head, key tile) of
+  // the longest sequence (units past a sequence's end exit at once).
+  const int64_t grid = a.cu_seqlens ? (int64_t)ZHkv * n_kt : (int64_t)a.num_programs;
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, T, CAUSAL>), dim3((unsigned)grid), dim3(C::NW * 64), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dout, a.stats + a.Z * a.H * a.N, a.stats, (uint16_t*)a.dk, (uint16_t*)a.dv, (int)a.N,
-                     ZHkv, G, n_kt, n_qt, a.scale * kLog2e, a.scale, a.num_programs);
+                     (const uint16_t*)a.dout, a.stats + a.rows(), a.stats, (uint16_t*)a.dk, (uint16_t*)a.dv,
+                     (int)a.N, ZHkv, (int)a.Hkv, G, n_kt, a.scale * kLog2e, a.scale, a.num_programs, a.cu_seqlens,
+                     a.T);
   return hipGetLastError();
 }
 template <int D, typename T>
@@ -728,15 +749,14 @@ hipError_t dkdv_blocks_per_cu(int D, int dtype, int* out) {
 template <int D, typename T, bool CAUSAL, int STATS>
 static hipError_t launch_dq_t(const BwdArgs& a) {
   using C = DqTile<D>;
-  const int ZH = (int)(a.Z * a.H);
   const int ZHkv = (int)(a.Z * a.Hkv);
   const int G = (int)(a.H / a.Hkv);
   const int n_qt = (int)((a.N + C::BM - 1) / C::BM);
   hipLaunchKernelGGL((fa_bwd_dq_kernel<D, T, CAUSAL, STATS>),
                      dim3((unsigned)xcd_grid_grouped(ZHkv, G, paired_groups(n_qt, CAUSAL))), dim3(256), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dout, a.stats + a.Z * a.H * a.N, a.stats, (uint16_t*)a.dq, (int)a.N, ZH, n_qt,
-                     a.scale * kLog2e, a.scale, a.o, a.lse, a.stats, ZHkv, G);
+                     (const uint16_t*)a.dout, a.stats + a.rows(), a.stats, (uint16_t*)a.dq, (int)a.N, a.rows(), n_qt,
+                     a.scale * kLog2e, a.scale, a.o, a.lse, a.stats, ZHkv, (int)a.Hkv, G, a.cu_seqlens, a.T);
   return hipGetLastError();
 }
 template <int D, typename T, int STATS>

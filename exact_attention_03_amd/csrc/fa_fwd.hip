@@ -70,8 +70,8 @@ inline constexpr float kRescaleSlack = kIsBF16<T> ? 0.0f : 8.0f;
 template <int D, typename T, bool CAUSAL, typename OT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdTile<D>::OCC, FwdTile<D>::OCC)))
 void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                   const uint16_t* __restrict__ v, void* __restrict__ o, float* __restrict__ lse, int N,
-                   int ZHkv, int G, int n_qtiles, float c2) {
+                   const uint16_t* __restrict__ v, void* __restrict__ o, float* __restrict__ lse, int N_max,
+                   int ZHkv, int Hkv, int G, int n_qtiles_max, float c2, const int* __restrict__ cu, int64_t n_tokens) {
   using C = FwdTile<D>;
   using Tile = CmTile<C::BN>;
   // One LDS object per ring stage and operand.  With the stage of every
@@ -90,16 +90,20 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int l32 = lane & 31;
 
   // Query tiles of this workgroup: one, or with the causal mask a long and a
-  // short one of the same head (the longest pairs go first).
-  // Query head `head` reads key/value head `kvh` (head / G).
+  // short one of the same head (the longest pairs go first).  The grid is
+  // dealt over (batch key/value head, member, slot) for the longest
+  // sequence; blocks past their own sequence's tiles have no work.
   uint32_t kvh_u, head_u, slot_u, qt_a_u, qt_b_u;
-  xcd_tile_grouped(blockIdx.x, (uint32_t)G, (uint32_t)paired_groups(n_qtiles, CAUSAL), &kvh_u, &head_u, &slot_u);
+  xcd_tile_grouped(blockIdx.x, (uint32_t)G, (uint32_t)paired_groups(n_qtiles_max, CAUSAL), &kvh_u, &head_u, &slot_u);
   if (kvh_u >= (uint32_t)ZHkv) return;  // padding block
+  const HeadRows hr = head_rows(kvh_u, head_u - kvh_u * (uint32_t)G, (uint32_t)Hkv, (uint32_t)G, N_max, cu, n_tokens);
+  const int N = hr.n;  // this problem's sequence length
+  const int n_qtiles = (N + C::BM - 1) / C::BM;
+  if (slot_u >= (uint32_t)paired_groups(n_qtiles, CAUSAL)) return;  // past this sequence (uniform)
   const int n_items = paired_items(slot_u, n_qtiles, CAUSAL, &qt_a_u, &qt_b_u);
   const int qt_a = (int)qt_a_u, qt_b = (int)qt_b_u;
-  const int head = (int)head_u;
-  const size_t hoff = (size_t)head * (size_t)N * D;
-  const size_t kvoff = (size_t)kvh_u * (size_t)N * D;
+  const size_t hoff = (size_t)hr.q_row0 * D;
+  const size_t kvoff = (size_t)hr.kv_row0 * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc(q + hoff, head_bytes);
   const auto rk = make_rsrc(k + kvoff, head_bytes);
@@ -285,7 +289,7 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       }
     }
     if (h == 0) {
-      const auto rl = make_rsrc(lse + (size_t)head * N, (uint32_t)N * 4);
+      const auto rl = make_rsrc(lse + hr.q_row0, (uint32_t)N * 4);
       gstore_f32(rl, (uint32_t)query * 4, (m_run + __log2f(lsum)) * kLn2);
     }
     first_tile_issued = chain;
@@ -306,7 +310,7 @@ hipError_t launch_fwd_t(const FwdArgs& a) {
   const dim3 grid((unsigned)xcd_grid_grouped(ZHkv, G, paired_groups(n_qtiles, CAUSAL)));
   hipLaunchKernelGGL((fa_fwd_kernel<D, T, CAUSAL, OT>), grid, dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.lse,
-                     (int)a.N, ZHkv, G, n_qtiles, a.scale * kLog2e);
+                     (int)a.N, ZHkv, (int)a.Hkv, G, n_qtiles, a.scale * kLog2e, a.cu_seqlens, a.T);
   return hipGetLastError();
 }
 

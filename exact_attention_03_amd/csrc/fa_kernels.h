@@ -16,6 +16,11 @@ struct FwdArgs {
   float scale;
   int causal;
   hipStream_t stream;
+  // Variable-length batches: Z sequences packed head-major, (H, T, D), with
+  // sequence z at tokens cu_seqlens[z] .. cu_seqlens[z+1]-1 (device int32)
+  // and N the longest sequence.  nullptr for dense (Z, H, N, D) batches.
+  const int* cu_seqlens = nullptr;
+  int64_t T = 0;
 };
 
 struct BwdArgs {
@@ -35,6 +40,11 @@ struct BwdArgs {
   // stats (instead of reading them from the preprocess pass).
   bool dq_stats;
   hipStream_t stream;
+  const int* cu_seqlens = nullptr;  // as in FwdArgs
+  int64_t T = 0;
+  // Query rows of every head and problem together: Z*H*N dense, H*T packed
+  // (the offset of the second plane of stats).
+  int64_t rows() const { return cu_seqlens ? H * T : Z * H * N; }
 };
 
 hipError_t launch_fwd(const FwdArgs& a);

@@ -118,4 +118,40 @@ FA_SCHED_HD void xcd_tile_grouped(uint32_t b, uint32_t G, uint32_t n_slots, uint
   *slot = s % n_slots;
 }
 
+// Rows of one (sequence, query head) problem and of its key/value head.
+// Dense batches are (Z, H, N, D): the problem of query head hq of batch z
+// starts at row (z H + hq) N and has N rows.  Variable-length batches are
+// packed head-major, (H, T, D) with sequence b at tokens cu[b] .. cu[b+1]-1:
+// the problem starts at row hq T + cu[b] and has cu[b+1] - cu[b] rows.  The
+// grids deal "batch key/value heads" bkv in [0, batch * Hkv) (bkv = z Hkv +
+// hk) and members m in [0, G) of each (query head hk G + m).
+struct HeadRows {
+  int64_t q_row0;   // first row of the query head's problem (Q, O, dO, lse, ...)
+  int64_t kv_row0;  // first row of the key/value head's problem (K, V, dK, dV)
+  int64_t q_stride; // rows from one query head of the group to the next
+  int n;            // rows of the problem (the sequence length)
+};
+FA_SCHED_HD HeadRows head_rows(uint32_t bkv, uint32_t member, uint32_t Hkv, uint32_t G, int N, const int* cu,
+                               int64_t T) {
+  HeadRows r;
+  if (cu == nullptr) {
+    r.q_row0 = ((int64_t)bkv * G + member) * N;
+    r.kv_row0 = (int64_t)bkv * N;
+    r.q_stride = N;
+    r.n = N;
+  } else {
+    // Offsets are clamped into [0, T], so that no offsets array, however
+    // wrong, makes a kernel touch rows outside the tensors.
+    const uint32_t b = bkv / Hkv, hk = bkv % Hkv;
+    const int64_t s0 = cu[b], s1 = cu[b + 1];
+    const int64_t start = s0 < 0 ? 0 : (s0 > T ? T : s0);
+    const int64_t end = s1 < start ? start : (s1 > T ? T : s1);
+    r.n = (int)(end - start);
+    r.q_row0 = ((int64_t)hk * G + member) * T + start;
+    r.kv_row0 = (int64_t)hk * T + start;
+    r.q_stride = T;
+  }
+  return r;
+}
+
 }  // namespace fa

@@ -209,6 +209,57 @@ int fa_bwd_dkdv_gqa(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int
                     int num_programs, hipStream_t stream);
 
 /*
+ * Variable-length batches.  [Serving-Ascend] (the page named above, sections
+ * "GQA Paged Attention" and the integration discussion before it) has the
+ * sequences of one batch differ in length (context_lens), with tokens past a
+ * sequence's end taking no part.  Here the B sequences are packed one after
+ * another along the token axis, head-major:
+ *   q, o, dout, dq : (H, T, D);  k, v, dk, dv : (Hkv, T, D);  lse : (H, T);
+ *   cu_seqlens     : DEVICE int32[B+1], token offsets: sequence b is tokens
+ *                    cu_seqlens[b] .. cu_seqlens[b+1]-1 of every head
+ *                    (0 = cu_seqlens[0] <= ... <= cu_seqlens[B] = T; empty
+ *                    sequences allowed); read by the kernels, never written;
+ *   max_seqlen     : at least the longest sequence (it sizes the grids; the
+ *                    tiles of a longer sequence past max_seqlen are not
+ *                    computed and their outputs are left unwritten);
+ *   workspace      : fa_bwd_workspace_bytes(1, H, T, D) bytes (stats are
+ *                    (2, H, T) for the stage forms).
+ * Each sequence is its own attention problem (causal within itself when
+ * causal = 1) with the grouping of fa_fwd_gqa (Hkv = H for plain heads).
+ * Offsets outside [0, T] or decreasing are clamped into range by the kernels,
+ * so no offsets array makes them access memory outside the tensors; the
+ * results for such an array are unspecified.  Errors as for fa_fwd_gqa /
+ * fa_bwd_gqa, plus FA_ERR_INVALID_ARGUMENT for a NULL or misaligned
+ * cu_seqlens or T < 0, and FA_ERR_UNSUPPORTED when G * (T + 256) * D * 2 or
+ * (T + 256) * D * 4 reaches 2^31.  B*H*T == 0 is an empty problem.
+ * The dK/dV stage of a packed batch runs one workgroup per (sequence
+ * key/value head, key tile), first key tiles first, instead of the
+ * persistent schedule (whose static dealing does not know the lengths):
+ * fa_bwd_dkdv_varlen ignores num_programs.
+ */
+int fa_fwd_varlen(int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t max_seqlen,
+                  int64_t D, int dtype, int o_dtype, const int32_t* cu_seqlens,
+                  const void* q, const void* k, const void* v, void* o, float* lse,
+                  float scale, int causal, hipStream_t stream);
+int fa_bwd_varlen(int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t max_seqlen,
+                  int64_t D, int dtype, int o_dtype, const int32_t* cu_seqlens,
+                  const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                  float scale, int causal, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+int fa_bwd_dq_and_stats_varlen(int64_t B, int64_t H, int64_t Hkv, int64_t T,
+                               int64_t max_seqlen, int64_t D, int dtype, int o_dtype,
+                               const int32_t* cu_seqlens, const void* q, const void* k,
+                               const void* v, const void* o, const void* dout,
+                               const float* lse, float* stats, void* dq, float scale,
+                               int causal, hipStream_t stream);
+int fa_bwd_dkdv_varlen(int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t max_seqlen,
+                       int64_t D, int dtype, const int32_t* cu_seqlens, const void* q,
+                       const void* k, const void* v, const void* dout,
+                       const float* stats, void* dk, void* dv, float scale, int causal,
+                       int num_programs, hipStream_t stream);
+
+/*
  * Device facts used for launch sizing, for the current device: compute
  * units, and the persistent grid fa_bwd_dkdv uses for (D, dtype) when
  * num_programs is 0.  Either output pointer may be NULL.

@@ -114,3 +114,30 @@ def oracle_group(cpu, z, kvh, scale, causal):
     O, lse = oracle.attention_forward_gqa(qq, kk, vv, scale, causal)
     dq, dk, dv = oracle.attention_backward_gqa(qq, kk, vv, dd, scale, causal)
     return {"heads": heads, "O": O[0], "lse": lse[0], "dq": dq[0], "dk": dk[0, 0], "dv": dv[0, 0]}
+
+
+def varlen_device_inputs(w: workloads.Workload):
+    """(cpu tensors, gpu tensors, gpu int32 offsets) of a variable-length workload."""
+    import torch
+
+    cpu, gpu = device_inputs(w)
+    cu = torch.from_numpy(w.cu_seqlens).cuda()
+    return cpu, gpu, cu
+
+
+def oracle_varlen_group(cpu, cu_seqlens, b, kvh, scale, causal):
+    """Oracle for sequence b and key/value head kvh (with its G query heads)
+    of a packed variable-length input: {"heads", "rows" (slice), "O", "lse",
+    "dq", "dk", "dv"} over that sequence's rows only."""
+    q, k, v, do = cpu
+    H, Hkv = q.shape[0], k.shape[0]
+    G = H // Hkv
+    s, e = int(cu_seqlens[b]), int(cu_seqlens[b + 1])
+    hs = slice(kvh * G, (kvh + 1) * G)
+    qq, dd = to_f64(q[hs, s:e]), to_f64(do[hs, s:e])
+    kk, vv = to_f64(k[kvh:kvh + 1, s:e]), to_f64(v[kvh:kvh + 1, s:e])
+    one = [0, e - s]
+    O, lse = oracle.attention_forward_varlen(qq, kk, vv, one, scale, causal)
+    dq, dk, dv = oracle.attention_backward_varlen(qq, kk, vv, dd, one, scale, causal)
+    return {"heads": list(range(kvh * G, (kvh + 1) * G)), "rows": slice(s, e), "O": O, "lse": lse, "dq": dq,
+            "dk": dk[0], "dv": dv[0]}

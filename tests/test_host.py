@@ -170,3 +170,26 @@ def test_grouped_head_argument_errors(fa):
         assert "group" in fa.last_error()
     assert lib.fa_fwd_gqa(1, 0, 0, 128, 64, 0, 0, *([None] * 5), 0.125, 0, None) == 0  # no heads: empty
     assert lib.fa_bwd_gqa(0, 4, 2, 128, 64, 0, 0, *([None] * 9), 0.125, 0, None, 0, None) == 0
+
+
+def test_varlen_argument_errors(fa):
+    lib = fa.lib()
+    CU = ctypes.c_void_p(0x20000)
+
+    def fwd(B=2, H=4, Hkv=2, T=100, mx=60, D=64, cu=CU):
+        return lib.fa_fwd_varlen(B, H, Hkv, T, mx, D, 0, 0, cu, P, P, P, P, P, 0.125, 1, None)
+
+    def bwd(B=2, H=4, Hkv=2, T=100, mx=60, D=64, cu=CU, ws=1 << 30):
+        return lib.fa_bwd_varlen(B, H, Hkv, T, mx, D, 0, 0, cu, *([P] * 9), 0.125, 1, P, ws, None)
+
+    for f in (fwd, bwd):
+        assert f(cu=None) == 1 and "cu_seqlens" in fa.last_error()
+        assert f(cu=ctypes.c_void_p(0x20002)) == 1                 # misaligned offsets
+        assert f(T=-1) == 1
+        assert f(H=6, Hkv=4) == 1                                   # grouping
+        assert f(D=96) == 2
+        assert f(T=1 << 26, D=128) == 2 and "packed" in fa.last_error()
+        assert f(B=0, cu=None) == 0 and f(T=0) == 0 and f(mx=0, cu=None) == 0  # empty problems
+    assert bwd(ws=2 * 4 * 100 * 4 - 4) == 1 and "workspace" in fa.last_error()
+    assert lib.fa_bwd_dkdv_varlen(2, 4, 2, 100, 60, 64, 0, CU, *([P] * 4), None, P, P, 0.125, 1, 0, None) == 1
+    assert lib.fa_bwd_dq_and_stats_varlen(2, 4, 2, 100, 60, 64, 0, 1, CU, *([P] * 8), 0.125, 1, None) == 1

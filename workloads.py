@@ -9,7 +9,11 @@ Recipe (one generator per workload, PCG64 through ``numpy.random.default_rng``):
 * seed = the workload's index (1..5);
 * draw, in this order, ``q, k, v, do`` as ``standard_normal(shape, float32)``
   with shape (Z, H, N, D) for q and do and (Z, Hkv, N, D) for k and v (Hkv =
-  H except for the grouped key/value head workload);
+  H except for the grouped key/value head workload); a variable-length
+  workload draws, in the same order, q and do of shape (H, T, D) and k and v
+  of shape (Hkv, T, D), T the sum of its sequence lengths (packed head-major);
+* variable-length workloads take their sequence lengths from a generator of
+  their own, ``default_rng(1000 + seed).integers(lo, hi + 1, size=B)``;
 * for the long-sequence workload only, multiply q and k by 2 in float32 (exact),
   which sharpens the softmax and exercises the running-max rescaling;
 * cast to the workload's dtype with round-to-nearest-even.
@@ -39,6 +43,7 @@ class Workload:
     causal: bool
     qk_gain: float = 1.0  # multiplier applied to q and k in float32
     Hkv: int = 0          # key/value heads (0 = H: one per query head)
+    lengths: tuple = ()   # variable-length batch: per-sequence lengths (Z = count, N = longest)
 
     @property
     def scale(self) -> float:
@@ -59,6 +64,28 @@ class Workload:
     @property
     def heads(self) -> int:
         return self.Z * self.H
+
+    @property
+    def varlen(self) -> bool:
+        return len(self.lengths) > 0
+
+    @property
+    def T(self) -> int:
+        """Tokens of a variable-length batch (sum of the lengths)."""
+        return int(sum(self.lengths))
+
+    @property
+    def cu_seqlens(self):
+        """Token offsets (B+1,) int32 of a variable-length batch."""
+        return np.concatenate([[0], np.cumsum(np.asarray(self.lengths, dtype=np.int64))]).astype(np.int32)
+
+    @property
+    def q_shape(self):
+        return (self.H, self.T, self.D) if self.varlen else self.shape
+
+    @property
+    def kv_draw_shape(self):
+        return (self.kv_heads, self.T, self.D) if self.varlen else self.kv_shape
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -83,6 +110,19 @@ WORKLOADS = {
 }
 
 
+def draw_lengths(seed: int, count: int, lo: int, hi: int) -> tuple:
+    """Sequence lengths of a variable-length workload: uniform integers in
+    [lo, hi] from the workload's own length generator."""
+    rng = np.random.default_rng(1000 + seed)
+    return tuple(int(x) for x in rng.integers(lo, hi + 1, size=count))
+
+
+_VARLEN_LENGTHS = draw_lengths(7, 32, 64, 4096)
+# A variable-length causal batch: 32 sequences of 64..4096 tokens, 16 heads.
+WORKLOADS["varlen_causal_bf16"] = Workload("varlen_causal_bf16", 7, len(_VARLEN_LENGTHS), 16, max(_VARLEN_LENGTHS),
+                                           128, "bf16", True, 1.0, 0, _VARLEN_LENGTHS)
+
+
 def by_name(name: str) -> Workload:
     return WORKLOADS[name]
 
@@ -97,7 +137,7 @@ def draw_f32(w: Workload, heads: slice | None = None):
     rng = np.random.default_rng(w.seed)
     out = []
     for name in ("q", "k", "v", "do"):
-        x = rng.standard_normal(size=w.kv_shape if name in ("k", "v") else w.shape, dtype=np.float32)
+        x = rng.standard_normal(size=w.kv_draw_shape if name in ("k", "v") else w.q_shape, dtype=np.float32)
         if name in ("q", "k") and w.qk_gain != 1.0:
             x *= np.float32(w.qk_gain)
         out.append(x)
