@@ -10,7 +10,8 @@ CV Pipeline 优化实战" ("Porting FlashAttention to Ascend: CV-pipeline
 optimisation with Triton-Ascend", BiumBiu, 2026-08-30), cited below as
 [FA-Ascend] with the section it comes from; the grouped key/value heads follow
 the page "从算子到 Serving：昇腾推理评测链路实践" (BiumBiu, 2026-04-30), cited
-as [Serving-Ascend].
+as [Serving-Ascend], as do the variable-length batches and the paged KV cache
+(``paged.py``: cache writes and decode attention over pages).
 
 Pinning: every function here is pinned by tests marked ``not gpu`` to facts
 other than itself (finite differences, closed forms, invariants, a library
@@ -28,3 +29,4 @@ from .attention import (  # noqa: F401
     attention_forward_varlen,
     attention_backward_varlen,
 )
+from .paged import gather_context, paged_decode, reshape_and_cache  # noqa: F401
