@@ -371,15 +371,182 @@ def run(args):
     return out
 
 
+# ------------------------------------------------------------------ paged decode
+def decode_bytes(w, lens) -> float:
+    """Algorithmic HBM bytes of one decode step: the new tokens' K / V rows
+    read and written into the cache, every cached K and V element of the
+    contexts read once, q read, O (16-bit) and lse written, the block-table
+    entries of the contexts and the context lengths read."""
+    import numpy as np
+
+    lens = np.asarray(lens, dtype=np.int64)
+    e = 2  # bytes per 16-bit element
+    ctx = float(lens.sum()) * w.Hkv * w.D * 2 * e
+    new = float(w.B) * w.Hkv * w.D * 2 * e * 2
+    qo = float(w.B) * w.H * w.D * e * 2 + w.B * w.H * 4
+    tables = float((-(-lens // w.block_size)).sum()) * 4 + w.B * 4
+    return ctx + new + qo + tables
+
+
+def _oracle_decode(args):
+    import oracle
+
+    q, kc, vc, tables, lens, scale = args
+    oracle.paged_decode(q, kc, vc, tables, lens, scale)
+    return len(lens)
+
+
+def decode_cpu_baseline(w, cpu, n_seq: int, workers: int):
+    """The paged-decode oracle on the first n_seq sequences (one process per
+    chunk of sequences, one BLAS thread each), in the same GB/s unit."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    import numpy as np
+
+    q, kc, vc, tables, lens = cpu
+    n_seq = min(n_seq, w.B)
+    # The oracle reads only the pages of the sampled sequences: hand each
+    # worker those pages, renumbered.
+    jobs = []
+    for c in np.array_split(np.arange(n_seq), max(1, min(workers, n_seq))):
+        if not len(c):
+            continue
+        t = tables[c].numpy()
+        used = sorted({int(x) for x in t.flatten() if x >= 0})
+        remap = {b: i for i, b in enumerate(used)}
+        t2 = np.vectorize(lambda x: remap.get(int(x), -1))(t).astype(np.int32)
+        jobs.append((q[c].float().numpy(), kc[used].float().numpy(), vc[used].float().numpy(), t2,
+                     lens[c].numpy(), w.scale))
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"
+    try:
+        with cf.ProcessPoolExecutor(max_workers=len(jobs), mp_context=mp.get_context("spawn")) as ex:
+            t0 = time.perf_counter()
+            done = sum(ex.map(_oracle_decode, jobs))
+            dt = time.perf_counter() - t0
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    sub = lens[:done].numpy()
+    nbytes = decode_bytes(w, sub) * 1.0
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": len(jobs), "kind": "oracle",
+            "sample": (f"fp64 numpy paged-decode oracle (token-by-token gather through the block table, plain "
+                       f"softmax) on {done} of {w.B} sequences ({int(sub.sum())} context tokens) of the same "
+                       f"seeded workload, {len(jobs)} processes x 1 BLAS thread, wall {dt:.2f} s (process start "
+                       f"included); bytes counted as for the GPU")}
+
+
+def run_decode(args):
+    """One step = fa_reshape_and_cache of one new token per sequence (at the
+    last position of its context) + fa_paged_decode over the whole context."""
+    import numpy as np
+    import torch
+
+    import exact_attention_03_amd as fa
+
+    w = workloads.DECODE_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cpu = workloads.make_decode_inputs(w)
+    q, kc, vc, tables, lens = (t.to(dev) for t in cpu)
+    lens_np = cpu[4].numpy().astype(np.int64)
+    tab_np = cpu[3].numpy()
+    slots = torch.tensor([int(tab_np[b, (n - 1) // w.block_size]) * w.block_size + (n - 1) % w.block_size
+                          for b, n in enumerate(lens_np)], dtype=torch.int64, device=dev)
+    gen = torch.Generator().manual_seed(w.seed)
+    new_k = torch.randn((w.B, w.Hkv, w.D), generator=gen).to(q.dtype).to(dev)
+    new_v = torch.randn((w.B, w.Hkv, w.D), generator=gen).to(q.dtype).to(dev)
+    o = torch.empty((w.B, w.H, w.D), dtype=q.dtype, device=dev)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+    L = fa.lib()
+    code = fa._dtype_code(q)
+    nb, mxb = kc.shape[0], tables.shape[1]
+    ws_bytes = L.fa_paged_decode_workspace_bytes(w.B, w.H, w.Hkv, w.D, w.hi)
+    ws = torch.empty((max(1, ws_bytes // 4),), dtype=torch.float32, device=dev)
+    P = lambda t: t.data_ptr()  # noqa: E731
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def call(st, name):
+        if st != 0:
+            raise fa.FAError(st, name, fa.last_error())
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        call(L.fa_reshape_and_cache(w.B, w.Hkv, w.D, w.block_size, nb, code, P(new_k), P(new_v), P(slots), P(kc),
+                                    P(vc), sp), "fa_reshape_and_cache")
+        if ev is not None:
+            ev[1].record(stream)
+        call(L.fa_paged_decode(w.B, w.H, w.Hkv, w.D, w.block_size, nb, mxb, w.hi, code, code, P(q), P(kc), P(vc),
+                               P(tables), P(lens), P(o), P(lse), w.scale, P(ws), ws_bytes, sp), "fa_paged_decode")
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    cache_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    nbytes = decode_bytes(w, lens_np)
+    dec_bytes = nbytes - float(w.B) * w.Hkv * w.D * 2 * 2 * 2  # the cache write's bytes are the other kernel's
+    splits = max(1, ws_bytes // (4 * w.B * w.H * (w.D + 1))) if ws_bytes else 1
+    ach = dec_bytes / (dec_ms * 1e-3) / 1e9
+    out = {
+        "metric": "paged decode attention (cache write + decode) HBM GB/s on 1 MI355X",
+        "value": round(nbytes / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} sequences, contexts {int(lens_np.min())}..{int(lens_np.max())} "
+                               f"tokens ({int(lens_np.sum())} total), H={w.H} Hkv={w.Hkv} D={w.D} pages of "
+                               f"{w.block_size} tokens, {w.dtype}, {splits} context splits",
+                   "B": w.B, "H": w.H, "Hkv": w.Hkv, "D": w.D, "block_size": w.block_size, "seed": w.seed},
+        "breakdown": {"reshape_and_cache_ms": round(cache_ms, 4), "paged_decode_ms": round(dec_ms, 4),
+                      "splits": splits},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "fa_paged_decode (decode kernel and, with splits, its combine kernel)",
+                     "algorithmic": {"amount": dec_bytes, "unit": "byte", "per_launch": True}},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = decode_cpu_baseline(w, cpu, args.cpu_decode_seqs, args.cpu_workers)
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    choices=sorted(workloads.WORKLOADS) + sorted(workloads.DECODE_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-heads", type=int, default=384, help="heads in the oracle timing sample")
     ap.add_argument("--cpu-workers", type=int, default=min(16, len(os.sched_getaffinity(0))))
+    ap.add_argument("--cpu-decode-seqs", type=int, default=64, help="sequences in the decode oracle timing sample")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before warm-up, copy a buffer of this many MiB (for HBM counter calibration)")
     args = ap.parse_args(argv)
@@ -390,7 +557,7 @@ def main(argv=None):
         return 2
     if args.steps < 1 or args.warmup < 0:
         ap.error("--steps must be >= 1 and --warmup >= 0")
-    out = run(args)
+    out = run_decode(args) if args.workload in workloads.DECODE_WORKLOADS else run(args)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -20,7 +20,8 @@ import math
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32, FAError, check, last_error, lib,  # noqa: F401
                    status_name)
 
-__all__ = ["forward", "backward", "forward_varlen", "backward_varlen", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_dq_and_stats", "workspace_bytes",
+__all__ = ["forward", "backward", "forward_varlen", "backward_varlen", "reshape_and_cache", "paged_decode",
+           "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_dq_and_stats", "workspace_bytes",
            "device_info", "dkdv_schedule", "fwd_tile_pairs", "FAError", "lib"]
 
 
@@ -221,6 +222,68 @@ def backward_varlen(q, k, v, o, do, lse, cu_seqlens, max_seqlen=None, causal=Fal
                                  _scale(scale, D), int(bool(causal)), _ptr(ws), ws.numel() * 4, _stream(q))
     check(st, "fa_bwd_varlen")
     return dq, dk, dv
+
+
+def reshape_and_cache(key, value, slot_mapping, k_cache, v_cache):
+    """Write new tokens into a paged cache, in place.
+
+    key, value: (num_tokens, Hkv, D); slot_mapping: int64 GPU tensor
+    (num_tokens,), negative = skip; k_cache: (num_blocks, Hkv, D/8, block_size, 8)
+    (keys in chunks of 8 channels, chunk-major), v_cache: (num_blocks, Hkv, D,
+    block_size) (values transposed), both of key's dtype.
+    """
+    torch = _torch()
+    T, Hkv, D = key.shape
+    nb, bs = k_cache.shape[0], k_cache.shape[3]
+    for t, n, shp in ((key, "key", (T, Hkv, D)), (value, "value", (T, Hkv, D)),
+                      (k_cache, "k_cache", (nb, Hkv, D // 8, bs, 8)), (v_cache, "v_cache", (nb, Hkv, D, bs))):
+        if not t.is_cuda or tuple(t.shape) != shp or not t.is_contiguous() or t.dtype != key.dtype:
+            raise ValueError(f"{n} must be a contiguous GPU tensor of shape {shp} and dtype {key.dtype}")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,) or not slot_mapping.is_cuda:
+        raise ValueError("slot_mapping must be an int64 GPU tensor of shape (num_tokens,)")
+    with torch.cuda.device(key.device):
+        st = lib().fa_reshape_and_cache(T, Hkv, D, bs, nb, _dtype_code(key), _ptr(key), _ptr(value),
+                                        _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), _stream(key))
+    check(st, "fa_reshape_and_cache")
+
+
+def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len=None, scale=None,
+                 out_dtype=None):
+    """Decode attention over a paged cache: (O (B, H, D), lse (B, H)).
+
+    q: (B, H, D); caches as for ``reshape_and_cache``; block_tables: int32
+    (B, max_blocks); context_lens: int32 (B,).  max_context_len (host int)
+    sizes the split of long contexts; read from context_lens when omitted.
+    """
+    torch = _torch()
+    B, H, D = q.shape
+    if k_cache.dim() != 5:
+        raise ValueError("k_cache must be (num_blocks, Hkv, D/8, block_size, 8)")
+    nb, Hkv, _, bs, _ = k_cache.shape
+    if k_cache.shape != (nb, Hkv, D // 8, bs, 8) or v_cache.shape != (nb, Hkv, D, bs):
+        raise ValueError("caches must be (num_blocks, Hkv, D/8, block_size, 8) and (num_blocks, Hkv, D, block_size)")
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{n} must be a contiguous GPU tensor of q's dtype and device")
+    for t, n in ((block_tables, "block_tables"), (context_lens, "context_lens")):
+        if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 GPU tensor")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be (B, max_blocks) and context_lens (B,)")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if B > 0 else 0
+    odt = q.dtype if out_dtype is None else out_dtype
+    with torch.cuda.device(q.device):
+        o = torch.empty((B, H, D), dtype=odt, device=q.device)
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+        nbytes = lib().fa_paged_decode_workspace_bytes(B, H, Hkv, D, int(max_context_len))
+        ws = torch.empty((max(1, nbytes // 4),), dtype=torch.float32, device=q.device)
+        st = lib().fa_paged_decode(B, H, Hkv, D, bs, nb, block_tables.shape[1], int(max_context_len), _dtype_code(q),
+                                   _dtype_code(o), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                   _ptr(context_lens), _ptr(o), _ptr(lse), _scale(scale, D), _ptr(ws), nbytes,
+                                   _stream(q))
+    check(st, "fa_paged_decode")
+    return o, lse
 
 
 def bwd_preprocess(o, do, lse):

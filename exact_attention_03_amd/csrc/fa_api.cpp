@@ -476,6 +476,87 @@ int fa_bwd_dkdv_varlen(int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t max
                    stream, Packing{cu_seqlens, T});
 }
 
+int fa_reshape_and_cache(int64_t num_tokens, int64_t Hkv, int64_t D, int64_t block_size, int64_t num_blocks,
+                         int dtype, const void* key, const void* value, const int64_t* slot_mapping, void* k_cache,
+                         void* v_cache, hipStream_t stream) {
+  g_last_error.clear();
+  if (num_tokens < 0 || Hkv < 0 || num_blocks < 0 || block_size < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "negative size (num_tokens=%lld Hkv=%lld num_blocks=%lld block_size=%lld)",
+                (long long)num_tokens, (long long)Hkv, (long long)num_blocks, (long long)block_size);
+  if (D != 64 && D != 128 && D != 256)
+    return fail(FA_ERR_UNSUPPORTED, "head dim D=%lld not supported (64, 128 or 256)", (long long)D);
+  if (block_size < 16 || block_size > 1024 || block_size % 16 != 0)
+    return fail(FA_ERR_UNSUPPORTED, "block_size=%lld must be a multiple of 16 in [16, 1024]", (long long)block_size);
+  FA_TRY(check_dtypes(dtype, dtype, false));
+  if (num_tokens == 0 || Hkv == 0 || num_blocks == 0) return FA_OK;
+  if (num_tokens * Hkv > kMaxI32 * 8) return fail(FA_ERR_UNSUPPORTED, "too many tokens");
+  FA_TRY(check_ptr(key, "key"));
+  FA_TRY(check_ptr(value, "value"));
+  FA_TRY(check_ptr(k_cache, "k_cache"));
+  FA_TRY(check_ptr(v_cache, "v_cache"));
+  if (slot_mapping == nullptr || reinterpret_cast<uintptr_t>(slot_mapping) % 8 != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "slot_mapping is NULL or not 8-byte aligned");
+  fa::CacheArgs a{num_tokens, Hkv, D, block_size, num_blocks, key, value, slot_mapping, k_cache, v_cache, stream};
+  return finish(fa::launch_reshape_and_cache(a), stream, "fa_reshape_and_cache launch");
+}
+
+size_t fa_paged_decode_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t max_context_len) {
+  if (B <= 0 || H <= 0 || Hkv <= 0 || D <= 0) return 0;
+  const int s = fa::decode_split(B, Hkv, max_context_len).n_splits;
+  return s > 1 ? (size_t)(B * H * s * (D + 1)) * sizeof(float) : 0;
+}
+
+int fa_paged_decode(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_size, int64_t num_blocks,
+                    int64_t max_blocks_per_seq, int64_t max_context_len, int dtype, int o_dtype, const void* q,
+                    const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                    const int32_t* context_lens, void* o, float* lse, float scale, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  if (B < 0 || H < 0 || Hkv < 0 || num_blocks < 0 || block_size < 0 || max_blocks_per_seq < 0 ||
+      max_context_len < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "negative size");
+  if (D != 64 && D != 128 && D != 256)
+    return fail(FA_ERR_UNSUPPORTED, "head dim D=%lld not supported (64, 128 or 256)", (long long)D);
+  if (block_size < 16 || block_size > 1024 || block_size % 16 != 0)
+    return fail(FA_ERR_UNSUPPORTED, "block_size=%lld must be a multiple of 16 in [16, 1024]", (long long)block_size);
+  FA_TRY(check_dtypes(dtype, o_dtype, true));
+  FA_TRY(check_scale(scale, 0));
+  if (H > 0 && (Hkv == 0 || H % Hkv != 0))
+    return fail(FA_ERR_INVALID_ARGUMENT, "H=%lld query heads must be a whole multiple of Hkv=%lld", (long long)H,
+                (long long)Hkv);
+  if (B == 0 || H == 0) return FA_OK;
+  if (H / Hkv > 16)
+    return fail(FA_ERR_UNSUPPORTED, "at most 16 query heads per key/value head (H/Hkv=%lld)", (long long)(H / Hkv));
+  if (B * H > kMaxI32 || max_blocks_per_seq > kMaxI32 || num_blocks > kMaxI32 ||
+      max_blocks_per_seq * block_size > kMaxI32)
+    return fail(FA_ERR_UNSUPPORTED, "problem too large");
+  FA_TRY(check_ptr(q, "q"));
+  FA_TRY(check_ptr(k_cache, "k_cache"));
+  FA_TRY(check_ptr(v_cache, "v_cache"));
+  FA_TRY(check_ptr(o, "o"));
+  if (block_tables == nullptr || context_lens == nullptr ||
+      reinterpret_cast<uintptr_t>(block_tables) % 4 != 0 || reinterpret_cast<uintptr_t>(context_lens) % 4 != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "block_tables / context_lens NULL or not 4-byte aligned");
+  if (lse != nullptr && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "lse is not 4-byte aligned");
+  const fa::DecodeSplit split = fa::decode_split(B, Hkv, max_context_len);
+  const size_t need = fa_paged_decode_workspace_bytes(B, H, Hkv, D, max_context_len);
+  if (need > 0) {
+    if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+      return fail(FA_ERR_INVALID_ARGUMENT, "workspace is NULL or not 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                  workspace_bytes, need);
+  }
+  fa::DecodeArgs a{};
+  a.B = B; a.H = H; a.Hkv = Hkv; a.D = D; a.block_size = block_size; a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq; a.dtype = dtype; a.o_dtype = o_dtype; a.q = q; a.k_cache = k_cache;
+  a.v_cache = v_cache; a.block_tables = block_tables; a.context_lens = context_lens; a.o = o; a.lse = lse;
+  a.scale = scale; a.n_splits = split.n_splits; a.chunk = split.chunk; a.workspace = static_cast<float*>(workspace);
+  a.stream = stream;
+  return finish(fa::launch_paged_decode(a), stream, "fa_paged_decode launch");
+}
+
 int fa_device_info(int64_t D, int dtype, int* compute_units, int* dkdv_programs) {
   g_last_error.clear();
   FA_TRY(check_shape(Shape{1, 1, 1, D}));

@@ -84,6 +84,39 @@ FA_DEV f32x16 mfma32<BF16>(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 // Two fp32 values to one dword of two 16-bit values, round to nearest even.
+// v_mfma_f32_16x16x32_{f16,bf16} (A 16(m) x 32(k), B 32(k) x 16(n)) and
+// v_mfma_f32_16x16x16_{f16,bf16} (k = 16).  Lane l (g = l/16) supplies
+// A[m = l%16][k in K_g] and B[k in K_g][n = l%16], the same set K_g for A and
+// B (this library feeds k = 8g + i, i = 0..7, and k = 4g + i, i = 0..3); the
+// 16x16 fp32 result lands in 4 registers per lane: register i of lane l holds
+// C[m = 4g + i][n = l%16].  That is the B-operand layout of a k = 16 product,
+// so a result can feed the next product as its B operand directly.
+template <typename T>
+FA_DEV f32x4 mfma16k32(u32x4 a, u32x4 b, f32x4 c);
+template <>
+FA_DEV f32x4 mfma16k32<F16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                0, 0);
+}
+template <>
+FA_DEV f32x4 mfma16k32<BF16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+FA_DEV f32x4 mfma16k16(u32x2 a, u32x2 b, f32x4 c);
+template <>
+FA_DEV f32x4 mfma16k16<F16>(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a), __builtin_bit_cast(f16x4, b), c, 0, 0,
+                                               0);
+}
+template <>
+FA_DEV f32x4 mfma16k16<BF16>(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c,
+                                                   0, 0, 0);
+}
+
 template <typename T>
 FA_DEV uint32_t pack2(float a, float b);
 template <>
@@ -169,6 +202,9 @@ FA_DEV float gload_f32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 }
 FA_DEV void gstore_f32(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+FA_DEV u32x2 gload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
 }
 
 // Global -> LDS copy without a register round trip (gfx950 16-byte buffer

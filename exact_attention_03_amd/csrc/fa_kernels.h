@@ -47,6 +47,63 @@ struct BwdArgs {
   int64_t rows() const { return cu_seqlens ? H * T : Z * H * N; }
 };
 
+// Paged KV cache writes: token i's key / value rows (num_tokens, Hkv, D) go
+// to block slots[i] / block_size, offset slots[i] % block_size.
+struct CacheArgs {
+  int64_t num_tokens, Hkv, D, block_size, num_blocks;
+  const void *key, *value;
+  const int64_t* slots;
+  void *k_cache, *v_cache;
+  hipStream_t stream;
+};
+
+// Decode attention over a paged cache (one query token per sequence).
+struct DecodeArgs {
+  int64_t B, H, Hkv, D, block_size, num_blocks, max_blocks;
+  int dtype, o_dtype;
+  const void *q, *k_cache, *v_cache;
+  const int* block_tables;
+  const int* context_lens;
+  void* o;
+  float* lse;  // may be nullptr
+  float scale;
+  int n_splits;      // context splits per (sequence, key/value head); > 1 needs workspace
+  int64_t chunk;     // context tokens per split (a multiple of 64; the last split takes the rest)
+  float* workspace;  // (B, H, n_splits, D) partial outputs, then (B, H, n_splits) partial lse
+  hipStream_t stream;
+};
+
+hipError_t launch_reshape_and_cache(const CacheArgs& a);
+hipError_t launch_paged_decode(const DecodeArgs& a);
+
+// Context split of the decode kernel for B sequences over Hkv key/value heads
+// and contexts up to max_context tokens.  Every split holds the same number
+// of context tokens (chunk, a multiple of 64), so that workgroups of
+// sequences of very different lengths carry equal work and the dispatcher
+// balances them; chunk is sized for about 1024 (sequence, head, split)
+// workgroups when every context has max_context tokens, at least 256 tokens
+// (64 per wave) and at most 64 splits per sequence.  Shapes only, so that the
+// workspace size is known without a device.
+struct DecodeSplit {
+  int64_t chunk;
+  int n_splits;
+};
+inline DecodeSplit decode_split(int64_t B, int64_t Hkv, int64_t max_context) {
+  const int64_t groups = B * Hkv;
+  if (groups <= 0 || max_context <= 0) return {64, 1};
+  const int64_t want = 1024;
+  int64_t chunk = (groups * max_context + want - 1) / want;
+  if (chunk < 256) chunk = 256;
+  chunk = (chunk + 63) / 64 * 64;
+  int64_t s = (max_context + chunk - 1) / chunk;
+  if (s > 64) {
+    s = 64;
+    chunk = ((max_context + s - 1) / s + 63) / 64 * 64;
+    s = (max_context + chunk - 1) / chunk;
+  }
+  return {chunk, (int)(s < 1 ? 1 : s)};
+}
+
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd_pre(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);

@@ -260,6 +260,63 @@ int fa_bwd_dkdv_varlen(int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t max
                        int num_programs, hipStream_t stream);
 
 /*
+ * Paged KV cache ([Serving-Ascend], sections "ReshapeAndCache" and "GQA Paged
+ * Attention").  One page is one physical block of one key/value head:
+ *   k_cache : (num_blocks, Hkv, D/8, block_size, 8) dtype, the page's keys in
+ *             16-byte chunks of 8 channels, chunk-major: channel d of the
+ *             token at offset o is element [block][head][d/8][o][d%8];
+ *   v_cache : (num_blocks, Hkv, D, block_size) dtype, the page's values
+ *             transposed (one row of block_size values per channel d).
+ * block_size is a multiple of 16 in [16, 1024].
+ *
+ * fa_reshape_and_cache: writes new tokens into the cache.
+ *   key, value   : (num_tokens, Hkv, D) dtype, read;
+ *   slot_mapping : DEVICE int64[num_tokens]; token i goes to block
+ *                  slot / block_size at offset slot % block_size; a negative
+ *                  slot skips the token (as on the page), and so does a slot
+ *                  past the cache (slot >= num_blocks * block_size).  Slots of
+ *                  one call must be distinct (two tokens on one slot leave
+ *                  either one there).
+ *   k_cache, v_cache : written at the tokens' slots only.
+ *
+ * fa_paged_decode: attention of one query token per sequence over its cached
+ * context.
+ *   q            : (B, H, D) dtype; query head h uses key/value head
+ *                  h / (H / Hkv); H / Hkv <= 16;
+ *   block_tables : DEVICE int32 (B, max_blocks_per_seq): token t of sequence
+ *                  b is in physical block block_tables[b][t / block_size] at
+ *                  offset t % block_size;
+ *   context_lens : DEVICE int32[B], tokens of each context (clamped to
+ *                  [0, max_blocks_per_seq * block_size]); every token of the
+ *                  context is visible; the rest of the last block is masked;
+ *   max_context_len : host bound on the context lengths, used only to size
+ *                  the split of long contexts (and the workspace); longer
+ *                  contexts are still processed whole;
+ *   o            : (B, H, D) o_dtype (dtype or FA_DTYPE_F32), written;
+ *   lse          : (B, H) float32 natural-log log-sum-exp of each score row,
+ *                  written, or NULL;
+ *   workspace    : fa_paged_decode_workspace_bytes(B, H, Hkv, D,
+ *                  max_context_len) bytes of device memory (0 bytes: NULL is
+ *                  fine), 16-byte aligned.
+ * A block-table entry outside [0, num_blocks) makes the tokens of that block
+ * take no part (they are not read).  A context of 0 tokens gives O = 0 and
+ * lse = -inf.  Long contexts are split over several workgroups per (sequence,
+ * key/value head) whose partial (O, lse) pairs a second kernel combines.
+ */
+int fa_reshape_and_cache(int64_t num_tokens, int64_t Hkv, int64_t D, int64_t block_size,
+                         int64_t num_blocks, int dtype, const void* key, const void* value,
+                         const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                         hipStream_t stream);
+size_t fa_paged_decode_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t D,
+                                       int64_t max_context_len);
+int fa_paged_decode(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_size,
+                    int64_t num_blocks, int64_t max_blocks_per_seq, int64_t max_context_len,
+                    int dtype, int o_dtype, const void* q, const void* k_cache,
+                    const void* v_cache, const int32_t* block_tables,
+                    const int32_t* context_lens, void* o, float* lse, float scale,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Device facts used for launch sizing, for the current device: compute
  * units, and the persistent grid fa_bwd_dkdv uses for (D, dtype) when
  * num_programs is 0.  Either output pointer may be NULL.

@@ -12,10 +12,11 @@ last block, and lets several query heads share one key/value head.
 
 Readings of what it leaves open (listed in the design doc):
 
-* cache layouts: k_cache is (num_blocks, Hkv, block_size, D), one page of a
-  key/value head being block_size contiguous key rows; v_cache is
-  (num_blocks, Hkv, D, block_size), the page's values stored transposed
-  (one row of block_size values per channel d);
+* cache layouts: k_cache is (num_blocks, Hkv, D/8, block_size, 8), one page
+  of a key/value head holding its keys in chunks of 8 channels, chunk-major
+  (channel d of the token at offset o is at [block, head, d // 8, o, d % 8]);
+  v_cache is (num_blocks, Hkv, D, block_size), the page's values stored
+  transposed (one row of block_size values per channel d);
 * new tokens arrive as key, value (num_tokens, Hkv, D) with an int64
   slot_mapping (num_tokens,); slots of one call are distinct;
 * decode: one query token per sequence, q (B, H, D); block_tables
@@ -45,7 +46,8 @@ def reshape_and_cache(key, value, slot_mapping, k_cache, v_cache):
     """
     k_cache = np.array(k_cache, copy=True)
     v_cache = np.array(v_cache, copy=True)
-    num_blocks, n_kv, block_size, D = k_cache.shape
+    num_blocks, n_kv, n_chunks, block_size, x = k_cache.shape
+    D = n_chunks * x
     slots = np.asarray(slot_mapping, dtype=np.int64)
     if key.shape != (slots.size, n_kv, D) or value.shape != key.shape:
         raise ValueError("key and value must be (num_tokens, Hkv, D) matching the caches")
@@ -56,7 +58,7 @@ def reshape_and_cache(key, value, slot_mapping, k_cache, v_cache):
         if block >= num_blocks:
             raise ValueError(f"slot {slot} lies past the last block")
         for hk in range(n_kv):
-            k_cache[block, hk, offset, :] = key[i, hk, :]
+            k_cache[block, hk, :, offset, :] = key[i, hk, :].reshape(n_chunks, x)
             v_cache[block, hk, :, offset] = value[i, hk, :]
     return k_cache, v_cache
 
@@ -66,14 +68,15 @@ def gather_context(k_cache, v_cache, table_row, context_len, kv_head):
     (context_len, D) K and V, token by token through the block table
     ([Serving-Ascend] "GQA Paged Attention": logical block t // block_size
     maps to a physical block, the token sits at offset t % block_size)."""
-    num_blocks, _, block_size, D = k_cache.shape
+    num_blocks, _, n_chunks, block_size, x = k_cache.shape
+    D = n_chunks * x
     K = np.empty((context_len, D), dtype=k_cache.dtype)
     V = np.empty((context_len, D), dtype=v_cache.dtype)
     for t in range(context_len):
         block = int(table_row[t // block_size])
         if not 0 <= block < num_blocks:
             raise ValueError(f"block table entry {block} out of range")
-        K[t] = k_cache[block, kv_head, t % block_size, :]
+        K[t] = k_cache[block, kv_head, :, t % block_size, :].reshape(D)
         V[t] = v_cache[block, kv_head, :, t % block_size]
     return K, V
 

@@ -18,7 +18,7 @@ def _scatter_pages(rng, K, V, num_blocks, block_size):
     plain indexing.  Returns caches and block tables; unused cache entries
     hold NaN so that any stray read shows."""
     n_kv, D = K[0].shape[0], K[0].shape[2]
-    kc = np.full((num_blocks, n_kv, block_size, D), np.nan)
+    kc = np.full((num_blocks, n_kv, D // 8, block_size, 8), np.nan)
     vc = np.full((num_blocks, n_kv, D, block_size), np.nan)
     need = [-(-k.shape[1] // block_size) for k in K]
     perm = rng.permutation(num_blocks)[: sum(need)]
@@ -29,7 +29,7 @@ def _scatter_pages(rng, K, V, num_blocks, block_size):
             blk = int(perm[i]); i += 1
             tables[b, p] = blk
             t0, t1 = p * block_size, min((p + 1) * block_size, k.shape[1])
-            kc[blk, :, : t1 - t0, :] = k[:, t0:t1, :]
+            kc[blk, :, :, : t1 - t0, :] = k[:, t0:t1, :].reshape(n_kv, t1 - t0, D // 8, 8).transpose(0, 2, 1, 3)
             vc[blk, :, :, : t1 - t0] = np.swapaxes(v[:, t0:t1, :], 1, 2)
     return kc, vc, tables
 
@@ -84,14 +84,14 @@ def test_paged_decode_invariances_and_closed_forms():
     # in-block offset (t+1) % bs, a plausible slip, reads a NaN or another token
     Kg, Vg = gather_context(kc, vc, tables[1], 30, 1)
     assert np.array_equal(Kg, K[1][1]) and np.array_equal(Vg, V[1][1])
-    slipped = np.array([kc[tables[1][t // bs], 1, (t + 1) % bs] for t in range(30)])
+    slipped = np.array([kc[tables[1][t // bs], 1, :, (t + 1) % bs, :].reshape(D) for t in range(30)])
     assert not np.allclose(slipped[:29], K[1][1][:29])
 
 
 def test_reshape_and_cache_round_trip_and_skips():
     rng = np.random.default_rng(89)
     nb, Hkv, bs, D, T = 6, 2, 16, 8, 20
-    kc0 = rng.standard_normal((nb, Hkv, bs, D)).astype(np.float16)
+    kc0 = rng.standard_normal((nb, Hkv, D // 8, bs, 8)).astype(np.float16)
     vc0 = rng.standard_normal((nb, Hkv, D, bs)).astype(np.float16)
     key = rng.standard_normal((T, Hkv, D)).astype(np.float16)
     val = rng.standard_normal((T, Hkv, D)).astype(np.float16)
@@ -104,14 +104,14 @@ def test_reshape_and_cache_round_trip_and_skips():
         if s < 0:
             continue
         b, o = s // bs, s % bs
-        assert np.array_equal(kc[b, :, o, :], key[i]) and np.array_equal(vc[b, :, :, o], val[i])
-        touched_k[b, :, o, :] = True
+        assert np.array_equal(kc[b, :, :, o, :].reshape(Hkv, D), key[i]) and np.array_equal(vc[b, :, :, o], val[i])
+        touched_k[b, :, :, o, :] = True
         touched_v[b, :, :, o] = True
     assert np.array_equal(kc[~touched_k], kc0[~touched_k]) and np.array_equal(vc[~touched_v], vc0[~touched_v])
     assert touched_k.sum() == (T - 2) * Hkv * D
     # a plausible slip: block and offset swapped
     b, o = slots[0] % bs, slots[0] // bs
     if b < nb and o < bs and (b, o) != (slots[0] // bs, slots[0] % bs):
-        assert not np.array_equal(kc[b, :, o, :], key[0])
+        assert not np.array_equal(kc[b, :, :, o, :].reshape(Hkv, D), key[0])
     with pytest.raises(ValueError):
         reshape_and_cache(key, val, np.full(T, nb * bs, dtype=np.int64), kc0, vc0)

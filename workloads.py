@@ -156,3 +156,82 @@ def random_inputs(shape, dtype: str, seed: int, qk_gain: float = 1.0, kv_heads: 
     """Seeded (q, k, v, do) torch CPU tensors of an arbitrary shape, same recipe."""
     w = Workload("adhoc", seed, *shape, dtype, False, qk_gain, kv_heads)
     return make_inputs(w)
+
+
+# ---------------------------------------------------------------- paged decode
+# Decode over a paged KV cache: B sequences, one query token each, contexts of
+# drawn lengths stored in pages (physical blocks) of block_size tokens per
+# key/value head.  Recipe: a generator default_rng(seed) draws, in order, the
+# context lengths (uniform integers in [lo, hi]), the physical block of every
+# page (a random permutation of the blocks, taken sequence by sequence), then
+# q (B, H, D), k_cache (num_blocks, Hkv, D/8, block_size, 8) and v_cache
+# (num_blocks, Hkv, D, block_size) as integers uniform in [-32, 32) divided by
+# 16 (values in [-2, 2) on a 1/16 grid, exact in fp16 and bf16, so that a
+# gigabyte-scale cache is drawn in seconds).  Every cache element is random
+# (also slots past a context), and num_blocks has a spare block per 8 in use
+# that no sequence uses.
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    seed: int
+    B: int
+    H: int
+    Hkv: int
+    D: int
+    block_size: int
+    lo: int            # shortest context
+    hi: int            # longest context
+    dtype: str
+
+    @property
+    def scale(self) -> float:
+        return f32_scale(self.D)
+
+    def lengths(self):
+        rng = np.random.default_rng(self.seed)
+        return rng.integers(self.lo, self.hi + 1, size=self.B)
+
+    def layout(self):
+        """(context_lens int32 (B,), block_tables int32 (B, max_blocks), num_blocks)."""
+        rng = np.random.default_rng(self.seed)
+        lens = rng.integers(self.lo, self.hi + 1, size=self.B)
+        pages = -(-lens // self.block_size)
+        used = int(pages.sum())
+        num_blocks = used + used // 8 + 1
+        perm = rng.permutation(num_blocks)
+        max_blocks = int(pages.max()) if self.B else 0
+        tables = np.full((self.B, max(max_blocks, 1)), -1, dtype=np.int32)
+        i = 0
+        for b in range(self.B):
+            tables[b, : pages[b]] = perm[i:i + pages[b]]
+            i += int(pages[b])
+        return lens.astype(np.int32), tables, num_blocks
+
+
+DECODE_WORKLOADS = {
+    # 64 sequences of 512..16000 tokens (about 8K on average), 32 query heads over 8
+    # key/value heads, D = 128, pages of 16 tokens
+    "decode_gqa_bf16": DecodeWorkload("decode_gqa_bf16", 11, 64, 32, 8, 128, 16, 512, 16000, "bf16"),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload):
+    """torch CPU tensors (q, k_cache, v_cache, block_tables, context_lens) of a decode workload."""
+    import torch
+
+    lens, tables, num_blocks = w.layout()
+    rng = np.random.default_rng(w.seed)
+    rng.integers(w.lo, w.hi + 1, size=w.B)  # the lengths drawn by layout()
+    rng.permutation(num_blocks)             # the page placement drawn by layout()
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+
+    def draw(shape):
+        x = torch.from_numpy(rng.integers(-32, 32, size=shape, dtype=np.int8))
+        return x.to(tdt) * 0.0625  # exact: a power-of-two scale of small integers
+
+    q = draw((w.B, w.H, w.D))
+    kc = draw((num_blocks, w.Hkv, w.D // 8, w.block_size, 8))
+    vc = draw((num_blocks, w.Hkv, w.D, w.block_size))
+    return q, kc, vc, torch.from_numpy(tables), torch.from_numpy(lens)
