@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "fa_bwd_pre": ("fa_bwd.hip", "fa_device.h", "fa_kernels.h"),
     "fa_bwd_dkdv": ("fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_schedule.h"),
     "fa_bwd_dq": ("fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_schedule.h"),
+    "fa_paged_decode": ("fa_paged.hip", "fa_device.h", "fa_kernels.h"),
 }
 
 
@@ -476,6 +477,16 @@ def run_decode(args):
         if st != 0:
             raise fa.FAError(st, name, fa.last_error())
 
+    if args.calib_copy_mib > 0:
+        # A plain device copy of known size, for scaling HBM counters.
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
@@ -526,7 +537,7 @@ def run_decode(args):
         "breakdown": {"reshape_and_cache_ms": round(cache_ms, 4), "paged_decode_ms": round(dec_ms, 4),
                       "splits": splits},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": stored_traffic("fa_paged_decode", w.name),
                      "kernel": "fa_paged_decode (decode kernel and, with splits, its combine kernel)",
                      "algorithmic": {"amount": dec_bytes, "unit": "byte", "per_launch": True}},
         "cpu_baseline": None,
