@@ -11,7 +11,9 @@ optimisation with Triton-Ascend", BiumBiu, 2026-08-30), cited below as
 [FA-Ascend] with the section it comes from; the grouped key/value heads follow
 the page "从算子到 Serving：昇腾推理评测链路实践" (BiumBiu, 2026-04-30), cited
 as [Serving-Ascend], as do the variable-length batches and the paged KV cache
-(``paged.py``: cache writes and decode attention over pages).
+(``paged.py``: cache writes and decode attention over pages) and the
+query-aware page selection with attention over the selected pages
+(``quest.py``).
 
 Pinning: every function here is pinned by tests marked ``not gpu`` to facts
 other than itself (finite differences, closed forms, invariants, a library
@@ -30,3 +32,4 @@ from .attention import (  # noqa: F401
     attention_backward_varlen,
 )
 from .paged import gather_context, paged_decode, reshape_and_cache  # noqa: F401
+from .quest import quest_page_minmax, quest_scores, quest_select, quest_sparse_decode  # noqa: F401
