@@ -21,6 +21,7 @@ from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32, FAError, check, la
                    status_name)
 
 __all__ = ["forward", "backward", "forward_varlen", "backward_varlen", "reshape_and_cache", "paged_decode",
+           "quest_page_minmax", "quest_select", "paged_decode_sparse",
            "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_dq_and_stats", "workspace_bytes",
            "device_info", "dkdv_schedule", "fwd_tile_pairs", "FAError", "lib"]
 
@@ -283,6 +284,79 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_le
                                    _ptr(context_lens), _ptr(o), _ptr(lse), _scale(scale, D), _ptr(ws), nbytes,
                                    _stream(q))
     check(st, "fa_paged_decode")
+    return o, lse
+
+
+def _check_paged(q, k_cache, v_cache, block_tables, context_lens):
+    torch = _torch()
+    B, H, D = q.shape
+    if k_cache.dim() != 5:
+        raise ValueError("k_cache must be (num_blocks, Hkv, D/8, block_size, 8)")
+    nb, Hkv, _, bs, _ = k_cache.shape
+    if k_cache.shape != (nb, Hkv, D // 8, bs, 8) or (v_cache is not None and v_cache.shape != (nb, Hkv, D, bs)):
+        raise ValueError("caches must be (num_blocks, Hkv, D/8, block_size, 8) and (num_blocks, Hkv, D, block_size)")
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        if t is not None and (not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device):
+            raise ValueError(f"{n} must be a contiguous GPU tensor of q's dtype and device")
+    for t, n in ((block_tables, "block_tables"), (context_lens, "context_lens")):
+        if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous int32 GPU tensor")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be (B, max_blocks) and context_lens (B,)")
+    return B, H, Hkv, D, bs, nb, block_tables.shape[1]
+
+
+def quest_page_minmax(k_cache, block_tables, context_lens):
+    """Page key minimum / maximum (num_blocks, Hkv, 2, D) over each context's valid tokens."""
+    torch = _torch()
+    nb, Hkv, nc, bs, x = k_cache.shape
+    D = nc * x
+    B = block_tables.shape[0]
+    q_dummy = torch.empty((B, Hkv, D), dtype=k_cache.dtype, device=k_cache.device)
+    _check_paged(q_dummy, k_cache, None, block_tables, context_lens)
+    with torch.cuda.device(k_cache.device):
+        kmeta = torch.zeros((nb, Hkv, 2, D), dtype=k_cache.dtype, device=k_cache.device)
+        st = lib().fa_quest_page_minmax(B, Hkv, D, bs, nb, block_tables.shape[1], _dtype_code(k_cache), _ptr(k_cache),
+                                        _ptr(block_tables), _ptr(context_lens), _ptr(kmeta), _stream(k_cache))
+    check(st, "fa_quest_page_minmax")
+    return kmeta
+
+
+def quest_select(q, kmeta, k_cache, block_tables, context_lens, topk):
+    """Kept pages (B, Hkv, topk) int32 (ascending; -1 past the count) and their count (B, Hkv)."""
+    torch = _torch()
+    B, H, Hkv, D, bs, nb, mxb = _check_paged(q, k_cache, None, block_tables, context_lens)
+    if kmeta.shape != (nb, Hkv, 2, D) or kmeta.dtype != q.dtype or not kmeta.is_contiguous():
+        raise ValueError("kmeta must be the (num_blocks, Hkv, 2, D) output of quest_page_minmax")
+    with torch.cuda.device(q.device):
+        sel = torch.full((B, Hkv, topk), -1, dtype=torch.int32, device=q.device)
+        nsel = torch.empty((B, Hkv), dtype=torch.int32, device=q.device)
+        st = lib().fa_quest_select(B, H, Hkv, D, bs, nb, mxb, topk, _dtype_code(q), _ptr(q), _ptr(kmeta),
+                                   _ptr(block_tables), _ptr(context_lens), _ptr(sel), _ptr(nsel), _stream(q))
+    check(st, "fa_quest_select")
+    return sel, nsel
+
+
+def paged_decode_sparse(q, k_cache, v_cache, block_tables, context_lens, selected, n_selected, scale=None,
+                        out_dtype=None):
+    """Decode attention over the tokens of the kept pages: (O (B, H, D), lse (B, H))."""
+    torch = _torch()
+    B, H, Hkv, D, bs, nb, mxb = _check_paged(q, k_cache, v_cache, block_tables, context_lens)
+    topk = selected.shape[2]
+    if selected.shape != (B, Hkv, topk) or n_selected.shape != (B, Hkv) or selected.dtype != torch.int32 \
+            or n_selected.dtype != torch.int32:
+        raise ValueError("selected must be int32 (B, Hkv, topk) and n_selected int32 (B, Hkv)")
+    odt = q.dtype if out_dtype is None else out_dtype
+    with torch.cuda.device(q.device):
+        o = torch.empty((B, H, D), dtype=odt, device=q.device)
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+        nbytes = lib().fa_paged_decode_workspace_bytes(B, H, Hkv, D, topk * bs)
+        ws = torch.empty((max(1, nbytes // 4),), dtype=torch.float32, device=q.device)
+        st = lib().fa_paged_decode_sparse(B, H, Hkv, D, bs, nb, mxb, topk, _dtype_code(q), _dtype_code(o), _ptr(q),
+                                          _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+                                          _ptr(selected), _ptr(n_selected), _ptr(o), _ptr(lse), _scale(scale, D),
+                                          _ptr(ws), nbytes, _stream(q))
+    check(st, "fa_paged_decode_sparse")
     return o, lse
 
 

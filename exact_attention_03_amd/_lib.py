@@ -54,6 +54,11 @@ SIGNATURES = {
     "fa_paged_decode_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "fa_paged_decode": (_int, [_i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp,
                                _vp, _vp, _f32, _vp, _sz, _vp]),
+    "fa_quest_page_minmax": (_int, [_i64, _i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp]),
+    "fa_quest_select": (_int, [_i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp,
+                               _vp]),
+    "fa_paged_decode_sparse": (_int, [_i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _vp, _f32, _vp, _sz, _vp]),
     "fa_device_info": (_int, [_i64, _int, _intp, _intp]),
     "fa_dkdv_schedule": (_int, [_i64, _i64, _i64, _i64, _int, _int, _i64p, _i64p, _i64p]),
     "fa_fwd_tile_pairs": (_int, [_i64, _i64, _int, _i64p, _i64p]),

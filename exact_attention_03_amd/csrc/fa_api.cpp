@@ -506,11 +506,18 @@ size_t fa_paged_decode_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_
   return s > 1 ? (size_t)(B * H * s * (D + 1)) * sizeof(float) : 0;
 }
 
-int fa_paged_decode(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_size, int64_t num_blocks,
-                    int64_t max_blocks_per_seq, int64_t max_context_len, int dtype, int o_dtype, const void* q,
-                    const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                    const int32_t* context_lens, void* o, float* lse, float scale, void* workspace,
-                    size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Paged decode over whole contexts (selected == nullptr) or over the kept
+// pages of each (sequence, key/value head).
+int paged_decode_impl(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_size, int64_t num_blocks,
+                      int64_t max_blocks_per_seq, int64_t max_context_len, int dtype, int o_dtype, const void* q,
+                      const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, void* o, float* lse, float scale, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream, const int32_t* selected,
+                      const int32_t* n_selected, int64_t topk) {
   g_last_error.clear();
   if (B < 0 || H < 0 || Hkv < 0 || num_blocks < 0 || block_size < 0 || max_blocks_per_seq < 0 ||
       max_context_len < 0)
@@ -553,9 +560,103 @@ int fa_paged_decode(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_
   a.max_blocks = max_blocks_per_seq; a.dtype = dtype; a.o_dtype = o_dtype; a.q = q; a.k_cache = k_cache;
   a.v_cache = v_cache; a.block_tables = block_tables; a.context_lens = context_lens; a.o = o; a.lse = lse;
   a.scale = scale; a.n_splits = split.n_splits; a.chunk = split.chunk; a.workspace = static_cast<float*>(workspace);
-  a.stream = stream;
+  a.stream = stream; a.selected = selected; a.n_selected = n_selected; a.topk = topk;
   return finish(fa::launch_paged_decode(a), stream, "fa_paged_decode launch");
 }
+
+}  // namespace
+
+extern "C" {
+
+int fa_paged_decode(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_size, int64_t num_blocks,
+                    int64_t max_blocks_per_seq, int64_t max_context_len, int dtype, int o_dtype, const void* q,
+                    const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                    const int32_t* context_lens, void* o, float* lse, float scale, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  return paged_decode_impl(B, H, Hkv, D, block_size, num_blocks, max_blocks_per_seq, max_context_len, dtype,
+                           o_dtype, q, k_cache, v_cache, block_tables, context_lens, o, lse, scale, workspace,
+                           workspace_bytes, stream, nullptr, nullptr, 0);
+}
+
+// The common checks of the page-selection calls.
+static int check_quest(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_size, int64_t num_blocks,
+                       int64_t max_blocks_per_seq, int64_t topk, int dtype) {
+  if (B < 0 || H < 0 || Hkv < 0 || num_blocks < 0 || block_size < 0 || max_blocks_per_seq < 0 || topk < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "negative size");
+  if (D != 64 && D != 128 && D != 256)
+    return fail(FA_ERR_UNSUPPORTED, "head dim D=%lld not supported (64, 128 or 256)", (long long)D);
+  if (block_size < 16 || block_size > 1024 || block_size % 16 != 0)
+    return fail(FA_ERR_UNSUPPORTED, "block_size=%lld must be a multiple of 16 in [16, 1024]", (long long)block_size);
+  FA_TRY(check_dtypes(dtype, dtype, false));
+  if (H > 0 && (Hkv == 0 || H % Hkv != 0))
+    return fail(FA_ERR_INVALID_ARGUMENT, "H=%lld query heads must be a whole multiple of Hkv=%lld", (long long)H,
+                (long long)Hkv);
+  if (H > 0 && H / Hkv > 16)
+    return fail(FA_ERR_UNSUPPORTED, "at most 16 query heads per key/value head (H/Hkv=%lld)", (long long)(H / Hkv));
+  if (max_blocks_per_seq > fa::kQuestMaxPagesHost)
+    return fail(FA_ERR_UNSUPPORTED, "at most %d pages per context (max_blocks_per_seq=%lld)", fa::kQuestMaxPagesHost,
+                (long long)max_blocks_per_seq);
+  if (topk > kMaxI32) return fail(FA_ERR_UNSUPPORTED, "topk too large");
+  if (B * Hkv > kMaxI32 || num_blocks > kMaxI32) return fail(FA_ERR_UNSUPPORTED, "problem too large");
+  return FA_OK;
+}
+
+int fa_quest_page_minmax(int64_t B, int64_t Hkv, int64_t D, int64_t block_size, int64_t num_blocks,
+                         int64_t max_blocks_per_seq, int dtype, const void* k_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, void* kmeta, hipStream_t stream) {
+  g_last_error.clear();
+  FA_TRY(check_quest(B, Hkv, Hkv, D, block_size, num_blocks, max_blocks_per_seq, 0, dtype));
+  if (B == 0 || Hkv == 0 || max_blocks_per_seq == 0 || num_blocks == 0) return FA_OK;
+  FA_TRY(check_ptr(k_cache, "k_cache"));
+  FA_TRY(check_ptr(kmeta, "kmeta"));
+  if (block_tables == nullptr || context_lens == nullptr ||
+      reinterpret_cast<uintptr_t>(block_tables) % 4 != 0 || reinterpret_cast<uintptr_t>(context_lens) % 4 != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "block_tables / context_lens NULL or not 4-byte aligned");
+  fa::QuestArgs a{};
+  a.B = B; a.Hkv = Hkv; a.H = Hkv; a.D = D; a.block_size = block_size; a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq; a.dtype = dtype; a.k_cache = k_cache; a.block_tables = block_tables;
+  a.context_lens = context_lens; a.kmeta = kmeta; a.stream = stream;
+  return finish(fa::launch_quest_minmax(a), stream, "fa_quest_page_minmax launch");
+}
+
+int fa_quest_select(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_size, int64_t num_blocks,
+                    int64_t max_blocks_per_seq, int64_t topk, int dtype, const void* q, const void* kmeta,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t* selected,
+                    int32_t* n_selected, hipStream_t stream) {
+  g_last_error.clear();
+  FA_TRY(check_quest(B, H, Hkv, D, block_size, num_blocks, max_blocks_per_seq, topk, dtype));
+  if (B == 0 || H == 0) return FA_OK;
+  FA_TRY(check_ptr(q, "q"));
+  FA_TRY(check_ptr(kmeta, "kmeta"));
+  if (block_tables == nullptr || context_lens == nullptr || selected == nullptr || n_selected == nullptr ||
+      reinterpret_cast<uintptr_t>(block_tables) % 4 != 0 || reinterpret_cast<uintptr_t>(context_lens) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(selected) % 4 != 0 || reinterpret_cast<uintptr_t>(n_selected) % 4 != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "an index array is NULL or not 4-byte aligned");
+  fa::QuestArgs a{};
+  a.B = B; a.H = H; a.Hkv = Hkv; a.D = D; a.block_size = block_size; a.num_blocks = num_blocks;
+  a.max_blocks = max_blocks_per_seq; a.topk = topk; a.dtype = dtype; a.q = q; a.block_tables = block_tables;
+  a.context_lens = context_lens; a.kmeta = const_cast<void*>(kmeta); a.selected = selected;
+  a.n_selected = n_selected; a.stream = stream;
+  return finish(fa::launch_quest_select(a), stream, "fa_quest_select launch");
+}
+
+int fa_paged_decode_sparse(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_size, int64_t num_blocks,
+                           int64_t max_blocks_per_seq, int64_t topk, int dtype, int o_dtype, const void* q,
+                           const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, const int32_t* selected, const int32_t* n_selected,
+                           void* o, float* lse, float scale, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  g_last_error.clear();
+  if (topk < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative topk");
+  if (B > 0 && H > 0 && (selected == nullptr || n_selected == nullptr ||
+                         reinterpret_cast<uintptr_t>(selected) % 4 != 0 ||
+                         reinterpret_cast<uintptr_t>(n_selected) % 4 != 0))
+    return fail(FA_ERR_INVALID_ARGUMENT, "selected / n_selected NULL or not 4-byte aligned");
+  return paged_decode_impl(B, H, Hkv, D, block_size, num_blocks, max_blocks_per_seq, topk * block_size, dtype,
+                           o_dtype, q, k_cache, v_cache, block_tables, context_lens, o, lse, scale, workspace,
+                           workspace_bytes, stream, selected, n_selected, topk);
+}
+
 
 int fa_device_info(int64_t D, int dtype, int* compute_units, int* dkdv_programs) {
   g_last_error.clear();

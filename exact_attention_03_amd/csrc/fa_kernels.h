@@ -70,8 +70,31 @@ struct DecodeArgs {
   int n_splits;      // context splits per (sequence, key/value head); > 1 needs workspace
   int64_t chunk;     // context tokens per split (a multiple of 64; the last split takes the rest)
   float* workspace;  // (B, H, n_splits, D) partial outputs, then (B, H, n_splits) partial lse
+  // Sparse decode: the kept logical pages of each (sequence, key/value head),
+  // (B, Hkv, topk) ascending, and their count (B, Hkv); nullptr for dense.
+  const int* selected = nullptr;
+  const int* n_selected = nullptr;
+  int64_t topk = 0;
   hipStream_t stream;
 };
+
+// Query-aware page selection over a paged cache: page key min / max, then
+// per (sequence, key/value head) the topk best pages.
+struct QuestArgs {
+  int64_t B, H, Hkv, D, block_size, num_blocks, max_blocks, topk;
+  int dtype;
+  const void* q;
+  const void* k_cache;
+  const int* block_tables;
+  const int* context_lens;
+  void* kmeta;     // (num_blocks, Hkv, 2, D) dtype
+  int* selected;   // (B, Hkv, topk) int32
+  int* n_selected; // (B, Hkv) int32
+  hipStream_t stream;
+};
+hipError_t launch_quest_minmax(const QuestArgs& a);
+hipError_t launch_quest_select(const QuestArgs& a);
+constexpr int kQuestMaxPagesHost = 4096;  // pages per context the selection handles
 
 hipError_t launch_reshape_and_cache(const CacheArgs& a);
 hipError_t launch_paged_decode(const DecodeArgs& a);

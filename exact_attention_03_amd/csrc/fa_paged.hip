@@ -88,7 +88,8 @@ void fa_paged_decode_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
     const int* __restrict__ block_tables, const int* __restrict__ context_lens, void* __restrict__ o,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse, int H, int Hkv, int G, int bs,
-    int64_t num_blocks, int max_blocks, int n_splits, int64_t chunk, float c2) {
+    int64_t num_blocks, int max_blocks, int n_splits, int64_t chunk, float c2, const int* __restrict__ sel,
+    const int* __restrict__ nsel, int topk) {
   using C = DecodeTile<D>;
   __shared__ float sm_m[C::NW][16];
   __shared__ float sm_l[C::NW][16];
@@ -105,8 +106,25 @@ void fa_paged_decode_kernel(
   const int hk = bh % Hkv;
   const int b = bh / Hkv;
   const int64_t max_tokens = (int64_t)max_blocks * bs;
-  int64_t n_ctx = context_lens[b];
-  n_ctx = n_ctx < 0 ? 0 : (n_ctx > max_tokens ? max_tokens : n_ctx);
+  const int64_t n_real = context_lens[b] < 0 ? 0 : (context_lens[b] > max_tokens ? max_tokens : context_lens[b]);
+  int64_t n_ctx = n_real;  // tokens this (sequence, head) attends to, in order
+  // Sparse decode: the tokens of the kept pages, back to back (a virtual
+  // context); the last kept page is cut at the context's end when it is the
+  // context's last page.
+  const int* selrow = nullptr;
+  int ns = 0;
+  if (sel != nullptr) {
+    const int64_t row = (int64_t)b * Hkv + hk;
+    ns = nsel[row] < 0 ? 0 : (nsel[row] > topk ? topk : nsel[row]);
+    selrow = sel + row * topk;
+    const int64_t n_pages = (n_real + bs - 1) / bs;
+    if (ns == 0) {
+      n_ctx = 0;
+    } else {
+      const int64_t last = selrow[ns - 1];
+      n_ctx = (int64_t)(ns - 1) * bs + (last == n_pages - 1 ? n_real - last * bs : bs);
+    }
+  }
   // This split's tokens: chunk tokens (a whole number of 64-token steps, one
   // 16-token tile per wave per step) from s * chunk on; the last split takes
   // the rest of a context longer than the split was sized for.
@@ -144,8 +162,10 @@ void fa_paged_decode_kernel(
   const int64_t w_first = t_begin + 16 * w;  // this wave's first token
   int vblk = -1;
   auto load_blocks = [&](int64_t j0) {
-    const int64_t page = (w_first + 64 * (j0 + lane)) / bs;
-    vblk = page < max_blocks ? table[page] : -1;
+    int64_t page = (w_first + 64 * (j0 + lane)) / bs;  // position in the (virtual) context
+    if (selrow != nullptr) page = page < ns ? selrow[page] : -1;  // kept page -> logical page
+    // a logical page outside the context takes no part
+    vblk = (page >= 0 && page < max_blocks && page * bs < n_real) ? table[page] : -1;
   };
   auto load_tile = [&](int64_t j, Tile& x) -> bool {
     const int64_t t0 = w_first + 64 * j;
@@ -315,7 +335,8 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   hipLaunchKernelGGL((fa_paged_decode_kernel<D, T, OT>), dim3((unsigned)grid), dim3(256), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_tables,
                      a.context_lens, a.o, a.lse, part_o, part_lse, (int)a.H, (int)a.Hkv, G, (int)a.block_size,
-                     a.num_blocks, (int)a.max_blocks, a.n_splits, a.chunk, a.scale * kLog2e);
+                     a.num_blocks, (int)a.max_blocks, a.n_splits, a.chunk, a.scale * kLog2e, a.selected,
+                     a.n_selected, (int)a.topk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits == 1) return e;
   hipLaunchKernelGGL((fa_paged_decode_combine_kernel<D, T, OT>), dim3((unsigned)(a.B * a.H)), dim3(D), 0, a.stream,

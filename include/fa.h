@@ -317,6 +317,51 @@ int fa_paged_decode(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Query-aware page selection and attention over the kept pages
+ * ([Serving-Ascend], section "Quest Sparse Attention": score the pages of a
+ * long context cheaply, keep the Top-K, run exact attention over their
+ * tokens only).  The scoring rule is the published Quest one: a page keeps
+ * the channel-wise minimum and maximum of its valid keys, and its score for a
+ * query q is sum_d max(q_d * min_d, q_d * max_d), an upper bound of q . k
+ * over the page.  A key/value head keeps one set of pages for its G query
+ * heads (G <= 16), scored by the sum of their scores; ties go to the lower
+ * page; kept pages are listed in ascending order.  Caches, block tables and
+ * context lengths as for fa_paged_decode; contexts of at most 4096 pages
+ * (max_blocks_per_seq <= 4096).
+ *
+ * fa_quest_page_minmax: kmeta (num_blocks, Hkv, 2, D) dtype, written for the
+ *   physical blocks of every context: [.., 0, :] = minimum, [.., 1, :] =
+ *   maximum over the page's tokens inside the context (exact).  A physical
+ *   block shared by two contexts gets the metadata of either.
+ * fa_quest_select: selected (B, Hkv, topk) int32, n_selected (B, Hkv) int32,
+ *   written: the kept logical pages of each (sequence, key/value head), min(topk,
+ *   pages of the context) of them, ascending; entries past n_selected are
+ *   left unwritten.
+ * fa_paged_decode_sparse: fa_paged_decode over the tokens of the kept pages
+ *   (selected / n_selected as written by fa_quest_select, or any ascending
+ *   lists of logical pages); the last page of a context is cut at the
+ *   context's end.  workspace: fa_paged_decode_workspace_bytes(B, H, Hkv, D,
+ *   topk * block_size) bytes.  Pages outside the context, and counts outside
+ *   [0, topk], are clamped or skipped, never read out of bounds.
+ */
+int fa_quest_page_minmax(int64_t B, int64_t Hkv, int64_t D, int64_t block_size,
+                         int64_t num_blocks, int64_t max_blocks_per_seq, int dtype,
+                         const void* k_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, void* kmeta, hipStream_t stream);
+int fa_quest_select(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_size,
+                    int64_t num_blocks, int64_t max_blocks_per_seq, int64_t topk, int dtype,
+                    const void* q, const void* kmeta, const int32_t* block_tables,
+                    const int32_t* context_lens, int32_t* selected, int32_t* n_selected,
+                    hipStream_t stream);
+int fa_paged_decode_sparse(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_size,
+                           int64_t num_blocks, int64_t max_blocks_per_seq, int64_t topk,
+                           int dtype, int o_dtype, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, const int32_t* selected,
+                           const int32_t* n_selected, void* o, float* lse, float scale,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Device facts used for launch sizing, for the current device: compute
  * units, and the persistent grid fa_bwd_dkdv uses for (D, dtype) when
  * num_programs is 0.  Either output pointer may be NULL.
