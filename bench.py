@@ -392,8 +392,21 @@ def decode_bytes(w, lens) -> float:
 def _oracle_decode(args):
     import oracle
 
-    q, kc, vc, tables, lens, scale = args
-    oracle.paged_decode(q, kc, vc, tables, lens, scale)
+    q, kc, vc, tables, lens, scale, topk = args
+    if not topk:
+        oracle.paged_decode(q, kc, vc, tables, lens, scale)
+        return len(lens)
+    # query-aware: page min / max, scores, Top-K, attention over the kept pages
+    n_kv = kc.shape[1]
+    G = q.shape[1] // n_kv
+    selected = []
+    for b in range(len(lens)):
+        row = []
+        for hk in range(n_kv):
+            mn, mx = oracle.quest_page_minmax(kc, tables[b], int(lens[b]), hk)
+            row.append(oracle.quest_select(oracle.quest_scores(q[b, hk * G:(hk + 1) * G], mn, mx), topk))
+        selected.append(row)
+    oracle.quest_sparse_decode(q, kc, vc, tables, lens, selected, scale)
     return len(lens)
 
 
@@ -418,7 +431,7 @@ def decode_cpu_baseline(w, cpu, n_seq: int, workers: int):
         remap = {b: i for i, b in enumerate(used)}
         t2 = np.vectorize(lambda x: remap.get(int(x), -1))(t).astype(np.int32)
         jobs.append((q[c].float().numpy(), kc[used].float().numpy(), vc[used].float().numpy(), t2,
-                     lens[c].numpy(), w.scale))
+                     lens[c].numpy(), w.scale, w.topk))
     saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
     for k in saved:
         os.environ[k] = "1"
@@ -434,12 +447,131 @@ def decode_cpu_baseline(w, cpu, n_seq: int, workers: int):
             else:
                 os.environ[k] = v
     sub = lens[:done].numpy()
-    nbytes = decode_bytes(w, sub) * 1.0
+    nbytes = sum(quest_bytes(w, sub)) if w.topk else decode_bytes(w, sub)
+    what = ("query-aware oracle (page min / max, scores, Top-K, attention over the kept pages)" if w.topk
+            else "paged-decode oracle (token-by-token gather through the block table, plain softmax)")
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": len(jobs), "kind": "oracle",
-            "sample": (f"fp64 numpy paged-decode oracle (token-by-token gather through the block table, plain "
-                       f"softmax) on {done} of {w.B} sequences ({int(sub.sum())} context tokens) of the same "
-                       f"seeded workload, {len(jobs)} processes x 1 BLAS thread, wall {dt:.2f} s (process start "
-                       f"included); bytes counted as for the GPU")}
+            "sample": (f"fp64 numpy {what} on {done} of {w.B} sequences ({int(sub.sum())} context tokens) of the "
+                       f"same seeded workload, {len(jobs)} processes x 1 BLAS thread, wall {dt:.2f} s (process "
+                       f"start included); bytes counted as for the GPU")}
+
+
+def quest_bytes(w, lens):
+    """Algorithmic HBM bytes of one query-aware step: the selection reads q,
+    the block-table entries and the min / max of every page of each context
+    and writes the kept page lists; the sparse decode reads the kept pages'
+    valid K and V tokens, q, the lists and the table entries of the kept pages,
+    and writes O (16-bit) and lse.  Returns (selection bytes, decode bytes)."""
+    import numpy as np
+
+    lens = np.asarray(lens, dtype=np.int64)
+    e = 2
+    pages = -(-lens // w.block_size)
+    sel = (float(pages.sum()) * w.Hkv * 2 * w.D * e + float(pages.sum()) * 4 + w.B * w.H * w.D * e
+           + w.B * w.Hkv * (w.topk + 1) * 4)
+    kept_tokens = 0.0
+    for n, p in zip(lens, pages):
+        k = min(int(p), w.topk)
+        # the kept pages are full except possibly the context's last page
+        kept_tokens += k * w.block_size - (w.block_size * p - n if k == p else 0)
+    dec = (kept_tokens * w.Hkv * w.D * 2 * e + w.B * w.H * w.D * e * 2 + w.B * w.H * 4
+           + w.B * w.Hkv * (w.topk + 1) * 4 + float(np.minimum(pages, w.topk).sum()) * w.Hkv * 4)
+    return sel, dec
+
+
+def run_quest(args):
+    """One step = fa_quest_select (scores of every page, Top-K) + fa_paged_decode_sparse
+    over the kept pages.  The page min / max are computed once before timing (a
+    serving engine updates them as pages fill)."""
+    import numpy as np
+    import torch
+
+    import exact_attention_03_amd as fa
+
+    w = workloads.DECODE_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cpu = workloads.make_decode_inputs(w)
+    q, kc, vc, tables, lens = (t.to(dev) for t in cpu)
+    lens_np = cpu[4].numpy().astype(np.int64)
+    kmeta = fa.quest_page_minmax(kc, tables, lens)
+    sel = torch.empty((w.B, w.Hkv, w.topk), dtype=torch.int32, device=dev)
+    nsel = torch.empty((w.B, w.Hkv), dtype=torch.int32, device=dev)
+    o = torch.empty((w.B, w.H, w.D), dtype=q.dtype, device=dev)
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+    L = fa.lib()
+    code = fa._dtype_code(q)
+    nb, mxb = kc.shape[0], tables.shape[1]
+    ws_bytes = L.fa_paged_decode_workspace_bytes(w.B, w.H, w.Hkv, w.D, w.topk * w.block_size)
+    ws = torch.empty((max(1, ws_bytes // 4),), dtype=torch.float32, device=dev)
+    P = lambda t: t.data_ptr()  # noqa: E731
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def call(st, name):
+        if st != 0:
+            raise fa.FAError(st, name, fa.last_error())
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        call(L.fa_quest_select(w.B, w.H, w.Hkv, w.D, w.block_size, nb, mxb, w.topk, code, P(q), P(kmeta), P(tables),
+                               P(lens), P(sel), P(nsel), sp), "fa_quest_select")
+        if ev is not None:
+            ev[1].record(stream)
+        call(L.fa_paged_decode_sparse(w.B, w.H, w.Hkv, w.D, w.block_size, nb, mxb, w.topk, code, code, P(q), P(kc),
+                                      P(vc), P(tables), P(lens), P(sel), P(nsel), P(o), P(lse), w.scale, P(ws),
+                                      ws_bytes, sp), "fa_paged_decode_sparse")
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        step(evs[k])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    sel_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    sel_b, dec_b = quest_bytes(w, lens_np)
+    kern = {"fa_quest_select": (sel_ms, sel_b), "fa_paged_decode_sparse": (dec_ms, dec_b)}
+    dom = max(kern, key=lambda k: kern[k][0])
+    ach = kern[dom][1] / (kern[dom][0] * 1e-3) / 1e9
+    out = {
+        "metric": "query-aware sparse decode (page selection + attention over the kept pages) HBM GB/s on 1 MI355X",
+        "value": round((sel_b + dec_b) / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} sequences, contexts {int(lens_np.min())}..{int(lens_np.max())} "
+                               f"tokens, H={w.H} Hkv={w.Hkv} D={w.D} pages of {w.block_size} tokens, {w.topk} pages "
+                               f"kept per context, {w.dtype}",
+                   "B": w.B, "H": w.H, "Hkv": w.Hkv, "D": w.D, "block_size": w.block_size, "topk": w.topk,
+                   "seed": w.seed},
+        "breakdown": {"select_ms": round(sel_ms, 4), "sparse_decode_ms": round(dec_ms, 4),
+                      "select_GB/s": round(sel_b / (sel_ms * 1e-3) / 1e9, 1),
+                      "sparse_decode_GB/s": round(dec_b / (dec_ms * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
+                     "algorithmic": {"amount": kern[dom][1], "unit": "byte", "per_launch": True}},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = decode_cpu_baseline(w, cpu, args.cpu_decode_seqs, args.cpu_workers)
+    return out
 
 
 def run_decode(args):
@@ -568,7 +700,10 @@ def main(argv=None):
         return 2
     if args.steps < 1 or args.warmup < 0:
         ap.error("--steps must be >= 1 and --warmup >= 0")
-    out = run_decode(args) if args.workload in workloads.DECODE_WORKLOADS else run(args)
+    if args.workload in workloads.DECODE_WORKLOADS:
+        out = run_quest(args) if workloads.DECODE_WORKLOADS[args.workload].topk else run_decode(args)
+    else:
+        out = run(args)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -628,9 +628,10 @@ int fa_quest_select(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_
   if (B == 0 || H == 0) return FA_OK;
   FA_TRY(check_ptr(q, "q"));
   FA_TRY(check_ptr(kmeta, "kmeta"));
-  if (block_tables == nullptr || context_lens == nullptr || selected == nullptr || n_selected == nullptr ||
-      reinterpret_cast<uintptr_t>(block_tables) % 4 != 0 || reinterpret_cast<uintptr_t>(context_lens) % 4 != 0 ||
-      reinterpret_cast<uintptr_t>(selected) % 4 != 0 || reinterpret_cast<uintptr_t>(n_selected) % 4 != 0)
+  if (block_tables == nullptr || context_lens == nullptr || (selected == nullptr && topk > 0) ||
+      n_selected == nullptr || reinterpret_cast<uintptr_t>(block_tables) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(context_lens) % 4 != 0 || reinterpret_cast<uintptr_t>(selected) % 4 != 0 ||
+      reinterpret_cast<uintptr_t>(n_selected) % 4 != 0)
     return fail(FA_ERR_INVALID_ARGUMENT, "an index array is NULL or not 4-byte aligned");
   fa::QuestArgs a{};
   a.B = B; a.H = H; a.Hkv = Hkv; a.D = D; a.block_size = block_size; a.num_blocks = num_blocks;
@@ -648,13 +649,16 @@ int fa_paged_decode_sparse(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t
                            hipStream_t stream) {
   g_last_error.clear();
   if (topk < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative topk");
-  if (B > 0 && H > 0 && (selected == nullptr || n_selected == nullptr ||
+  if (B > 0 && H > 0 && ((selected == nullptr && topk > 0) || n_selected == nullptr ||
                          reinterpret_cast<uintptr_t>(selected) % 4 != 0 ||
                          reinterpret_cast<uintptr_t>(n_selected) % 4 != 0))
     return fail(FA_ERR_INVALID_ARGUMENT, "selected / n_selected NULL or not 4-byte aligned");
+  // With topk == 0 no list entry is read (every count clamps to 0); the
+  // kernel only needs a non-null list to take the sparse path.
+  const int32_t* sel = selected != nullptr ? selected : n_selected;
   return paged_decode_impl(B, H, Hkv, D, block_size, num_blocks, max_blocks_per_seq, topk * block_size, dtype,
                            o_dtype, q, k_cache, v_cache, block_tables, context_lens, o, lse, scale, workspace,
-                           workspace_bytes, stream, selected, n_selected, topk);
+                           workspace_bytes, stream, sel, n_selected, topk);
 }
 
 

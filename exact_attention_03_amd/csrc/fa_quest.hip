@@ -85,7 +85,6 @@ __global__ __launch_bounds__(256) void fa_quest_select_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kmeta, const int* __restrict__ block_tables,
     const int* __restrict__ context_lens, int* __restrict__ selected, int* __restrict__ n_selected, int H, int Hkv,
     int G, int bs, int64_t num_blocks, int max_blocks, int topk) {
-  __shared__ float sq[16 * D];
   __shared__ float skey[kQuestMaxPages];
   __shared__ int sidx[kQuestMaxPages];
   __shared__ int scount[256];
@@ -98,105 +97,183 @@ __global__ __launch_bounds__(256) void fa_quest_select_kernel(
   const int n_pages = (int)((n_ctx + bs - 1) / bs);
   const int keep = n_pages < topk ? n_pages : topk;
 
-  for (int e = tid; e < G * D; e += 256) {
-    const int h = hk * G + e / D;
-    const uint16_t x = q[((int64_t)b * H + h) * D + e % D];
-    sq[e] = lo16_to_f32<T>(x);
+  // Scores.  For min <= max, max(a x, a y) = a (x + y) / 2 + |a| (y - x) / 2,
+  // so the group's score sum_h sum_d max(q_hd min_d, q_hd max_d) equals
+  // sum_d (A_d min_d + B_d max_d) with A = (Q1 - Q2) / 2, B = (Q1 + Q2) / 2,
+  // Q1_d = sum_h q_hd and Q2_d = sum_h |q_hd|: one dot product per page for
+  // any G.  Sixteen lanes score one page (lane holding channels E l .. E l +
+  // E - 1 of the page's min and max rows), so a wave scores 4 pages per
+  // instruction and sums over 16 lanes.
+  __shared__ float sab[2 * D];
+  constexpr int E = D / 16;
+  const int lane = tid & 63;
+  const int w = wave_id();
+  const int sub = lane >> 4;  // which of the wave's 4 pages
+  const int c0 = E * (lane & 15);
+  for (int d = tid; d < D; d += 256) {
+    float q1 = 0.f, q2 = 0.f;
+    for (int h = 0; h < G; ++h) {
+      const float x = lo16_to_f32<T>(q[((int64_t)b * H + hk * G + h) * D + d]);
+      q1 += x;
+      q2 += fabsf(x);
+    }
+    sab[d] = 0.5f * (q1 - q2);
+    sab[D + d] = 0.5f * (q1 + q2);
   }
   int P2 = 1;
   while (P2 < n_pages) P2 <<= 1;
   __syncthreads();
+  float va[E], vb[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    va[e] = sab[c0 + e];
+    vb[e] = sab[D + c0 + e];
+  }
 
   const int* table = block_tables + (int64_t)b * max_blocks;
-  for (int p = tid; p < P2; p += 256) {
-    float s = -INFINITY;
-    int idx = 0x7fffffff;  // padding sorts last
-    if (p < n_pages) {
-      idx = p;
-      const int blk = table[p];
-      if (blk >= 0 && blk < num_blocks) {
-        const uint16_t* m = kmeta + ((int64_t)blk * Hkv + hk) * 2 * D;
-        s = 0.f;
-        for (int d = 0; d < D; d += 8) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(m + d);
-          const u32x4 z = *reinterpret_cast<const u32x4*>(m + D + d);
+  constexpr int U = 4;  // 4 pages per lane group per iteration: 16 pages per wave
+  for (int base = 16 * w; base < P2; base += 64) {
+    constexpr int NV = E / 4;  // 8-byte pieces of the lane's channels
+    u32x2 mn[U][NV], mx[U][NV];
+    bool ok[U];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float mn = (i & 1) ? hi16_to_f32<T>(a[i / 2]) : lo16_to_f32<T>(a[i / 2]);
-            const float mx = (i & 1) ? hi16_to_f32<T>(z[i / 2]) : lo16_to_f32<T>(z[i / 2]);
-            for (int h = 0; h < G; ++h) {
-              const float qd = sq[h * D + d + i];
-              s += fmaxf(qd * mn, qd * mx);
-            }
-          }
+    for (int u = 0; u < U; ++u) {
+      const int p = base + 4 * u + sub;
+      const int blk = p < n_pages ? table[p] : -1;
+      ok[u] = blk >= 0 && blk < num_blocks;
+      if (ok[u]) {
+        const uint16_t* m = kmeta + ((int64_t)blk * Hkv + hk) * 2 * D + c0;
+#pragma unroll
+        for (int x = 0; x < NV; ++x) {
+          mn[u][x] = *reinterpret_cast<const u32x2*>(m + 4 * x);
+          mx[u][x] = *reinterpret_cast<const u32x2*>(m + D + 4 * x);
         }
       }
     }
-    skey[p] = s;
-    sidx[p] = idx;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = base + 4 * u + sub;
+      float part = 0.f;
+      if (ok[u]) {
+#pragma unroll
+        for (int x = 0; x < NV; ++x)
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int e = 4 * x + 2 * i;
+            part = __builtin_fmaf(va[e], lo16_to_f32<T>(mn[u][x][i]), part);
+            part = __builtin_fmaf(vb[e], lo16_to_f32<T>(mx[u][x][i]), part);
+            part = __builtin_fmaf(va[e + 1], hi16_to_f32<T>(mn[u][x][i]), part);
+            part = __builtin_fmaf(vb[e + 1], hi16_to_f32<T>(mx[u][x][i]), part);
+          }
+      }
+#pragma unroll
+      for (int x = 8; x >= 1; x >>= 1) part += __shfl_xor(part, x, 64);
+      if ((lane & 15) == 0 && p < P2) {
+        skey[p] = ok[u] ? part : -INFINITY;
+        sidx[p] = p < n_pages ? p : 0x7fffffff;  // padding sorts last
+      }
+    }
   }
   __syncthreads();
 
-  // Bitonic sort of P2 entries: "before" = higher score, or equal score and
-  // lower page.
-  for (int k = 2; k <= P2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P2; i += 256) {
-        const int l = i ^ j;
-        if (l > i) {
-          const float si = skey[i], sl = skey[l];
-          const int ii = sidx[i], il = sidx[l];
-          const bool l_before_i = sl > si || (sl == si && il < ii);
-          const bool i_before_l = si > sl || (si == sl && ii < il);
-          const bool up = (i & k) == 0;  // this run sorts "before" first
-          if (up ? l_before_i : i_before_l) {
-            skey[i] = sl;
-            skey[l] = si;
-            sidx[i] = il;
-            sidx[l] = ii;
+  // Top-K by radix select: the key of the K-th best page is found 8 bits at a
+  // time (most significant first) from LDS histograms of the order-preserving
+  // integer form of the scores; every page above it is kept, and of the pages
+  // equal to it the lowest ones, up to K in all.  Pages are then listed in
+  // ascending order.  Thread t owns pages [t * per, (t + 1) * per).
+  const int per = (n_pages + 255) / 256;
+  const int p0 = tid * per;
+  const int p1 = p0 + per < n_pages ? p0 + per : n_pages;
+  auto ukey = [&](int p) -> uint32_t {  // larger score -> larger key
+    const uint32_t u = __float_as_uint(skey[p]);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  };
+  uint32_t thr = 0;  // key of the K-th best page
+  int need = keep;   // how many pages equal to thr are kept
+  if (keep > 0 && keep < n_pages) {
+    uint32_t mask = 0;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      scount[tid] = 0;
+      __syncthreads();
+      for (int p = p0; p < p1; ++p) {
+        const uint32_t u = ukey(p);
+        if ((u & mask) == thr) atomicAdd(&scount[(u >> shift) & 255], 1);
+      }
+      __syncthreads();
+      // wave 0 finds the digit: lane l holds bins 255 - 4l .. 252 - 4l
+      if (tid < 64) {
+        int c[4], tot = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          c[i] = scount[255 - 4 * tid - i];
+          tot += c[i];
+        }
+        int incl = tot;  // inclusive prefix over lanes (bins in descending order)
+#pragma unroll
+        for (int x = 1; x < 64; x <<= 1) {
+          const int y = __shfl_up(incl, x, 64);
+          if (tid >= x) incl += y;
+        }
+        int above = incl - tot;  // pages in higher bins
+        if (above < need && need <= incl) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (above < need && need <= above + c[i]) {
+              sidx[0] = 255 - 4 * tid - i;  // the digit (sidx[0] is free scratch here)
+              sidx[1] = need - above;
+            }
+            above += c[i];
           }
         }
       }
       __syncthreads();
+      thr |= (uint32_t)sidx[0] << shift;
+      need = sidx[1];
+      mask |= 255u << shift;
+      __syncthreads();
     }
   }
-
-  // Flag the kept pages (the first `keep` entries), then list them in order:
-  // thread t owns pages [t * per, (t + 1) * per).
-  const int kept0 = tid < keep ? sidx[tid] : -1;  // first 256 kept pages, read before reuse
-  int kept_more[kQuestMaxPages / 256 - 1];
+  // Block-wide exclusive prefix of one int per thread.
+  auto block_scan = [&](int v) -> int {
+    int incl = v;
 #pragma unroll
-  for (int r = 1; r < kQuestMaxPages / 256; ++r) {
-    const int e = r * 256 + tid;
-    kept_more[r - 1] = e < keep ? sidx[e] : -1;
-  }
-  __syncthreads();
-  for (int p = tid; p < n_pages; p += 256) sidx[p] = 0;
-  __syncthreads();
-  if (kept0 >= 0) sidx[kept0] = 1;
-#pragma unroll
-  for (int r = 0; r < kQuestMaxPages / 256 - 1; ++r)
-    if (kept_more[r] >= 0) sidx[kept_more[r]] = 1;
-  __syncthreads();
-  const int per = (n_pages + 255) / 256;
-  const int p0 = tid * per;
-  int cnt = 0;
-  for (int p = p0; p < p0 + per && p < n_pages; ++p) cnt += sidx[p];
-  scount[tid] = cnt;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int t = 0; t < 256; ++t) {
-      const int c = scount[t];
-      scount[t] = run;
-      run += c;
+    for (int x = 1; x < 64; x <<= 1) {
+      const int y = __shfl_up(incl, x, 64);
+      if ((tid & 63) >= x) incl += y;
     }
+    __syncthreads();
+    if ((tid & 63) == 63) scount[tid >> 6] = incl;
+    __syncthreads();
+    int off = 0;
+    for (int x = 0; x < (tid >> 6); ++x) off += scount[x];
+    return off + incl - v;
+  };
+  // Rank of each page equal to thr among those equal to it, in page order.
+  int n_eq = 0;
+  for (int p = p0; p < p1; ++p) n_eq += keep > 0 && keep < n_pages && ukey(p) == thr;
+  int eq_rank = block_scan(n_eq);
+  int n_kept = 0;
+  bool kept_flags[kQuestMaxPages / 256];
+#pragma unroll
+  for (int i = 0; i < kQuestMaxPages / 256; ++i) {
+    const int p = p0 + i;
+    bool k = false;
+    if (p < p1) {
+      if (keep >= n_pages) {
+        k = true;
+      } else if (keep > 0) {
+        const uint32_t u = ukey(p);
+        k = u > thr || (u == thr && eq_rank++ < need);
+      }
+    }
+    kept_flags[i] = k;
+    n_kept += k;
   }
-  __syncthreads();
+  int pos = block_scan(n_kept);
   int* out = selected + ((int64_t)b * Hkv + hk) * topk;
-  int pos = scount[tid];
-  for (int p = p0; p < p0 + per && p < n_pages; ++p)
-    if (sidx[p]) out[pos++] = p;
+#pragma unroll
+  for (int i = 0; i < kQuestMaxPages / 256; ++i)
+    if (kept_flags[i]) out[pos++] = p0 + i;
   if (tid == 0) n_selected[(int64_t)b * Hkv + hk] = keep;
 }
 

@@ -336,7 +336,8 @@ int fa_paged_decode(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_
  * fa_quest_select: selected (B, Hkv, topk) int32, n_selected (B, Hkv) int32,
  *   written: the kept logical pages of each (sequence, key/value head), min(topk,
  *   pages of the context) of them, ascending; entries past n_selected are
- *   left unwritten.
+ *   left unwritten (with topk == 0, selected may be NULL; so in
+ *   fa_paged_decode_sparse, whose outputs are then O = 0 and lse = -inf).
  * fa_paged_decode_sparse: fa_paged_decode over the tokens of the kept pages
  *   (selected / n_selected as written by fa_quest_select, or any ascending
  *   lists of logical pages); the last page of a context is cut at the

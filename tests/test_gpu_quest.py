@@ -100,6 +100,7 @@ SMALL = [
     (2, 16, 1, 128, 16, 200, 3000, "f16", 40),
     (3, 6, 3, 256, 64, 17, 900, "bf16", 5),
     (5, 4, 2, 64, 16, 1, 60, "f16", 16),     # topk above the page count: every page kept
+    (2, 4, 2, 128, 16, 100, 200, "f16", 0),  # nothing kept
 ]
 
 
@@ -162,6 +163,24 @@ def test_quest_given_selection():
     assert np.all(np.isneginf(to_f64(lse[1, :2]))) and np.all(to_f64(o[1, :2]) == 0)
     fin = np.isfinite(L)
     assert max_abs(to_f64(lse)[fin], L[fin]) <= LSE_MAX_ABS
+
+
+def test_quest_ties_go_to_the_lower_page():
+    """Pages with equal scores (identical metadata): the kept ones are the
+    lowest pages of the tie, as in the oracle."""
+    import torch
+
+    fa = _fa()
+    w = workloads.DecodeWorkload("quest_ties", 417, 2, 4, 2, 64, 16, 300, 600, "bf16")
+    q, kc, vc, tables, lens = workloads.make_decode_inputs(w)
+    g = [t.cuda() for t in (q, kc, vc, tables, lens)]
+    kmeta = fa.quest_page_minmax(g[1], g[3], g[4])
+    # make every page of sequence 0 / head 1 score the same: copy one page's metadata to all
+    blocks = tables[0, : -(-int(lens[0]) // 16)].long().cuda()
+    kmeta[blocks, 1] = kmeta[blocks[3], 1].clone()
+    sel, nsel = fa.quest_select(g[0], kmeta, g[1], g[3], g[4], 5)
+    torch.cuda.synchronize()
+    assert sel[0, 1, :5].tolist() == [0, 1, 2, 3, 4] and int(nsel[0, 1]) == 5
 
 
 def test_quest_workload():

@@ -193,3 +193,40 @@ def test_varlen_argument_errors(fa):
     assert bwd(ws=2 * 4 * 100 * 4 - 4) == 1 and "workspace" in fa.last_error()
     assert lib.fa_bwd_dkdv_varlen(2, 4, 2, 100, 60, 64, 0, CU, *([P] * 4), None, P, P, 0.125, 1, 0, None) == 1
     assert lib.fa_bwd_dq_and_stats_varlen(2, 4, 2, 100, 60, 64, 0, 1, CU, *([P] * 8), 0.125, 1, None) == 1
+
+
+def test_paged_and_quest_argument_errors(fa):
+    """Every call here must fail validation (or be empty) before any HIP call:
+    the pointers are dummies that no kernel may ever see."""
+    lib = fa.lib()
+    I4 = ctypes.c_void_p(0x30000)   # 4-byte aligned index array
+    I8 = ctypes.c_void_p(0x30008)
+
+    def dec(B=2, H=8, Hkv=2, D=128, bs=16, nb=10, mxb=4, mctx=64, ws=None, wsb=0, bt=I4):
+        return lib.fa_paged_decode(B, H, Hkv, D, bs, nb, mxb, mctx, 0, 0, P, P, P, bt, I4, P, P, 0.1, ws, wsb, None)
+
+    assert dec(Hkv=0) == 1 and dec(H=6, Hkv=4) == 1
+    assert dec(H=34, Hkv=2) == 2                                   # 17 query heads per key/value head
+    assert dec(D=96) == 2 and dec(bs=8) == 2 and dec(bs=24) == 2
+    assert dec(bt=ctypes.c_void_p(0x30002)) == 1
+    need = lib.fa_paged_decode_workspace_bytes(1, 8, 1, 128, 10000)
+    assert need > 0 and lib.fa_paged_decode_workspace_bytes(64, 32, 8, 128, 200) == 0  # one split
+    assert dec(B=1, Hkv=1, mctx=10000, mxb=700) == 1 and "workspace" in fa.last_error()
+    assert dec(B=1, Hkv=1, mctx=10000, mxb=700, ws=P, wsb=need - 4) == 1
+    assert dec(B=0, bt=None) == 0                                   # empty batch
+    # cache writes
+    rc = lambda T=4, Hkv=2, D=128, bs=16, nb=4, sl=I8: lib.fa_reshape_and_cache(  # noqa: E731
+        T, Hkv, D, bs, nb, 0, P, P, sl, P, P, None)
+    assert rc(sl=ctypes.c_void_p(0x30004)) == 1                     # slots not 8-byte aligned
+    assert rc(sl=None) == 1 and rc(bs=8) == 2 and rc(D=32) == 2 and rc(T=-1) == 1
+    assert rc(T=0, sl=None) == 0
+    # page selection
+    sel = lambda B=2, H=8, Hkv=2, mxb=100, topk=8, s=I4, ns=I4: lib.fa_quest_select(  # noqa: E731
+        B, H, Hkv, 128, 16, 1000, mxb, topk, 0, P, P, I4, I4, s, ns, None)
+    assert sel(mxb=4097) == 2 and "4096" in fa.last_error()
+    assert sel(topk=-1) == 1 and sel(s=None) == 1 and sel(ns=None) == 1 and sel(H=40, Hkv=2) == 2
+    assert lib.fa_quest_page_minmax(2, 2, 128, 16, 100, 5, 0, P, I4, I4, None, None) == 1
+    assert lib.fa_quest_page_minmax(2, 2, 96, 16, 100, 5, 0, P, I4, I4, P, None) == 2
+    sp = lambda topk=8, s=I4: lib.fa_paged_decode_sparse(  # noqa: E731
+        2, 8, 2, 128, 16, 100, 50, topk, 0, 0, P, P, P, I4, I4, s, I4, P, P, 0.1, None, 0, None)
+    assert sp(topk=-1) == 1 and sp(s=None) == 1

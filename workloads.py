@@ -184,6 +184,7 @@ class DecodeWorkload:
     lo: int            # shortest context
     hi: int            # longest context
     dtype: str
+    topk: int = 0      # pages kept per (sequence, key/value head) by the query-aware selection; 0 = all
 
     @property
     def scale(self) -> float:
@@ -214,6 +215,8 @@ DECODE_WORKLOADS = {
     # 64 sequences of 512..16000 tokens (about 8K on average), 32 query heads over 8
     # key/value heads, D = 128, pages of 16 tokens
     "decode_gqa_bf16": DecodeWorkload("decode_gqa_bf16", 11, 64, 32, 8, 128, 16, 512, 16000, "bf16"),
+    # the same batch and cache with 64 pages (1024 tokens) kept per context by the query-aware selection
+    "quest_gqa_bf16": DecodeWorkload("quest_gqa_bf16", 11, 64, 32, 8, 128, 16, 512, 16000, "bf16", 64),
 }
 
 
