@@ -168,3 +168,28 @@ def test_gqa_shape_errors():
         fa.forward(q, k, k)  # 6 query heads over 4 key/value heads
     with pytest.raises(ValueError):
         fa.forward(q, k[:, :2], k[:, :3].contiguous())  # k and v differ
+
+
+def test_gqa_stage_forms_equal_fused_backward():
+    """fa_bwd_dq_and_stats_gqa then fa_bwd_dkdv_gqa (what a caller timing or
+    scheduling the stages runs) give fa_bwd_gqa's bits."""
+    import torch
+
+    fa = _fa()
+    lib = fa.lib()
+    Z, H, Hkv, N, D = 2, 6, 2, 300, 128
+    w = workloads.Workload("gqa_stages", 31, Z, H, N, D, "bf16", True, 1.0, Hkv)
+    cpu, gpu = device_inputs(w)
+    q, k, v, do = gpu
+    o, lse = fa.forward(q, k, v, causal=True, scale=w.scale)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal=True, scale=w.scale)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    stats = torch.empty((2, Z, H, N), dtype=torch.float32, device="cuda")
+    dq2, dk2, dv2 = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+    assert lib.fa_bwd_dq_and_stats_gqa(Z, H, Hkv, N, D, 1, 1, p(q), p(k), p(v), p(o), p(do), p(lse), p(stats),
+                                       p(dq2), w.scale, 1, None) == 0, fa.last_error()
+    assert lib.fa_bwd_dkdv_gqa(Z, H, Hkv, N, D, 1, p(q), p(k), p(v), p(do), p(stats), p(dk2), p(dv2), w.scale, 1, 0,
+                               None) == 0, fa.last_error()
+    torch.cuda.synchronize()
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))

@@ -181,3 +181,29 @@ def test_varlen_rows_of_other_sequences_are_untouched():
     for t, n in ((o, "o"), (lse, "lse"), (grads[0], "dq"), (grads[1], "dk"), (grads[2], "dv")):
         assert bool((t[:, 250:] == 7.0).all()), f"{n} written past the last sequence"
         assert not bool((t[:, :250] == 7.0).all()), f"{n} not written"
+
+
+def test_varlen_stage_forms_equal_fused_backward():
+    """fa_bwd_dq_and_stats_varlen then fa_bwd_dkdv_varlen give fa_bwd_varlen's bits."""
+    import torch
+
+    fa = _fa()
+    lib = fa.lib()
+    lengths = (77, 0, 300, 129)
+    H, Hkv, D = 4, 2, 64
+    w = workloads.Workload("varlen_stages", 37, len(lengths), H, max(lengths), D, "f16", True, 1.0, Hkv, lengths)
+    cpu, gpu, cu = varlen_device_inputs(w)
+    q, k, v, do = gpu
+    T, mx = w.T, max(lengths)
+    o, lse = fa.forward_varlen(q, k, v, cu, mx, causal=True, scale=w.scale)
+    dq, dk, dv = fa.backward_varlen(q, k, v, o, do, lse, cu, mx, causal=True, scale=w.scale)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    stats = torch.empty((2, H, T), dtype=torch.float32, device="cuda")
+    dq2, dk2, dv2 = torch.empty_like(dq), torch.empty_like(dk), torch.empty_like(dv)
+    assert lib.fa_bwd_dq_and_stats_varlen(len(lengths), H, Hkv, T, mx, D, 0, 0, p(cu), p(q), p(k), p(v), p(o), p(do),
+                                          p(lse), p(stats), p(dq2), w.scale, 1, None) == 0, fa.last_error()
+    assert lib.fa_bwd_dkdv_varlen(len(lengths), H, Hkv, T, mx, D, 0, p(cu), p(q), p(k), p(v), p(do), p(stats), p(dk2),
+                                  p(dv2), w.scale, 1, 0, None) == 0, fa.last_error()
+    torch.cuda.synchronize()
+    for a, b in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
