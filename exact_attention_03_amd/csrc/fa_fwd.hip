@@ -12,7 +12,8 @@
 // Work decomposition on gfx950
 //   * one workgroup = 4 waves working on a Q tile of BM = 128 queries of one
 //     head; wave w owns 32 consecutive queries and keeps them in registers as
-//     the B operand of the score MFMA.  With the causal mask a workgroup takes
+//     the B operand of the score MFMA (at D = 256, 8 waves: two per 32
+//     queries, each owning half of the output channels, see FwdTile).  With the causal mask a workgroup takes
 //     two tiles of the head, a long and a short one, so every workgroup has
 //     the same work; the second tile's Q rows and first K/V tile are fetched
 //     during the first tile's last step;
@@ -47,20 +48,31 @@ namespace fa {
 
 template <int D>
 struct FwdTile {
-  static constexpr int NW = 4;                               // waves per workgroup
+  // D = 256 is split into two D = 128 output halves ([FA-Ascend] §一, §七): a
+  // pair of waves shares 32 queries and each wave owns 128 of the output
+  // channels.  Both compute the full score tile (the same instructions on the
+  // same data give the same bits, so both take the same softmax decisions).
+  // That halves the output accumulator per wave, so two waves per SIMD fit
+  // where one wave with all 256 channels did: 1.90 -> 1.75 ms on the
+  // 128 x 8 x 1024 x 256 workload despite 1.5x the matrix instructions.
+  // Splitting the score contraction as well and summing the two partial
+  // tiles through LDS took 1.95 ms (one more barrier per tile).
+  static constexpr int SPLIT = D == 256 ? 2 : 1;             // waves per 32 queries
+  static constexpr int NW = 4 * SPLIT;                       // waves per workgroup
   static constexpr int BM = kFwdQueries;                     // queries per tile
   static constexpr int BN = fwd_keys(D);                     // keys per tile
   static constexpr int KB = BN / 32;                         // 32-key blocks per tile
-  static_assert(BM == NW * 32, "32 queries per wave");
+  static_assert(BM == 4 * 32, "32 queries per wave (pair)");
   static constexpr int TILE_BYTES = BN * D * 2;
+  static constexpr int DH = D / SPLIT;                       // channels per wave
   static constexpr int KSTEPS = D / 16;                      // k steps of the score MFMA
-  static constexpr int DB = D / 32;                          // 32-wide d blocks of O
+  static constexpr int DB = DH / 32;                         // this wave's 32-wide d blocks of O
   static constexpr int DMA = TILE_BYTES / (NW * 1024);       // 1 KiB copies per wave per tile
   static_assert(DMA * NW * 1024 == TILE_BYTES, "tile must split into 1 KiB copies per wave");
   // Waves per SIMD the register budget is sized for (measured best: more
   // resident waves hide the latency of each wave's chain of copy wait, LDS
   // reads, matrix products and softmax).
-  static constexpr int OCC = D == 256 ? 1 : (D == 128 ? 3 : 4);
+  static constexpr int OCC = D == 256 ? 2 : (D == 128 ? 3 : 4);
 };
 
 // Rescale threshold in exp2 units (see file comment).
@@ -68,7 +80,8 @@ template <typename T>
 inline constexpr float kRescaleSlack = kIsBF16<T> ? 0.0f : 8.0f;
 
 template <int D, typename T, bool CAUSAL, typename OT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FwdTile<D>::OCC, FwdTile<D>::OCC)))
+__global__ __launch_bounds__(FwdTile<D>::NW * 64)
+__attribute__((amdgpu_waves_per_eu(FwdTile<D>::OCC, FwdTile<D>::OCC)))
 void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, void* __restrict__ o, float* __restrict__ lse, int N_max,
                    int ZHkv, int Hkv, int G, int n_qtiles_max, float c2, const int* __restrict__ cu, int64_t n_tokens) {
@@ -86,6 +99,8 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = wave_id();
+  const int qg = C::SPLIT == 1 ? w : w & 3;  // this wave's 32 queries of the tile
+  const int hf = C::SPLIT == 1 ? 0 : w >> 2;  // this wave's channel half
   const int h = lane >> 5;
   const int l32 = lane & 31;
 
@@ -123,12 +138,12 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     }
   };
   // This wave's Q rows of tile qt -> registers, B-operand layout: lane owns
-  // query qt BM + 32 w + l32, k = d.
+  // query qt BM + 32 qg + l32, k = d.
   u32x4 qf[C::KSTEPS];
   auto load_q = [&](int qt) {
 #pragma unroll
     for (int t = 0; t < C::KSTEPS; ++t)
-      qf[t] = gload16(rq, (uint32_t)(((qt * C::BM + 32 * w + l32) * D + 16 * t + 8 * h) * 2));
+      qf[t] = gload16(rq, (uint32_t)(((qt * C::BM + 32 * qg + l32) * D + 16 * t + 8 * h) * 2));
   };
 
   // Per-lane LDS read bases: K rows 32 kb + sigma(l32) as the A operand of
@@ -142,7 +157,7 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   for (int it = 0; it < n_items; ++it) {
     const int qt = it == 0 ? qt_a : qt_b;
     const int q0 = qt * C::BM;
-    const int wq0 = q0 + 32 * w;  // first query of this wave
+    const int wq0 = q0 + 32 * qg;  // first query of this wave
     const int kv_end = CAUSAL ? min(N, q0 + C::BM) : N;
     const int nt = (kv_end + C::BN - 1) / C::BN;
     const bool more = it + 1 < n_items;
@@ -240,7 +255,7 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
           const u32x4 pk = pack8<T>(s[kb], 8 * t2);
 #pragma unroll
           for (int db = 0; db < C::DB; ++db) {
-            const u32x4 a = lds_read_tr_operand<C::BN>(vt, vrd, 32 * kb + 16 * t2, db);
+            const u32x4 a = lds_read_tr_operand<C::BN>(vt, vrd, 32 * kb + 16 * t2, db + C::DB * hf);
             acc[db] = mfma32<T>(a, pk, acc[db]);
           }
         }
@@ -261,7 +276,7 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const int d = 32 * db + 16 * half + 8 * h;
+          const int d = 32 * (db + C::DB * hf) + 16 * half + 8 * h;
           const int j0 = 8 * half;
           u32x4 lo, hi;
           lo.x = __float_as_uint(acc[db][j0 + 0] * inv);
@@ -283,12 +298,12 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         f32x16 y = acc[db] * inv;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const int d = 32 * db + 16 * half + 8 * h;
+          const int d = 32 * (db + C::DB * hf) + 16 * half + 8 * h;
           gstore16(ro, (uint32_t)((query * D + d) * 2), pack8<T>(y, 8 * half));
         }
       }
     }
-    if (h == 0) {
+    if (h == 0 && hf == 0) {
       const auto rl = make_rsrc(lse + hr.q_row0, (uint32_t)N * 4);
       gstore_f32(rl, (uint32_t)query * 4, (m_run + __log2f(lsum)) * kLn2);
     }
@@ -308,7 +323,7 @@ hipError_t launch_fwd_t(const FwdArgs& a) {
   const int ZHkv = (int)(a.Z * a.Hkv);
   const int G = (int)(a.H / a.Hkv);
   const dim3 grid((unsigned)xcd_grid_grouped(ZHkv, G, paired_groups(n_qtiles, CAUSAL)));
-  hipLaunchKernelGGL((fa_fwd_kernel<D, T, CAUSAL, OT>), grid, dim3(256), 0, a.stream,
+  hipLaunchKernelGGL((fa_fwd_kernel<D, T, CAUSAL, OT>), grid, dim3(C::NW * 64), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.o, a.lse,
                      (int)a.N, ZHkv, (int)a.Hkv, G, n_qtiles, a.scale * kLog2e, a.cu_seqlens, a.T);
   return hipGetLastError();
