@@ -306,6 +306,28 @@ def run(args):
             per[name].append(e[i].elapsed_time(e[i + 1]))
     avg = {n: sum(x) / len(x) for n, x in per.items()}
 
+    # The standalone Delta pass (fa_bwd_preprocess), outside the step (the
+    # step's dQ pass computes the same statistics): its HBM rate.
+    delta = None
+    if not w.varlen and Hkv == H:
+        stats2 = torch.empty_like(stats)
+        pre = lambda: call(L.fa_bwd_preprocess(Z, H, N, D, code, code, P(o), P(do), P(lse), P(stats2), sp),  # noqa
+                           "fa_bwd_preprocess")
+        for _ in range(3):
+            pre()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(20):
+            pre()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pre_ms = e0.elapsed_time(e1) / 20
+        pre_bytes = kernel_work(w, o.element_size())["fa_bwd_pre"][1]
+        delta = {"ms": round(pre_ms, 4), "GB/s": round(pre_bytes / (pre_ms * 1e-3) / 1e9, 1),
+                 "frac": round(pre_bytes / (pre_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "bytes": pre_bytes,
+                 "traffic": stored_traffic("fa_bwd_pre", w.name), "in_step": False}
+
     ff = fwd_flops(w)
     fwd_ms = avg["fa_fwd"]
     bwd_ms = avg["fa_bwd_dq"] + avg["fa_bwd_dkdv"]
@@ -363,6 +385,7 @@ def run(args):
             "fwd_frac": round(ff / (fwd_ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
             "bwd_frac": round(2.5 * ff / (bwd_ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS, 4),
             "kernels": kern,
+            "delta_pass": delta,
         },
         "roofline": roof,
         "cpu_baseline": None,
