@@ -532,8 +532,9 @@ int paged_decode_impl(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t bloc
     return fail(FA_ERR_INVALID_ARGUMENT, "H=%lld query heads must be a whole multiple of Hkv=%lld", (long long)H,
                 (long long)Hkv);
   if (B == 0 || H == 0) return FA_OK;
-  if (H / Hkv > 16)
-    return fail(FA_ERR_UNSUPPORTED, "at most 16 query heads per key/value head (H/Hkv=%lld)", (long long)(H / Hkv));
+  if (B * Hkv * ((H / Hkv + 15) / 16) * 64 > kMaxI32)
+    return fail(FA_ERR_UNSUPPORTED, "grid too large (B=%lld Hkv=%lld H/Hkv=%lld)", (long long)B, (long long)Hkv,
+                (long long)(H / Hkv));
   if (B * H > kMaxI32 || max_blocks_per_seq > kMaxI32 || num_blocks > kMaxI32 ||
       max_blocks_per_seq * block_size > kMaxI32)
     return fail(FA_ERR_UNSUPPORTED, "problem too large");
@@ -591,8 +592,6 @@ static int check_quest(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t blo
   if (H > 0 && (Hkv == 0 || H % Hkv != 0))
     return fail(FA_ERR_INVALID_ARGUMENT, "H=%lld query heads must be a whole multiple of Hkv=%lld", (long long)H,
                 (long long)Hkv);
-  if (H > 0 && H / Hkv > 16)
-    return fail(FA_ERR_UNSUPPORTED, "at most 16 query heads per key/value head (H/Hkv=%lld)", (long long)(H / Hkv));
   if (max_blocks_per_seq > fa::kQuestMaxPagesHost)
     return fail(FA_ERR_UNSUPPORTED, "at most %d pages per context (max_blocks_per_seq=%lld)", fa::kQuestMaxPagesHost,
                 (long long)max_blocks_per_seq);

@@ -101,10 +101,17 @@ void fa_paged_decode_kernel(
   const int col = lane & 15;  // head column of the score / output tiles
   const int grp = lane >> 4;  // k group: tokens 4 grp .. 4 grp + 3 of a tile
 
+  // Workgroup = (sequence b, key/value head hk, block hb of 16 of its G query
+  // heads, split s).
+  const int n_hb = (G + 15) / 16;
   const int s = blockIdx.x % n_splits;
-  const int bh = blockIdx.x / n_splits;
+  const int rest = blockIdx.x / n_splits;
+  const int hb = rest % n_hb;
+  const int bh = rest / n_hb;
   const int hk = bh % Hkv;
   const int b = bh / Hkv;
+  const int g0 = 16 * hb;                          // first query head of the block (in the group)
+  const int gn = G - g0 < 16 ? G - g0 : 16;        // query heads in the block
   const int64_t max_tokens = (int64_t)max_blocks * bs;
   const int64_t n_real = context_lens[b] < 0 ? 0 : (context_lens[b] > max_tokens ? max_tokens : context_lens[b]);
   int64_t n_ctx = n_real;  // tokens this (sequence, head) attends to, in order
@@ -131,16 +138,16 @@ void fa_paged_decode_kernel(
   const int64_t t_begin = s * chunk < n_ctx ? s * chunk : n_ctx;
   const int64_t t_end = (s + 1 < n_splits && (s + 1) * chunk < n_ctx) ? (s + 1) * chunk : n_ctx;
 
-  // Q^T as the B operand of the score product: lane supplies head col,
-  // channels 32 ks + 8 grp .. +7; heads past the group are zero.
+  // Q^T as the B operand of the score product: lane supplies head col of the
+  // block, channels 32 ks + 8 grp .. +7; columns past the block are zero.
   u32x4 qf[C::KSTEPS];
   {
-    const int h = hk * G + (col < G ? col : 0);
+    const int h = hk * G + g0 + (col < gn ? col : 0);
     const auto rq = make_rsrc(q + ((int64_t)b * H + h) * D, D * 2);
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
       const u32x4 x = gload16(rq, (uint32_t)((32 * ks + 8 * grp) * 2));
-      qf[ks] = col < G ? x : u32x4{0u, 0u, 0u, 0u};
+      qf[ks] = col < gn ? x : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -246,7 +253,7 @@ void fa_paged_decode_kernel(
   __syncthreads();
 
   constexpr float kLn2 = 0.69314718055994531f;
-  for (int e = tid; e < G * D; e += 256) {
+  for (int e = tid; e < gn * D; e += 256) {
     const int c = e / D, d = e % D;
     float m = -INFINITY;
 #pragma unroll
@@ -262,7 +269,7 @@ void fa_paged_decode_kernel(
     }
     const float val = m != -INFINITY ? acc / l : 0.f;
     const float lse_n = m != -INFINITY ? (m + __log2f(l)) * kLn2 : -INFINITY;
-    const int h = hk * G + c;
+    const int h = hk * G + g0 + c;
     const int64_t row = (int64_t)b * H + h;
     if (n_splits == 1) {
       if constexpr (sizeof(OT) == 4) {
@@ -329,7 +336,7 @@ hipError_t launch_reshape_and_cache(const CacheArgs& a) {
 template <int D, typename T, typename OT>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
   const int G = (int)(a.H / a.Hkv);
-  const int64_t grid = a.B * a.Hkv * a.n_splits;
+  const int64_t grid = a.B * a.Hkv * ((G + 15) / 16) * a.n_splits;
   float* part_o = a.workspace;
   float* part_lse = a.workspace + a.B * a.H * a.n_splits * a.D;
   hipLaunchKernelGGL((fa_paged_decode_kernel<D, T, OT>), dim3((unsigned)grid), dim3(256), 0, a.stream,

@@ -282,7 +282,7 @@ int fa_bwd_dkdv_varlen(int64_t B, int64_t H, int64_t Hkv, int64_t T, int64_t max
  * fa_paged_decode: attention of one query token per sequence over its cached
  * context.
  *   q            : (B, H, D) dtype; query head h uses key/value head
- *                  h / (H / Hkv); H / Hkv <= 16;
+ *                  h / (H / Hkv);
  *   block_tables : DEVICE int32 (B, max_blocks_per_seq): token t of sequence
  *                  b is in physical block block_tables[b][t / block_size] at
  *                  offset t % block_size;
@@ -324,7 +324,7 @@ int fa_paged_decode(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_
  * the channel-wise minimum and maximum of its valid keys, and its score for a
  * query q is sum_d max(q_d * min_d, q_d * max_d), an upper bound of q . k
  * over the page.  A key/value head keeps one set of pages for its G query
- * heads (G <= 16), scored by the sum of their scores; ties go to the lower
+ * heads, scored by the sum of their scores; ties go to the lower
  * page; kept pages are listed in ascending order.  Caches, block tables and
  * context lengths as for fa_paged_decode; contexts of at most 4096 pages
  * (max_blocks_per_seq <= 4096).

@@ -84,6 +84,8 @@ SMALL = [
     (5, 6, 3, 256, 64, 17, 520, "bf16"),
     (64, 16, 16, 64, 16, 1, 40, "f16"),      # one split
     (1, 2, 1, 128, 48, 1, 1, "bf16"),        # one token
+    (2, 32, 1, 128, 16, 100, 900, "bf16"),   # 32 query heads on one key/value head: two blocks of 16
+    (2, 40, 2, 64, 32, 1, 300, "f16"),       # 20 per key/value head: a full and a partial block
 ]
 
 

@@ -101,6 +101,7 @@ SMALL = [
     (3, 6, 3, 256, 64, 17, 900, "bf16", 5),
     (5, 4, 2, 64, 16, 1, 60, "f16", 16),     # topk above the page count: every page kept
     (2, 4, 2, 128, 16, 100, 200, "f16", 0),  # nothing kept
+    (2, 32, 1, 128, 16, 200, 1500, "f16", 10),  # 32 query heads on one key/value head
 ]
 
 

@@ -8,6 +8,21 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _gpu_visible() -> bool:
+    try:
+        import torch
+
+        return torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        return False
+
+
+# The argument-check tests hand the library dummy pointers that must fail
+# validation before any HIP call; where a GPU is visible a slip in such a test
+# would launch a kernel on them, so they run only where none is.
+_NO_GPU = pytest.mark.skipif(_gpu_visible(), reason="dummy-pointer argument checks run only without a GPU")
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
 
@@ -59,6 +74,7 @@ def _fwd(fa, Z=1, H=1, N=128, D=64, dtype=0, odt=0, q=P, k=P, v=P, o=P, lse=P, s
     return fa.lib().fa_fwd(Z, H, N, D, dtype, odt, q, k, v, o, lse, scale, causal, None)
 
 
+@_NO_GPU
 @pytest.mark.parametrize("kw,status", [
     (dict(D=96), 2), (dict(D=0), 2), (dict(N=-1), 1), (dict(dtype=7), 1), (dict(odt=1), 1),
     (dict(q=None), 1), (dict(o=MIS), 1), (dict(lse=None), 1), (dict(scale=0.0), 1),
@@ -70,6 +86,7 @@ def test_fwd_argument_errors(fa, kw, status):
     assert fa.last_error() != ""
 
 
+@_NO_GPU
 def test_empty_problem_is_ok_without_pointers(fa):
     assert _fwd(fa, Z=0, q=None, k=None, v=None, o=None, lse=None) == 0
     assert _fwd(fa, N=0, q=None, k=None, v=None, o=None, lse=None) == 0
@@ -77,6 +94,7 @@ def test_empty_problem_is_ok_without_pointers(fa):
     assert lib.fa_bwd(0, 1, 8, 64, 0, 0, *([None] * 9), 0.125, 0, None, 0, None) == 0
 
 
+@_NO_GPU
 def test_bwd_workspace_rules(fa):
     lib = fa.lib()
     assert lib.fa_bwd_workspace_bytes(128, 8, 1024, 128) == 2 * 128 * 8 * 1024 * 4
@@ -87,6 +105,7 @@ def test_bwd_workspace_rules(fa):
     assert st == 1
 
 
+@_NO_GPU
 def test_stage_argument_errors(fa):
     lib = fa.lib()
     assert lib.fa_bwd_preprocess(1, 1, 64, 64, 0, 1, P, P, P, P, None) == 1    # o_dtype bf16 with f16
@@ -152,6 +171,7 @@ def test_workspace_versus_page_full_scratch(fa):
     assert ours == 2 * g["Z"] * g["H"] * g["N"] * 4 and ours * 256 == full
 
 
+@_NO_GPU
 def test_grouped_head_argument_errors(fa):
     lib = fa.lib()
 
@@ -172,6 +192,7 @@ def test_grouped_head_argument_errors(fa):
     assert lib.fa_bwd_gqa(0, 4, 2, 128, 64, 0, 0, *([None] * 9), 0.125, 0, None, 0, None) == 0
 
 
+@_NO_GPU
 def test_varlen_argument_errors(fa):
     lib = fa.lib()
     CU = ctypes.c_void_p(0x20000)
@@ -195,6 +216,7 @@ def test_varlen_argument_errors(fa):
     assert lib.fa_bwd_dq_and_stats_varlen(2, 4, 2, 100, 60, 64, 0, 1, CU, *([P] * 8), 0.125, 1, None) == 1
 
 
+@_NO_GPU
 def test_paged_and_quest_argument_errors(fa):
     """Every call here must fail validation (or be empty) before any HIP call:
     the pointers are dummies that no kernel may ever see."""
@@ -206,7 +228,6 @@ def test_paged_and_quest_argument_errors(fa):
         return lib.fa_paged_decode(B, H, Hkv, D, bs, nb, mxb, mctx, 0, 0, P, P, P, bt, I4, P, P, 0.1, ws, wsb, None)
 
     assert dec(Hkv=0) == 1 and dec(H=6, Hkv=4) == 1
-    assert dec(H=34, Hkv=2) == 2                                   # 17 query heads per key/value head
     assert dec(D=96) == 2 and dec(bs=8) == 2 and dec(bs=24) == 2
     assert dec(bt=ctypes.c_void_p(0x30002)) == 1
     need = lib.fa_paged_decode_workspace_bytes(1, 8, 1, 128, 10000)
@@ -224,7 +245,7 @@ def test_paged_and_quest_argument_errors(fa):
     sel = lambda B=2, H=8, Hkv=2, mxb=100, topk=8, s=I4, ns=I4: lib.fa_quest_select(  # noqa: E731
         B, H, Hkv, 128, 16, 1000, mxb, topk, 0, P, P, I4, I4, s, ns, None)
     assert sel(mxb=4097) == 2 and "4096" in fa.last_error()
-    assert sel(topk=-1) == 1 and sel(s=None) == 1 and sel(ns=None) == 1 and sel(H=40, Hkv=2) == 2
+    assert sel(topk=-1) == 1 and sel(s=None) == 1 and sel(ns=None) == 1 and sel(H=40, Hkv=3) == 1
     assert lib.fa_quest_page_minmax(2, 2, 128, 16, 100, 5, 0, P, I4, I4, None, None) == 1
     assert lib.fa_quest_page_minmax(2, 2, 96, 16, 100, 5, 0, P, I4, I4, P, None) == 2
     sp = lambda topk=8, s=I4: lib.fa_paged_decode_sparse(  # noqa: E731
