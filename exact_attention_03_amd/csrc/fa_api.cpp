@@ -592,8 +592,8 @@ static int check_quest(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t blo
   if (H > 0 && (Hkv == 0 || H % Hkv != 0))
     return fail(FA_ERR_INVALID_ARGUMENT, "H=%lld query heads must be a whole multiple of Hkv=%lld", (long long)H,
                 (long long)Hkv);
-  if (max_blocks_per_seq > fa::kQuestMaxPagesHost)
-    return fail(FA_ERR_UNSUPPORTED, "at most %d pages per context (max_blocks_per_seq=%lld)", fa::kQuestMaxPagesHost,
+  if (max_blocks_per_seq > fa::kQuestMaxPages)
+    return fail(FA_ERR_UNSUPPORTED, "at most %d pages per context (max_blocks_per_seq=%lld)", fa::kQuestMaxPages,
                 (long long)max_blocks_per_seq);
   if (topk > kMaxI32) return fail(FA_ERR_UNSUPPORTED, "topk too large");
   if (B * Hkv > kMaxI32 || num_blocks > kMaxI32) return fail(FA_ERR_UNSUPPORTED, "problem too large");

@@ -94,7 +94,7 @@ struct QuestArgs {
 };
 hipError_t launch_quest_minmax(const QuestArgs& a);
 hipError_t launch_quest_select(const QuestArgs& a);
-constexpr int kQuestMaxPagesHost = 4096;  // pages per context the selection handles
+constexpr int kQuestMaxPages = 4096;  // pages per context the selection handles (LDS sized for it)
 
 hipError_t launch_reshape_and_cache(const CacheArgs& a);
 hipError_t launch_paged_decode(const DecodeArgs& a);

@@ -78,7 +78,6 @@ __global__ __launch_bounds__(256) void fa_quest_minmax_kernel(const uint16_t* __
 // a bitonic sort orders (score, page) by score descending and page
 // ascending, the first topk pages are flagged, and a prefix count over the
 // flags writes them in ascending page order.
-constexpr int kQuestMaxPages = 4096;
 // Threads per selection workgroup: 8 waves score the pages (one workgroup
 // per (sequence, key/value head) has to finish them all); 0.050 -> 0.036 ms
 // against 4 waves on the 64-sequence workload, 0.041 with 16.
