@@ -11,6 +11,12 @@ Pipeline 优化实战" (BiumBiu): §一 for the forward, §二 for the backward.
 (grouped-query attention, the page "从算子到 Serving：昇腾推理评测链路实践",
 section "GQA Paged Attention"): k and v of shape (Z, Hkv, N, D) with H a whole
 multiple of Hkv; query head h uses key/value head h // (H // Hkv).
+``forward_varlen`` / ``backward_varlen`` take packed batches of sequences of
+different lengths; ``reshape_and_cache`` / ``paged_decode`` work on a paged KV
+cache, and ``quest_page_minmax`` / ``quest_select`` / ``paged_decode_sparse``
+decode over query-selected pages (the same page, sections "ReshapeAndCache",
+"GQA Paged Attention" and "Quest Sparse Attention").  ``attention`` is the
+forward with its backward registered for torch autograd.
 """
 from __future__ import annotations
 
@@ -20,7 +26,7 @@ import math
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32, FAError, check, last_error, lib,  # noqa: F401
                    status_name)
 
-__all__ = ["forward", "backward", "forward_varlen", "backward_varlen", "reshape_and_cache", "paged_decode",
+__all__ = ["attention", "forward", "backward", "forward_varlen", "backward_varlen", "reshape_and_cache", "paged_decode",
            "quest_page_minmax", "quest_select", "paged_decode_sparse",
            "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_dq_and_stats", "workspace_bytes",
            "device_info", "dkdv_schedule", "fwd_tile_pairs", "FAError", "lib"]
@@ -452,3 +458,39 @@ def fwd_tile_pairs(N, D, causal):
     check(lib().fa_fwd_tile_pairs(N, D, int(bool(causal)), ctypes.byref(vis), ctypes.byref(tot)),
           "fa_fwd_tile_pairs")
     return vis.value, tot.value
+
+
+class _Attention:
+    """torch.autograd.Function for ``attention`` (built on first use, so that
+    importing the package does not import torch)."""
+
+    fn = None
+
+    @classmethod
+    def get(cls):
+        if cls.fn is None:
+            torch = _torch()
+
+            class AttentionFunction(torch.autograd.Function):
+                @staticmethod
+                def forward(ctx, q, k, v, causal, scale):
+                    o, lse = forward(q, k, v, causal=causal, scale=scale)
+                    ctx.save_for_backward(q, k, v, o, lse)
+                    ctx.causal, ctx.scale = causal, scale
+                    return o
+
+                @staticmethod
+                def backward(ctx, do):
+                    q, k, v, o, lse = ctx.saved_tensors
+                    dq, dk, dv = backward(q, k, v, o, do.contiguous(), lse, causal=ctx.causal, scale=ctx.scale)
+                    return dq, dk, dv, None, None
+
+            cls.fn = AttentionFunction
+        return cls.fn
+
+
+def attention(q, k, v, causal=False, scale=None):
+    """O = softmax(Q K^T * scale) V with autograd: the forward here, the
+    backward (dq, dk, dv) in the library's backward kernels.  Shapes and dtypes
+    as for ``forward`` (grouped key/value heads included)."""
+    return _Attention.get().apply(q, k, v, bool(causal), scale)

@@ -193,3 +193,23 @@ def test_empty_problem_and_errors():
     with pytest.raises(fa.FAError) as ei:
         fa.forward(bad, bad, bad)
     assert ei.value.status == 2  # FA_ERR_UNSUPPORTED
+
+
+def test_autograd_attention_matches_explicit_calls():
+    """fa.attention under torch autograd gives the explicit forward / backward
+    results bit for bit (plain and grouped heads)."""
+    import torch
+
+    fa = _fa()
+    for (Z, H, Hkv, N, D, causal) in ((1, 4, 4, 200, 64, True), (2, 8, 2, 129, 128, False)):
+        w = workloads.Workload("autograd", 41 + H, Z, H, N, D, "f16", causal, 1.0, Hkv)
+        cpu, gpu = device_inputs(w)
+        q, k, v, do = (t.clone().requires_grad_(i < 3) for i, t in enumerate(gpu))
+        o = fa.attention(q, k, v, causal=causal, scale=w.scale)
+        o.backward(do)
+        o2, lse2 = fa.forward(gpu[0], gpu[1], gpu[2], causal=causal, scale=w.scale)
+        dq2, dk2, dv2 = fa.backward(gpu[0], gpu[1], gpu[2], o2, gpu[3], lse2, causal=causal, scale=w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o.detach().view(torch.int16), o2.view(torch.int16))
+        for a, b in ((q.grad, dq2), (k.grad, dk2), (v.grad, dv2)):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16))
