@@ -13,7 +13,9 @@ the page "从算子到 Serving：昇腾推理评测链路实践" (BiumBiu, 2026-
 as [Serving-Ascend], as do the variable-length batches and the paged KV cache
 (``paged.py``: cache writes and decode attention over pages) and the
 query-aware page selection with attention over the selected pages
-(``quest.py``).
+(``quest.py``); decode attention over two KV sources under one softmax
+(``sources.py``) follows the page "在 4 张 A100 上部署 DeepSeek-V4-Flash-0731"
+(BiumBiu), section 7.5.
 
 Pinning: every function here is pinned by tests marked ``not gpu`` to facts
 other than itself (finite differences, closed forms, invariants, a library
@@ -33,3 +35,4 @@ from .attention import (  # noqa: F401
 )
 from .paged import gather_context, paged_decode, reshape_and_cache  # noqa: F401
 from .quest import quest_page_minmax, quest_scores, quest_select, quest_sparse_decode  # noqa: F401
+from .sources import decode_over_sources, source_tokens  # noqa: F401
