@@ -15,7 +15,9 @@ multiple of Hkv; query head h uses key/value head h // (H // Hkv).
 different lengths; ``reshape_and_cache`` / ``paged_decode`` work on a paged KV
 cache, and ``quest_page_minmax`` / ``quest_select`` / ``paged_decode_sparse``
 decode over query-selected pages (the same page, sections "ReshapeAndCache",
-"GQA Paged Attention" and "Quest Sparse Attention").  ``attention`` is the
+"GQA Paged Attention" and "Quest Sparse Attention"); ``paged_decode_sources``
+decodes over one or two KV sources under one softmax (the page "在 4 张 A100 上
+部署 DeepSeek-V4-Flash-0731", section 7.5).  ``attention`` is the
 forward with its backward registered for torch autograd.
 """
 from __future__ import annotations
@@ -27,7 +29,7 @@ from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32, FAError, check, la
                    status_name)
 
 __all__ = ["attention", "forward", "backward", "forward_varlen", "backward_varlen", "reshape_and_cache", "paged_decode",
-           "quest_page_minmax", "quest_select", "paged_decode_sparse",
+           "quest_page_minmax", "quest_select", "paged_decode_sparse", "paged_decode_sources",
            "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_dq_and_stats", "workspace_bytes",
            "device_info", "dkdv_schedule", "fwd_tile_pairs", "FAError", "lib"]
 
@@ -363,6 +365,63 @@ def paged_decode_sparse(q, k_cache, v_cache, block_tables, context_lens, selecte
                                           _ptr(selected), _ptr(n_selected), _ptr(o), _ptr(lse), _scale(scale, D),
                                           _ptr(ws), nbytes, _stream(q))
     check(st, "fa_paged_decode_sparse")
+    return o, lse
+
+
+def paged_decode_sources(q, sources, scale=None, out_dtype=None):
+    """Decode attention over one or two KV sources under one softmax:
+    (O (B, H, D), lse (B, H)).
+
+    Each source is a dict with k_cache, v_cache (layouts as for
+    ``reshape_and_cache``), block_tables (int32 (B, max_blocks)),
+    context_lens (int32 (B,)) and optionally selected / n_selected (int32
+    (B, Hkv, topk) / (B, Hkv), as from ``quest_select``: only the kept pages
+    take part) and max_context_len (host int sizing a dense source's split;
+    read from context_lens when omitted).  The sources' tokens form one set:
+    one maximum and one denominator per query head.
+    """
+    from . import _lib
+
+    torch = _torch()
+    if not 1 <= len(sources) <= 2:
+        raise ValueError("one or two sources")
+    B, H, D = q.shape
+    recs = []
+    for i, src in enumerate(sources):
+        kc, vc, bt, cl = src["k_cache"], src["v_cache"], src["block_tables"], src["context_lens"]
+        _, _, Hkv, _, bs, nb, mxb = _check_paged(q, kc, vc, bt, cl)
+        if i and Hkv != recs[0][1]:
+            raise ValueError("every source must have the same number of key/value heads")
+        sel, nsel = src.get("selected"), src.get("n_selected")
+        topk = 0
+        if nsel is not None:
+            if sel is None or sel.dim() != 3:
+                raise ValueError("a sparse source needs selected (B, Hkv, topk) with n_selected")
+            topk = sel.shape[2]
+            if sel.shape != (B, Hkv, topk) or nsel.shape != (B, Hkv) or sel.dtype != torch.int32 \
+                    or nsel.dtype != torch.int32 or not sel.is_cuda or not nsel.is_cuda \
+                    or not sel.is_contiguous() or not nsel.is_contiguous():
+                raise ValueError("selected must be int32 (B, Hkv, topk) and n_selected int32 (B, Hkv), on the GPU")
+        elif sel is not None:
+            raise ValueError("selected given without n_selected")
+        mcl = src.get("max_context_len")
+        if mcl is None:
+            mcl = int(cl.max().item()) if (B > 0 and nsel is None) else 0
+        rec = _lib.KvSource(_ptr(kc), _ptr(vc), _ptr(bt), _ptr(cl), bs, nb, mxb, int(mcl),
+                            _ptr(sel) if (nsel is not None and topk > 0) else None,
+                            _ptr(nsel) if nsel is not None else None, topk)
+        recs.append((rec, Hkv))
+    arr = (_lib.KvSource * len(recs))(*[r for r, _ in recs])
+    Hkv = recs[0][1]
+    odt = q.dtype if out_dtype is None else out_dtype
+    with torch.cuda.device(q.device):
+        o = torch.empty((B, H, D), dtype=odt, device=q.device)
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+        nbytes = lib().fa_paged_decode_sources_workspace_bytes(B, H, Hkv, D, len(recs), arr)
+        ws = torch.empty((max(1, nbytes // 4),), dtype=torch.float32, device=q.device)
+        st = lib().fa_paged_decode_sources(B, H, Hkv, D, _dtype_code(q), _dtype_code(o), _ptr(q), len(recs), arr,
+                                           _ptr(o), _ptr(lse), _scale(scale, D), _ptr(ws), nbytes, _stream(q))
+    check(st, "fa_paged_decode_sources")
     return o, lse
 
 

@@ -510,45 +510,86 @@ size_t fa_paged_decode_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_
 
 namespace {
 
-// Paged decode over whole contexts (selected == nullptr) or over the kept
-// pages of each (sequence, key/value head).
-int paged_decode_impl(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_size, int64_t num_blocks,
-                      int64_t max_blocks_per_seq, int64_t max_context_len, int dtype, int o_dtype, const void* q,
-                      const void* k_cache, const void* v_cache, const int32_t* block_tables,
-                      const int32_t* context_lens, void* o, float* lse, float scale, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream, const int32_t* selected,
-                      const int32_t* n_selected, int64_t topk) {
+// The context split of one source: sized for its longest context (dense) or
+// for topk pages (sparse).
+fa::DecodeSplit source_split(const fa_kv_source& x, int64_t B, int64_t Hkv) {
+  const int64_t longest = x.n_selected != nullptr ? x.topk * x.block_size : x.max_context_len;
+  return fa::decode_split(B, Hkv, longest < 0 ? 0 : longest);
+}
+
+// Checks one KV source of a decode call and fills its kernel record (the
+// split included).  A source with n_selected != NULL is sparse.
+// With check_pointers false (an empty call) the pointers are not looked at.
+int check_source(const fa_kv_source& x, int idx, int64_t B, int64_t Hkv, bool check_pointers,
+                 fa::DecodeSource* out) {
+  if (x.block_size < 0 || x.num_blocks < 0 || x.max_blocks_per_seq < 0 || x.max_context_len < 0 || x.topk < 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "source %d: negative size", idx);
+  if (x.block_size < 16 || x.block_size > 1024 || x.block_size % 16 != 0)
+    return fail(FA_ERR_UNSUPPORTED, "source %d: block_size=%lld must be a multiple of 16 in [16, 1024]", idx,
+                (long long)x.block_size);
+  if (x.max_blocks_per_seq > kMaxI32 || x.num_blocks > kMaxI32 || x.max_blocks_per_seq * x.block_size > kMaxI32 ||
+      x.topk > kMaxI32 || B * Hkv * (x.topk > 0 ? x.topk : 1) > (int64_t)1 << 40)
+    return fail(FA_ERR_UNSUPPORTED, "source %d: problem too large", idx);
+  const bool sparse = x.n_selected != nullptr;
+  if (!sparse && x.selected != nullptr)
+    return fail(FA_ERR_INVALID_ARGUMENT, "source %d: selected given without n_selected", idx);
+  if (!check_pointers) return FA_OK;
+  if (x.k_cache == nullptr || x.v_cache == nullptr || reinterpret_cast<uintptr_t>(x.k_cache) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(x.v_cache) % 16 != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "source %d: k_cache / v_cache NULL or not 16-byte aligned", idx);
+  if (x.block_tables == nullptr || x.context_lens == nullptr ||
+      reinterpret_cast<uintptr_t>(x.block_tables) % 4 != 0 || reinterpret_cast<uintptr_t>(x.context_lens) % 4 != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "source %d: block_tables / context_lens NULL or not 4-byte aligned", idx);
+  if (sparse && ((x.selected == nullptr && x.topk > 0) || reinterpret_cast<uintptr_t>(x.selected) % 4 != 0 ||
+                 reinterpret_cast<uintptr_t>(x.n_selected) % 4 != 0))
+    return fail(FA_ERR_INVALID_ARGUMENT, "source %d: selected NULL with topk > 0, or not 4-byte aligned", idx);
+  const fa::DecodeSplit split = source_split(x, B, Hkv);
+  out->k_cache = x.k_cache;
+  out->v_cache = x.v_cache;
+  out->block_tables = x.block_tables;
+  out->context_lens = x.context_lens;
+  out->block_size = x.block_size;
+  out->num_blocks = x.num_blocks;
+  out->max_blocks = x.max_blocks_per_seq;
+  // With topk == 0 no list entry is read (every count clamps to 0); the
+  // kernel only needs a non-null list to take the sparse path.
+  out->selected = sparse ? (x.selected != nullptr ? x.selected : x.n_selected) : nullptr;
+  out->n_selected = sparse ? x.n_selected : nullptr;
+  out->topk = sparse ? x.topk : 0;
+  out->n_splits = split.n_splits;
+  out->chunk = split.chunk;
+  return FA_OK;
+}
+
+// Paged decode over one or two sources.
+int paged_decode_impl(int64_t B, int64_t H, int64_t Hkv, int64_t D, int dtype, int o_dtype, const void* q,
+                      int n_sources, const fa_kv_source* sources, void* o, float* lse, float scale, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
   g_last_error.clear();
-  if (B < 0 || H < 0 || Hkv < 0 || num_blocks < 0 || block_size < 0 || max_blocks_per_seq < 0 ||
-      max_context_len < 0)
-    return fail(FA_ERR_INVALID_ARGUMENT, "negative size");
+  if (B < 0 || H < 0 || Hkv < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative size");
+  if (n_sources < 1 || n_sources > 2 || sources == nullptr)
+    return fail(FA_ERR_INVALID_ARGUMENT, "n_sources=%d must be 1 or 2 with a sources array", n_sources);
   if (D != 64 && D != 128 && D != 256)
     return fail(FA_ERR_UNSUPPORTED, "head dim D=%lld not supported (64, 128 or 256)", (long long)D);
-  if (block_size < 16 || block_size > 1024 || block_size % 16 != 0)
-    return fail(FA_ERR_UNSUPPORTED, "block_size=%lld must be a multiple of 16 in [16, 1024]", (long long)block_size);
   FA_TRY(check_dtypes(dtype, o_dtype, true));
   FA_TRY(check_scale(scale, 0));
   if (H > 0 && (Hkv == 0 || H % Hkv != 0))
     return fail(FA_ERR_INVALID_ARGUMENT, "H=%lld query heads must be a whole multiple of Hkv=%lld", (long long)H,
                 (long long)Hkv);
-  if (B == 0 || H == 0) return FA_OK;
-  if (B * Hkv * ((H / Hkv + 15) / 16) * 64 > kMaxI32)
+  fa::DecodeArgs a{};
+  const bool empty = B == 0 || H == 0;
+  for (int i = 0; i < n_sources; ++i) FA_TRY(check_source(sources[i], i, B, Hkv, !empty, &a.src[i]));
+  if (empty) return FA_OK;
+  const int64_t n_splits = a.src[0].n_splits + (n_sources > 1 ? a.src[1].n_splits : 0);
+  if (B * Hkv * ((H / Hkv + 15) / 16) * n_splits > kMaxI32 || B * H * n_splits * (D + 1) > ((int64_t)1 << 40))
     return fail(FA_ERR_UNSUPPORTED, "grid too large (B=%lld Hkv=%lld H/Hkv=%lld)", (long long)B, (long long)Hkv,
                 (long long)(H / Hkv));
-  if (B * H > kMaxI32 || max_blocks_per_seq > kMaxI32 || num_blocks > kMaxI32 ||
-      max_blocks_per_seq * block_size > kMaxI32)
-    return fail(FA_ERR_UNSUPPORTED, "problem too large");
+  if (B * H > kMaxI32) return fail(FA_ERR_UNSUPPORTED, "problem too large");
   FA_TRY(check_ptr(q, "q"));
-  FA_TRY(check_ptr(k_cache, "k_cache"));
-  FA_TRY(check_ptr(v_cache, "v_cache"));
   FA_TRY(check_ptr(o, "o"));
-  if (block_tables == nullptr || context_lens == nullptr ||
-      reinterpret_cast<uintptr_t>(block_tables) % 4 != 0 || reinterpret_cast<uintptr_t>(context_lens) % 4 != 0)
-    return fail(FA_ERR_INVALID_ARGUMENT, "block_tables / context_lens NULL or not 4-byte aligned");
   if (lse != nullptr && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
     return fail(FA_ERR_INVALID_ARGUMENT, "lse is not 4-byte aligned");
-  const fa::DecodeSplit split = fa::decode_split(B, Hkv, max_context_len);
-  const size_t need = fa_paged_decode_workspace_bytes(B, H, Hkv, D, max_context_len);
+  const size_t need = n_splits > 1 ? (size_t)(B * H * n_splits * (D + 1)) * sizeof(float) : 0;
   if (need > 0) {
     if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
       return fail(FA_ERR_INVALID_ARGUMENT, "workspace is NULL or not 16-byte aligned");
@@ -556,13 +597,30 @@ int paged_decode_impl(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t bloc
       return fail(FA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu bytes needed",
                   workspace_bytes, need);
   }
-  fa::DecodeArgs a{};
-  a.B = B; a.H = H; a.Hkv = Hkv; a.D = D; a.block_size = block_size; a.num_blocks = num_blocks;
-  a.max_blocks = max_blocks_per_seq; a.dtype = dtype; a.o_dtype = o_dtype; a.q = q; a.k_cache = k_cache;
-  a.v_cache = v_cache; a.block_tables = block_tables; a.context_lens = context_lens; a.o = o; a.lse = lse;
-  a.scale = scale; a.n_splits = split.n_splits; a.chunk = split.chunk; a.workspace = static_cast<float*>(workspace);
-  a.stream = stream; a.selected = selected; a.n_selected = n_selected; a.topk = topk;
+  a.B = B; a.H = H; a.Hkv = Hkv; a.D = D; a.dtype = dtype; a.o_dtype = o_dtype; a.q = q;
+  a.n_sources = n_sources; a.o = o; a.lse = lse; a.scale = scale; a.workspace = static_cast<float*>(workspace);
+  a.stream = stream;
   return finish(fa::launch_paged_decode(a), stream, "fa_paged_decode launch");
+}
+
+// A single dense or sparse source from the arguments of the one-source calls.
+fa_kv_source one_source(int64_t block_size, int64_t num_blocks, int64_t max_blocks_per_seq, int64_t max_context_len,
+                        const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                        const int32_t* context_lens, const int32_t* selected, const int32_t* n_selected,
+                        int64_t topk) {
+  fa_kv_source x{};
+  x.k_cache = k_cache;
+  x.v_cache = v_cache;
+  x.block_tables = block_tables;
+  x.context_lens = context_lens;
+  x.block_size = block_size;
+  x.num_blocks = num_blocks;
+  x.max_blocks_per_seq = max_blocks_per_seq;
+  x.max_context_len = max_context_len;
+  x.selected = selected;
+  x.n_selected = n_selected;
+  x.topk = topk;
+  return x;
 }
 
 }  // namespace
@@ -574,9 +632,10 @@ int fa_paged_decode(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_
                     const void* k_cache, const void* v_cache, const int32_t* block_tables,
                     const int32_t* context_lens, void* o, float* lse, float scale, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
-  return paged_decode_impl(B, H, Hkv, D, block_size, num_blocks, max_blocks_per_seq, max_context_len, dtype,
-                           o_dtype, q, k_cache, v_cache, block_tables, context_lens, o, lse, scale, workspace,
-                           workspace_bytes, stream, nullptr, nullptr, 0);
+  const fa_kv_source x = one_source(block_size, num_blocks, max_blocks_per_seq, max_context_len, k_cache, v_cache,
+                                    block_tables, context_lens, nullptr, nullptr, 0);
+  return paged_decode_impl(B, H, Hkv, D, dtype, o_dtype, q, 1, &x, o, lse, scale, workspace, workspace_bytes,
+                           stream);
 }
 
 // The common checks of the page-selection calls.
@@ -652,12 +711,25 @@ int fa_paged_decode_sparse(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t
                          reinterpret_cast<uintptr_t>(selected) % 4 != 0 ||
                          reinterpret_cast<uintptr_t>(n_selected) % 4 != 0))
     return fail(FA_ERR_INVALID_ARGUMENT, "selected / n_selected NULL or not 4-byte aligned");
-  // With topk == 0 no list entry is read (every count clamps to 0); the
-  // kernel only needs a non-null list to take the sparse path.
-  const int32_t* sel = selected != nullptr ? selected : n_selected;
-  return paged_decode_impl(B, H, Hkv, D, block_size, num_blocks, max_blocks_per_seq, topk * block_size, dtype,
-                           o_dtype, q, k_cache, v_cache, block_tables, context_lens, o, lse, scale, workspace,
-                           workspace_bytes, stream, sel, n_selected, topk);
+  const fa_kv_source x = one_source(block_size, num_blocks, max_blocks_per_seq, 0, k_cache, v_cache, block_tables,
+                                    context_lens, selected, n_selected, topk);
+  return paged_decode_impl(B, H, Hkv, D, dtype, o_dtype, q, 1, &x, o, lse, scale, workspace, workspace_bytes,
+                           stream);
+}
+
+size_t fa_paged_decode_sources_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t D, int n_sources,
+                                               const fa_kv_source* sources) {
+  if (B <= 0 || H <= 0 || Hkv <= 0 || D <= 0 || n_sources < 1 || n_sources > 2 || sources == nullptr) return 0;
+  int64_t s = 0;
+  for (int i = 0; i < n_sources; ++i) s += source_split(sources[i], B, Hkv).n_splits;
+  return s > 1 ? (size_t)(B * H * s * (D + 1)) * sizeof(float) : 0;
+}
+
+int fa_paged_decode_sources(int64_t B, int64_t H, int64_t Hkv, int64_t D, int dtype, int o_dtype, const void* q,
+                            int n_sources, const fa_kv_source* sources, void* o, float* lse, float scale,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return paged_decode_impl(B, H, Hkv, D, dtype, o_dtype, q, n_sources, sources, o, lse, scale, workspace,
+                           workspace_bytes, stream);
 }
 
 

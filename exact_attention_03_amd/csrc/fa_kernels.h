@@ -57,24 +57,36 @@ struct CacheArgs {
   hipStream_t stream;
 };
 
-// Decode attention over a paged cache (one query token per sequence).
-struct DecodeArgs {
-  int64_t B, H, Hkv, D, block_size, num_blocks, max_blocks;
-  int dtype, o_dtype;
-  const void *q, *k_cache, *v_cache;
+// One paged KV source of a decode call: a cache with its block table and
+// context lengths, attended whole or, with a selection, over its kept pages.
+struct DecodeSource {
+  const void *k_cache, *v_cache;
   const int* block_tables;
   const int* context_lens;
-  void* o;
-  float* lse;  // may be nullptr
-  float scale;
-  int n_splits;      // context splits per (sequence, key/value head); > 1 needs workspace
-  int64_t chunk;     // context tokens per split (a multiple of 64; the last split takes the rest)
-  float* workspace;  // (B, H, n_splits, D) partial outputs, then (B, H, n_splits) partial lse
+  int64_t block_size, num_blocks, max_blocks;
   // Sparse decode: the kept logical pages of each (sequence, key/value head),
   // (B, Hkv, topk) ascending, and their count (B, Hkv); nullptr for dense.
   const int* selected = nullptr;
   const int* n_selected = nullptr;
   int64_t topk = 0;
+  int n_splits = 1;   // context splits of this source per (sequence, key/value head)
+  int64_t chunk = 64;  // context tokens per split (a multiple of 64; the last split takes the rest)
+};
+
+// Decode attention (one query token per sequence) over one or two paged KV
+// sources whose tokens share one softmax.
+struct DecodeArgs {
+  int64_t B, H, Hkv, D;
+  int dtype, o_dtype;
+  const void* q;
+  DecodeSource src[2];
+  int n_sources;
+  void* o;
+  float* lse;  // may be nullptr
+  float scale;
+  // With more than one split over all sources: (B, H, S, D) partial outputs,
+  // then (B, H, S) partial lse, S = the sources' splits together.
+  float* workspace;
   hipStream_t stream;
 };
 

@@ -82,14 +82,24 @@ struct DecodeTile {
   static constexpr int OCC = D == 64 ? 5 : (D == 128 ? 2 : 1);
 };
 
+// One KV source as the kernel sees it (see DecodeSource).
+struct KvSrc {
+  const uint16_t* k;
+  const uint16_t* v;
+  const int* tables;
+  const int* lens;
+  const int* sel;   // kept pages (B, Hkv, topk), or nullptr for the whole context
+  const int* nsel;  // their count (B, Hkv)
+  int64_t num_blocks;
+  int64_t chunk;  // tokens per split
+  int bs, max_blocks, topk, n_splits;
+};
+
 template <int D, typename T, typename OT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecodeTile<D>::OCC, DecodeTile<D>::OCC)))
-void fa_paged_decode_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
-    const int* __restrict__ block_tables, const int* __restrict__ context_lens, void* __restrict__ o,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse, int H, int Hkv, int G, int bs,
-    int64_t num_blocks, int max_blocks, int n_splits, int64_t chunk, float c2, const int* __restrict__ sel,
-    const int* __restrict__ nsel, int topk) {
+void fa_paged_decode_kernel(const uint16_t* __restrict__ q, KvSrc src0, KvSrc src1, void* __restrict__ o,
+                            float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse, int H,
+                            int Hkv, int G, float c2) {
   using C = DecodeTile<D>;
   __shared__ float sm_m[C::NW][16];
   __shared__ float sm_l[C::NW][16];
@@ -102,9 +112,17 @@ void fa_paged_decode_kernel(
   const int grp = lane >> 4;  // k group: tokens 4 grp .. 4 grp + 3 of a tile
 
   // Workgroup = (sequence b, key/value head hk, block hb of 16 of its G query
-  // heads, split s).
+  // heads, split s_all); the splits of the first source come first, then
+  // those of the second (src1.n_splits = 0 with one source).  Every split's
+  // partial result joins the same combine, so the tokens of both sources
+  // share one softmax.
   const int n_hb = (G + 15) / 16;
-  const int s = blockIdx.x % n_splits;
+  const int n_splits = src0.n_splits + src1.n_splits;  // over all sources
+  const int s_all = blockIdx.x % n_splits;
+  const bool second = s_all >= src0.n_splits;
+  const KvSrc src = second ? src1 : src0;
+  const int s = second ? s_all - src0.n_splits : s_all;  // split within the source
+  const int bs = src.bs;
   const int rest = blockIdx.x / n_splits;
   const int hb = rest % n_hb;
   const int bh = rest / n_hb;
@@ -112,18 +130,20 @@ void fa_paged_decode_kernel(
   const int b = bh / Hkv;
   const int g0 = 16 * hb;                          // first query head of the block (in the group)
   const int gn = G - g0 < 16 ? G - g0 : 16;        // query heads in the block
-  const int64_t max_tokens = (int64_t)max_blocks * bs;
-  const int64_t n_real = context_lens[b] < 0 ? 0 : (context_lens[b] > max_tokens ? max_tokens : context_lens[b]);
+  const int64_t max_tokens = (int64_t)src.max_blocks * bs;
+  const int ctx = src.lens[b];
+  const int64_t n_real = ctx < 0 ? 0 : (ctx > max_tokens ? max_tokens : ctx);
   int64_t n_ctx = n_real;  // tokens this (sequence, head) attends to, in order
   // Sparse decode: the tokens of the kept pages, back to back (a virtual
   // context); the last kept page is cut at the context's end when it is the
   // context's last page.
   const int* selrow = nullptr;
   int ns = 0;
-  if (sel != nullptr) {
+  if (src.sel != nullptr) {
     const int64_t row = (int64_t)b * Hkv + hk;
-    ns = nsel[row] < 0 ? 0 : (nsel[row] > topk ? topk : nsel[row]);
-    selrow = sel + row * topk;
+    const int cnt = src.nsel[row];
+    ns = cnt < 0 ? 0 : (cnt > src.topk ? src.topk : cnt);
+    selrow = src.sel + row * src.topk;
     const int64_t n_pages = (n_real + bs - 1) / bs;
     if (ns == 0) {
       n_ctx = 0;
@@ -135,8 +155,9 @@ void fa_paged_decode_kernel(
   // This split's tokens: chunk tokens (a whole number of 64-token steps, one
   // 16-token tile per wave per step) from s * chunk on; the last split takes
   // the rest of a context longer than the split was sized for.
+  const int64_t chunk = src.chunk;
   const int64_t t_begin = s * chunk < n_ctx ? s * chunk : n_ctx;
-  const int64_t t_end = (s + 1 < n_splits && (s + 1) * chunk < n_ctx) ? (s + 1) * chunk : n_ctx;
+  const int64_t t_end = (s + 1 < src.n_splits && (s + 1) * chunk < n_ctx) ? (s + 1) * chunk : n_ctx;
 
   // Q^T as the B operand of the score product: lane supplies head col of the
   // block, channels 32 ks + 8 grp .. +7; columns past the block are zero.
@@ -165,23 +186,23 @@ void fa_paged_decode_kernel(
   // Block-table entries of this wave's tiles, 64 tiles at a time: lane i
   // holds the physical block of tile j0 + i (read with one vector load, so
   // that the loop does not wait on a scalar load per tile).
-  const int* table = block_tables + (int64_t)b * max_blocks;
+  const int* table = src.tables + (int64_t)b * src.max_blocks;
   const int64_t w_first = t_begin + 16 * w;  // this wave's first token
   int vblk = -1;
   auto load_blocks = [&](int64_t j0) {
     int64_t page = (w_first + 64 * (j0 + lane)) / bs;  // position in the (virtual) context
     if (selrow != nullptr) page = page < ns ? selrow[page] : -1;  // kept page -> logical page
     // a logical page outside the context takes no part
-    vblk = (page >= 0 && page < max_blocks && page * bs < n_real) ? table[page] : -1;
+    vblk = (page >= 0 && page < src.max_blocks && page * bs < n_real) ? table[page] : -1;
   };
   auto load_tile = [&](int64_t j, Tile& x) -> bool {
     const int64_t t0 = w_first + 64 * j;
     const int o0 = (int)(t0 % bs);
     const int blk = __builtin_amdgcn_readlane(vblk, (int)(j & 63));
-    if (blk < 0 || blk >= num_blocks) return false;  // tokens of an invalid block take no part
+    if (blk < 0 || blk >= src.num_blocks) return false;  // tokens of an invalid block take no part
     const int64_t pg = (int64_t)blk * Hkv + hk;
-    const auto rk = make_rsrc(k_cache + pg * bs * D, (uint32_t)(bs * D * 2));
-    const auto rv = make_rsrc(v_cache + pg * D * bs, (uint32_t)(D * bs * 2));
+    const auto rk = make_rsrc(src.k + pg * bs * D, (uint32_t)(bs * D * 2));
+    const auto rv = make_rsrc(src.v + pg * D * bs, (uint32_t)(D * bs * 2));
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks)  // chunk 4 ks + grp of token o0 + col: 1 KiB contiguous per load
       x.k[ks] = gload16(rk, (uint32_t)(((4 * ks + grp) * bs + o0 + col) * 16));
@@ -279,8 +300,8 @@ void fa_paged_decode_kernel(
       }
       if (d == 0 && lse != nullptr) lse[row] = lse_n;
     } else {
-      part_o[(row * n_splits + s) * D + d] = val;
-      if (d == 0) part_lse[row * n_splits + s] = lse_n;
+      part_o[(row * n_splits + s_all) * D + d] = val;
+      if (d == 0) part_lse[row * n_splits + s_all] = lse_n;
     }
   }
 }
@@ -333,21 +354,40 @@ hipError_t launch_reshape_and_cache(const CacheArgs& a) {
   }
 }
 
+static KvSrc kv_src(const DecodeSource& d) {
+  KvSrc k{};
+  k.k = (const uint16_t*)d.k_cache;
+  k.v = (const uint16_t*)d.v_cache;
+  k.tables = d.block_tables;
+  k.lens = d.context_lens;
+  k.sel = d.selected;
+  k.nsel = d.n_selected;
+  k.num_blocks = d.num_blocks;
+  k.chunk = d.chunk;
+  k.bs = (int)d.block_size;
+  k.max_blocks = (int)d.max_blocks;
+  k.topk = (int)d.topk;
+  k.n_splits = d.n_splits;
+  return k;
+}
+
 template <int D, typename T, typename OT>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
   const int G = (int)(a.H / a.Hkv);
-  const int64_t grid = a.B * a.Hkv * ((G + 15) / 16) * a.n_splits;
+  const KvSrc s0 = kv_src(a.src[0]);
+  KvSrc s1 = a.n_sources > 1 ? kv_src(a.src[1]) : s0;
+  if (a.n_sources < 2) s1.n_splits = 0;  // no workgroup takes the second source
+  const int n_splits = s0.n_splits + s1.n_splits;
+  const int64_t grid = a.B * a.Hkv * ((G + 15) / 16) * n_splits;
   float* part_o = a.workspace;
-  float* part_lse = a.workspace + a.B * a.H * a.n_splits * a.D;
+  float* part_lse = a.workspace + a.B * a.H * n_splits * a.D;
   hipLaunchKernelGGL((fa_paged_decode_kernel<D, T, OT>), dim3((unsigned)grid), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.block_tables,
-                     a.context_lens, a.o, a.lse, part_o, part_lse, (int)a.H, (int)a.Hkv, G, (int)a.block_size,
-                     a.num_blocks, (int)a.max_blocks, a.n_splits, a.chunk, a.scale * kLog2e, a.selected,
-                     a.n_selected, (int)a.topk);
+                     (const uint16_t*)a.q, s0, s1, a.o, a.lse, part_o, part_lse, (int)a.H, (int)a.Hkv, G,
+                     a.scale * kLog2e);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_splits == 1) return e;
+  if (e != hipSuccess || n_splits == 1) return e;
   hipLaunchKernelGGL((fa_paged_decode_combine_kernel<D, T, OT>), dim3((unsigned)(a.B * a.H)), dim3(D), 0, a.stream,
-                     part_o, part_lse, a.o, a.lse, a.n_splits);
+                     part_o, part_lse, a.o, a.lse, n_splits);
   return hipGetLastError();
 }
 template <int D, typename T>

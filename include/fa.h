@@ -363,6 +363,54 @@ int fa_paged_decode_sparse(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t
                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Decode attention over one or two KV sources normalised together (the page
+ * "在 4 张 A100 上部署 DeepSeek-V4-Flash-0731" (BiumBiu), section 7.5: one
+ * sparse attention kernel serves a single source (the sliding-window pool)
+ * or two sources (sliding-window and compressed pools, section 7.3) whose
+ * pages form one logical set under a single softmax denominator).
+ *
+ * A source is a paged cache in the layouts above with its own block table,
+ * context lengths and block size; it contributes every token of each
+ * context (n_selected == NULL) or the tokens of its kept logical pages
+ * (n_selected != NULL: as for fa_paged_decode_sparse, the last page of a
+ * context cut at the context's end).  For query head h of sequence b the
+ * attended set is the concatenation of the sources' tokens for key/value
+ * head h / (H / Hkv): O = softmax(scale q K^T) V and lse = ln sum exp over
+ * that set.  Every source has the same Hkv, D and dtype; q, o, lse as for
+ * fa_paged_decode.  The struct is read on the host during the call only.
+ *   max_context_len : dense source: host bound on its context lengths (sizes
+ *                     its split only, as for fa_paged_decode); ignored for a
+ *                     sparse source (topk * block_size is used);
+ *   selected        : (B, Hkv, topk) int32 ascending kept pages, or NULL
+ *                     (only with topk == 0) for a sparse source; must be
+ *                     NULL for a dense one.
+ * n_sources is 1 or 2.  workspace: fa_paged_decode_sources_workspace_bytes
+ * of the same arguments (0 bytes: NULL is fine), 16-byte aligned.  A query
+ * head with no token in any source gets O = 0 and lse = -inf.  Every split of
+ * every source writes a partial (O, lse) pair and one combine merges them, so
+ * the sources share one maximum and one denominator.
+ */
+typedef struct fa_kv_source {
+  const void* k_cache;          /* (num_blocks, Hkv, D/8, block_size, 8) dtype */
+  const void* v_cache;          /* (num_blocks, Hkv, D, block_size) dtype */
+  const int32_t* block_tables;  /* DEVICE (B, max_blocks_per_seq) */
+  const int32_t* context_lens;  /* DEVICE (B) */
+  int64_t block_size;           /* multiple of 16 in [16, 1024] */
+  int64_t num_blocks;
+  int64_t max_blocks_per_seq;
+  int64_t max_context_len;
+  const int32_t* selected;      /* DEVICE (B, Hkv, topk) or NULL */
+  const int32_t* n_selected;    /* DEVICE (B, Hkv), or NULL for a dense source */
+  int64_t topk;
+} fa_kv_source;
+size_t fa_paged_decode_sources_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t D,
+                                               int n_sources, const fa_kv_source* sources);
+int fa_paged_decode_sources(int64_t B, int64_t H, int64_t Hkv, int64_t D, int dtype,
+                            int o_dtype, const void* q, int n_sources,
+                            const fa_kv_source* sources, void* o, float* lse, float scale,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Device facts used for launch sizing, for the current device: compute
  * units, and the persistent grid fa_bwd_dkdv uses for (D, dtype) when
  * num_programs is 0.  Either output pointer may be NULL.

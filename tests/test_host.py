@@ -251,3 +251,42 @@ def test_paged_and_quest_argument_errors(fa):
     sp = lambda topk=8, s=I4: lib.fa_paged_decode_sparse(  # noqa: E731
         2, 8, 2, 128, 16, 100, 50, topk, 0, 0, P, P, P, I4, I4, s, I4, P, P, 0.1, None, 0, None)
     assert sp(topk=-1) == 1 and sp(s=None) == 1
+
+
+@_NO_GPU
+def test_two_source_decode_argument_errors(fa):
+    """Argument rules of fa_paged_decode_sources; every call fails validation
+    (or is empty) before any HIP call."""
+    from exact_attention_03_amd._lib import KvSource
+
+    lib = fa.lib()
+    I4 = ctypes.c_void_p(0x30000)
+
+    def src(bs=16, nb=100, mxb=50, mctx=800, sel=None, nsel=None, topk=0, kc=P, bt=I4):
+        return KvSource(kc, P, bt, I4, bs, nb, mxb, mctx, sel, nsel, topk)
+
+    def call(srcs, n=None, B=2, H=8, Hkv=2, ws=None, wsb=0):
+        arr = (KvSource * max(1, len(srcs)))(*srcs)
+        n = len(srcs) if n is None else n
+        return lib.fa_paged_decode_sources(B, H, Hkv, 128, 0, 0, P, n, arr, P, P, 0.1, ws, wsb, None)
+
+    dense, sparse = src(), src(sel=I4, nsel=I4, topk=8)
+    assert call([dense], n=0) == 1 and call([dense, sparse], n=3) == 1
+    assert lib.fa_paged_decode_sources(2, 8, 2, 128, 0, 0, P, 1, None, P, P, 0.1, None, 0, None) == 1
+    assert call([dense, src(bs=8)]) == 2 and "source 1" in fa.last_error()
+    assert call([src(sel=I4)]) == 1                                  # selected without n_selected
+    assert call([src(sel=None, nsel=I4, topk=4)]) == 1               # topk > 0 needs selected
+    assert call([dense, src(kc=None)]) == 1 and call([src(bt=ctypes.c_void_p(0x30002))]) == 1
+    assert call([src(mxb=-1)]) == 1
+    assert call([dense, sparse], B=0) == 0                           # empty batch
+    assert call([dense, src(kc=None)], B=0) == 0                     # pointers unread when empty
+    # workspace: the splits of both sources together
+    one = lib.fa_paged_decode_sources_workspace_bytes(1, 8, 1, 128, 1, (KvSource * 1)(src(mctx=10000)))
+    assert one == lib.fa_paged_decode_workspace_bytes(1, 8, 1, 128, 10000) > 0
+    two = lib.fa_paged_decode_sources_workspace_bytes(1, 8, 1, 128, 2, (KvSource * 2)(src(mctx=10000),
+                                                                                      src(mctx=5000)))
+    assert two > one
+    # two one-split sources still need a combine: workspace for 2 splits
+    small = (KvSource * 2)(src(mctx=64), src(sel=I4, nsel=I4, topk=2))
+    assert lib.fa_paged_decode_sources_workspace_bytes(1, 8, 1, 128, 2, small) == 8 * 2 * 129 * 4
+    assert call([src(mctx=64), src(sel=I4, nsel=I4, topk=2)], B=1, Hkv=1) == 1 and "workspace" in fa.last_error()
