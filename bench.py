@@ -415,7 +415,7 @@ def decode_bytes(w, lens) -> float:
 def _oracle_decode(args):
     import oracle
 
-    q, kc, vc, tables, lens, scale, topk = args
+    q, kc, vc, tables, lens, scale, topk, win = args
     if not topk:
         oracle.paged_decode(q, kc, vc, tables, lens, scale)
         return len(lens)
@@ -429,13 +429,32 @@ def _oracle_decode(args):
             mn, mx = oracle.quest_page_minmax(kc, tables[b], int(lens[b]), hk)
             row.append(oracle.quest_select(oracle.quest_scores(q[b, hk * G:(hk + 1) * G], mn, mx), topk))
         selected.append(row)
-    oracle.quest_sparse_decode(q, kc, vc, tables, lens, selected, scale)
+    if win is None:
+        oracle.quest_sparse_decode(q, kc, vc, tables, lens, selected, scale)
+    else:  # the window pool and the kept pages under one softmax
+        pool = {"k_cache": kc, "v_cache": vc, "block_tables": tables, "context_lens": lens, "selected": selected}
+        window = {"k_cache": win[0], "v_cache": win[1], "block_tables": win[2], "context_lens": win[3]}
+        oracle.decode_over_sources(q, [window, pool], scale)
     return len(lens)
 
 
-def decode_cpu_baseline(w, cpu, n_seq: int, workers: int):
+def _subset_pages(cache, c):
+    """The pages of sequences c of a (q, k_cache, v_cache, tables, lens)
+    cache, renumbered: (k_cache, v_cache, tables, lens) as float32 / int32."""
+    import numpy as np
+
+    _, kc, vc, tables, lens = cache
+    t = tables[c].numpy()
+    used = sorted({int(x) for x in t.flatten() if x >= 0})
+    remap = {b: i for i, b in enumerate(used)}
+    t2 = np.vectorize(lambda x: remap.get(int(x), -1))(t).astype(np.int32)
+    return kc[used].float().numpy(), vc[used].float().numpy(), t2, lens[c].numpy()
+
+
+def decode_cpu_baseline(w, cpu, n_seq: int, workers: int, window=None):
     """The paged-decode oracle on the first n_seq sequences (one process per
-    chunk of sequences, one BLAS thread each), in the same GB/s unit."""
+    chunk of sequences, one BLAS thread each), in the same GB/s unit; with a
+    window pool (its inputs), the two-source oracle."""
     import concurrent.futures as cf
     import multiprocessing as mp
 
@@ -449,12 +468,8 @@ def decode_cpu_baseline(w, cpu, n_seq: int, workers: int):
     for c in np.array_split(np.arange(n_seq), max(1, min(workers, n_seq))):
         if not len(c):
             continue
-        t = tables[c].numpy()
-        used = sorted({int(x) for x in t.flatten() if x >= 0})
-        remap = {b: i for i, b in enumerate(used)}
-        t2 = np.vectorize(lambda x: remap.get(int(x), -1))(t).astype(np.int32)
-        jobs.append((q[c].float().numpy(), kc[used].float().numpy(), vc[used].float().numpy(), t2,
-                     lens[c].numpy(), w.scale, w.topk))
+        jobs.append((q[c].float().numpy(), *_subset_pages(cpu, c), w.scale, w.topk,
+                     _subset_pages(window, c) if window is not None else None))
     saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
     for k in saved:
         os.environ[k] = "1"
@@ -473,6 +488,9 @@ def decode_cpu_baseline(w, cpu, n_seq: int, workers: int):
     nbytes = sum(quest_bytes(w, sub)) if w.topk else decode_bytes(w, sub)
     what = ("query-aware oracle (page min / max, scores, Top-K, attention over the kept pages)" if w.topk
             else "paged-decode oracle (token-by-token gather through the block table, plain softmax)")
+    if window is not None:
+        what = ("query-aware oracle (page min / max, scores, Top-K) and the two-source oracle (window pool and kept "
+                "pages under one softmax)")
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": len(jobs), "kind": "oracle",
             "sample": (f"fp64 numpy {what} on {done} of {w.B} sequences ({int(sub.sum())} context tokens) of the "
                        f"same seeded workload, {len(jobs)} processes x 1 BLAS thread, wall {dt:.2f} s (process "
@@ -484,7 +502,9 @@ def quest_bytes(w, lens):
     the block-table entries and the min / max of every page of each context
     and writes the kept page lists; the sparse decode reads the kept pages'
     valid K and V tokens, q, the lists and the table entries of the kept pages,
-    and writes O (16-bit) and lse.  Returns (selection bytes, decode bytes)."""
+    and writes O (16-bit) and lse; with a window pool it also reads the
+    window's K and V tokens and table entries.  Returns (selection bytes,
+    decode bytes)."""
     import numpy as np
 
     lens = np.asarray(lens, dtype=np.int64)
@@ -499,6 +519,9 @@ def quest_bytes(w, lens):
         kept_tokens += k * w.block_size - (w.block_size * p - n if k == p else 0)
     dec = (kept_tokens * w.Hkv * w.D * 2 * e + w.B * w.H * w.D * e * 2 + w.B * w.H * 4
            + w.B * w.Hkv * (w.topk + 1) * 4 + float(np.minimum(pages, w.topk).sum()) * w.Hkv * 4)
+    if w.window:
+        wpages = -(-w.window // w.block_size)
+        dec += len(lens) * (float(w.window) * w.Hkv * w.D * 2 * e + wpages * w.Hkv * 4)
     return sel, dec
 
 
@@ -511,6 +534,8 @@ def run_quest(args):
 
     import exact_attention_03_amd as fa
 
+    from exact_attention_03_amd._lib import KvSource
+
     w = workloads.DECODE_WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -518,6 +543,7 @@ def run_quest(args):
     q, kc, vc, tables, lens = (t.to(dev) for t in cpu)
     lens_np = cpu[4].numpy().astype(np.int64)
     kmeta = fa.quest_page_minmax(kc, tables, lens)
+    wcpu = workloads.make_decode_inputs(w.window_pool()) if w.window else None
     sel = torch.empty((w.B, w.Hkv, w.topk), dtype=torch.int32, device=dev)
     nsel = torch.empty((w.B, w.Hkv), dtype=torch.int32, device=dev)
     o = torch.empty((w.B, w.H, w.D), dtype=q.dtype, device=dev)
@@ -525,9 +551,19 @@ def run_quest(args):
     L = fa.lib()
     code = fa._dtype_code(q)
     nb, mxb = kc.shape[0], tables.shape[1]
-    ws_bytes = L.fa_paged_decode_workspace_bytes(w.B, w.H, w.Hkv, w.D, w.topk * w.block_size)
-    ws = torch.empty((max(1, ws_bytes // 4),), dtype=torch.float32, device=dev)
     P = lambda t: t.data_ptr()  # noqa: E731
+    if w.window:
+        # source 0: the window pool attended whole; source 1: the kept pages
+        _, wkc, wvc, wtab, wlens = (t.to(dev) for t in wcpu)
+        srcs = (KvSource * 2)(
+            KvSource(P(wkc), P(wvc), P(wtab), P(wlens), w.block_size, wkc.shape[0], wtab.shape[1], w.window,
+                     None, None, 0),
+            KvSource(P(kc), P(vc), P(tables), P(lens), w.block_size, nb, mxb, 0, P(sel), P(nsel), w.topk))
+        ws_bytes = L.fa_paged_decode_sources_workspace_bytes(w.B, w.H, w.Hkv, w.D, 2, srcs)
+    else:
+        ws_bytes = L.fa_paged_decode_workspace_bytes(w.B, w.H, w.Hkv, w.D, w.topk * w.block_size)
+    ws = torch.empty((max(1, ws_bytes // 4),), dtype=torch.float32, device=dev)
+    dec_name = "fa_paged_decode_sources" if w.window else "fa_paged_decode_sparse"
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
 
@@ -542,9 +578,13 @@ def run_quest(args):
                                P(lens), P(sel), P(nsel), sp), "fa_quest_select")
         if ev is not None:
             ev[1].record(stream)
-        call(L.fa_paged_decode_sparse(w.B, w.H, w.Hkv, w.D, w.block_size, nb, mxb, w.topk, code, code, P(q), P(kc),
-                                      P(vc), P(tables), P(lens), P(sel), P(nsel), P(o), P(lse), w.scale, P(ws),
-                                      ws_bytes, sp), "fa_paged_decode_sparse")
+        if w.window:
+            call(L.fa_paged_decode_sources(w.B, w.H, w.Hkv, w.D, code, code, P(q), 2, srcs, P(o), P(lse), w.scale,
+                                           P(ws), ws_bytes, sp), dec_name)
+        else:
+            call(L.fa_paged_decode_sparse(w.B, w.H, w.Hkv, w.D, w.block_size, nb, mxb, w.topk, code, code, P(q),
+                                          P(kc), P(vc), P(tables), P(lens), P(sel), P(nsel), P(o), P(lse), w.scale,
+                                          P(ws), ws_bytes, sp), dec_name)
         if ev is not None:
             ev[2].record(stream)
 
@@ -563,11 +603,16 @@ def run_quest(args):
     sel_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     sel_b, dec_b = quest_bytes(w, lens_np)
-    kern = {"fa_quest_select": (sel_ms, sel_b), "fa_paged_decode_sparse": (dec_ms, dec_b)}
+    kern = {"fa_quest_select": (sel_ms, sel_b), dec_name: (dec_ms, dec_b)}
     dom = max(kern, key=lambda k: kern[k][0])
     ach = kern[dom][1] / (kern[dom][0] * 1e-3) / 1e9
+    metric = ("query-aware sparse decode (page selection + attention over the kept pages) HBM GB/s on 1 MI355X"
+              if not w.window else
+              "two-source sparse decode (page selection + attention over a sliding-window pool and the kept pages "
+              "under one softmax) HBM GB/s on 1 MI355X")
+    window_txt = f", plus a window pool of {w.window} tokens per sequence" if w.window else ""
     out = {
-        "metric": "query-aware sparse decode (page selection + attention over the kept pages) HBM GB/s on 1 MI355X",
+        "metric": metric,
         "value": round((sel_b + dec_b) / (ms_step * 1e-3) / 1e9, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -581,9 +626,9 @@ def run_quest(args):
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} sequences, contexts {int(lens_np.min())}..{int(lens_np.max())} "
                                f"tokens, H={w.H} Hkv={w.Hkv} D={w.D} pages of {w.block_size} tokens, {w.topk} pages "
-                               f"kept per context, {w.dtype}",
+                               f"kept per context{window_txt}, {w.dtype}",
                    "B": w.B, "H": w.H, "Hkv": w.Hkv, "D": w.D, "block_size": w.block_size, "topk": w.topk,
-                   "seed": w.seed},
+                   "window": w.window, "seed": w.seed},
         "breakdown": {"select_ms": round(sel_ms, 4), "sparse_decode_ms": round(dec_ms, 4),
                       "select_GB/s": round(sel_b / (sel_ms * 1e-3) / 1e9, 1),
                       "sparse_decode_GB/s": round(dec_b / (dec_ms * 1e-3) / 1e9, 1)},
@@ -593,7 +638,7 @@ def run_quest(args):
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = decode_cpu_baseline(w, cpu, args.cpu_decode_seqs, args.cpu_workers)
+        out["cpu_baseline"] = decode_cpu_baseline(w, cpu, args.cpu_decode_seqs, args.cpu_workers, wcpu)
     return out
 
 

@@ -185,6 +185,7 @@ class DecodeWorkload:
     hi: int            # longest context
     dtype: str
     topk: int = 0      # pages kept per (sequence, key/value head) by the query-aware selection; 0 = all
+    window: int = 0    # tokens per sequence of a second, sliding-window pool attended whole; 0 = none
 
     @property
     def scale(self) -> float:
@@ -193,6 +194,12 @@ class DecodeWorkload:
     def lengths(self):
         rng = np.random.default_rng(self.seed)
         return rng.integers(self.lo, self.hi + 1, size=self.B)
+
+    def window_pool(self) -> "DecodeWorkload":
+        """The sliding-window pool: its own cache, every sequence holding
+        `window` tokens (drawn from seed + 1)."""
+        return DecodeWorkload(self.name + "_window", self.seed + 1, self.B, self.H, self.Hkv, self.D,
+                              self.block_size, self.window, self.window, self.dtype)
 
     def layout(self):
         """(context_lens int32 (B,), block_tables int32 (B, max_blocks), num_blocks)."""
@@ -217,6 +224,10 @@ DECODE_WORKLOADS = {
     "decode_gqa_bf16": DecodeWorkload("decode_gqa_bf16", 11, 64, 32, 8, 128, 16, 512, 16000, "bf16"),
     # the same batch and cache with 64 pages (1024 tokens) kept per context by the query-aware selection
     "quest_gqa_bf16": DecodeWorkload("quest_gqa_bf16", 11, 64, 32, 8, 128, 16, 512, 16000, "bf16", 64),
+    # two sources under one softmax: the same 64 kept pages plus a sliding-window pool of the
+    # last 1024 tokens of every sequence, held in a cache of its own
+    "window_quest_gqa_bf16": DecodeWorkload("window_quest_gqa_bf16", 11, 64, 32, 8, 128, 16, 512, 16000, "bf16",
+                                            64, 1024),
 }
 
 
