@@ -46,6 +46,9 @@ KERNEL_SOURCES = {
     "fa_bwd_dkdv": ("fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_schedule.h"),
     "fa_bwd_dq": ("fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_schedule.h"),
     "fa_paged_decode": ("fa_paged.hip", "fa_device.h", "fa_kernels.h"),
+    "fa_paged_decode_sparse": ("fa_paged.hip", "fa_device.h", "fa_kernels.h"),
+    "fa_paged_decode_sources": ("fa_paged.hip", "fa_device.h", "fa_kernels.h"),
+    "fa_quest_select": ("fa_quest.hip", "fa_device.h", "fa_kernels.h"),
 }
 
 
@@ -571,6 +574,16 @@ def run_quest(args):
         if st != 0:
             raise fa.FAError(st, name, fa.last_error())
 
+    if args.calib_copy_mib > 0:
+        # A plain device copy of known size, for scaling HBM counters.
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
@@ -633,7 +646,8 @@ def run_quest(args):
                       "select_GB/s": round(sel_b / (sel_ms * 1e-3) / 1e9, 1),
                       "sparse_decode_GB/s": round(dec_b / (dec_ms * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
+                     "frac": round(ach / PEAK_HBM_GBS, 4),
+                     "traffic": stored_traffic(dom, w.name) if dom in KERNEL_SOURCES else None, "kernel": dom,
                      "algorithmic": {"amount": kern[dom][1], "unit": "byte", "per_launch": True}},
         "cpu_baseline": None,
     }
