@@ -84,6 +84,36 @@ def kernel_work(w, o_bytes: int):
     }
 
 
+def _computed_pairs(n: int, bq: int, bk: int, causal: bool) -> int:
+    """(query, key) pairs a kernel computes for one head of n tokens when it
+    works in blocks of bq queries x bk keys and, with the causal mask, skips
+    only the blocks whose keys all follow the block's last query."""
+    n_kt = -(-n // bk)
+    total = 0
+    for q0 in range(0, n, bq):
+        nt = min((q0 + bq - 1) // bk + 1, n_kt) if causal else n_kt
+        total += bq * bk * nt
+    return total
+
+
+def executed_over_counted(w) -> dict:
+    """Matrix work each kernel executes over the work it is credited with.
+
+    fa_fwd: 32-query blocks (one per wave) x key tiles of 64 (D = 64) or 32
+      keys; at D = 256 both waves of a pair run the score product (1.5x).
+    fa_bwd_dq: the same blocks, three products (S, dP recomputed; dS K) for
+      the one counted.
+    fa_bwd_dkdv: 32-key x 32-query blocks, the four counted products.
+    Counted pairs are n^2 (n^2 / 2 causal), as in the FLOP convention."""
+    lengths = list(w.lengths) if w.varlen else [w.N]
+    bk = 64 if w.D == 64 else 32
+    counted = sum(n * n / (2 if w.causal else 1) for n in lengths)
+    fwd = sum(_computed_pairs(n, 32, bk, w.causal) for n in lengths) / counted
+    dkdv = sum(_computed_pairs(n, 32, 32, w.causal) for n in lengths) / counted
+    return {"fa_fwd": round(fwd * (1.5 if w.D == 256 else 1.0), 4), "fa_bwd_dq": round(3 * fwd, 4),
+            "fa_bwd_dkdv": round(dkdv, 4)}
+
+
 def sources_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
@@ -308,6 +338,9 @@ def run(args):
         for i, name in enumerate(KERNELS):
             per[name].append(e[i].elapsed_time(e[i + 1]))
     avg = {n: sum(x) / len(x) for n, x in per.items()}
+    step_times = sorted(e[0].elapsed_time(e[-1]) for e in evs)  # first launch to last completion
+    spread = {"median": round(step_times[len(step_times) // 2], 4), "min": round(step_times[0], 4),
+              "max": round(step_times[-1], 4)}
 
     # The standalone Delta pass (fa_bwd_preprocess), outside the step (the
     # step's dQ pass computes the same statistics): its HBM rate.
@@ -336,6 +369,7 @@ def run(args):
     bwd_ms = avg["fa_bwd_dq"] + avg["fa_bwd_dkdv"]
     value = 3.5 * ff / (ms_step * 1e-3) / 1e12
     work = kernel_work(w, o.element_size())
+    ratio = executed_over_counted(w)
     kern = {}
     for name in KERNELS:
         bound, amount, unit = work[name]
@@ -343,7 +377,8 @@ def run(args):
         if bound == "mfma":
             ach = amount / t / 1e12
             kern[name] = {"ms": round(avg[name], 4), "bound": "mfma", "TFLOP/s": round(ach, 1),
-                          "frac": round(ach / PEAK_MFMA_F16_TFLOPS, 4)}
+                          "frac": round(ach / PEAK_MFMA_F16_TFLOPS, 4), "executed_over_counted": ratio[name],
+                          "executed_TFLOP/s": round(ach * ratio[name], 1)}
         else:
             ach = amount / t / 1e9
             kern[name] = {"ms": round(avg[name], 4), "bound": "hbm", "GB/s": round(ach, 1),
@@ -382,6 +417,7 @@ def run(args):
                    "Z": Z, "H": H, "Hkv": Hkv, "N": N, "D": D, "causal": bool(w.causal), "seed": w.seed},
         "frac_of_peak": round(value / PEAK_MFMA_F16_TFLOPS, 4),
         "breakdown": {
+            "step_ms": spread,
             "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
             "fwd_TFLOP/s": round(ff / (fwd_ms * 1e-3) / 1e12, 1),
             "bwd_TFLOP/s": round(2.5 * ff / (bwd_ms * 1e-3) / 1e12, 1),
