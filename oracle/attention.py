@@ -9,7 +9,7 @@ materialises the full N x N score and probability matrices, which is precisely
 what the tiled method avoids.  The only library primitives used are matrix
 products, exp, log and reductions.
 
-Readings of points the page leaves open (each is listed in the design doc):
+Readings of points the page leaves open:
 
 * layout: q, k, v, do are (..., N, D) arrays; leading axes are independent heads;
 * self-attention with one key/value head per query head, N_q = N_k = N;
@@ -117,9 +117,9 @@ def loss_sum_o_do(q, k, v, do, scale, causal=False):
 # section "GQA Paged Attention": the number of query heads is an integer
 # multiple of the number of key/value heads, and consecutive query heads share
 # one key/value head (grouped-query attention; one KV head for all query
-# heads is the multi-query case).  Reading of the grouping (listed in
-# the design doc): with G = Hq / Hkv, query head h uses key/value head h // G, the
-# usual contiguous grouping.
+# heads is the multi-query case).  Reading of the grouping: with
+# G = Hq / Hkv, query head h uses key/value head h // G, the usual contiguous
+# grouping.
 
 
 def gqa_kv_head(h, n_q_heads, n_kv_heads):
@@ -177,8 +177,8 @@ def attention_backward_gqa(q, k, v, do, scale, causal=False):
 # ---------------------------------------------------------------- variable-length batches
 # [Serving-Ascend], sections "GQA Paged Attention" and the integration
 # discussion before it: a batch holds sequences of different real lengths
-# (context_lens), and tokens past a sequence's length take no part.  Reading
-# (listed in the design doc): the sequences of a batch are packed one after the
+# (context_lens), and tokens past a sequence's length take no part.  Reading:
+# the sequences of a batch are packed one after the
 # other along the token axis, sequence b occupying tokens cu_seqlens[b] ..
 # cu_seqlens[b+1]-1 of every head (head-major packed layout: q is (H, T, D),
 # k and v are (Hkv, T, D), T = cu_seqlens[-1]); each sequence is an

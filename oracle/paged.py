@@ -10,7 +10,7 @@ slot are skipped; attention reads the pages of a sequence through its block
 table, uses the sequence's context length, masks the invalid tokens of the
 last block, and lets several query heads share one key/value head.
 
-Readings of what it leaves open (listed in the design doc):
+Readings of what it leaves open:
 
 * cache layouts: k_cache is (num_blocks, Hkv, D/8, block_size, 8), one page
   of a key/value head holding its keys in chunks of 8 channels, chunk-major

@@ -12,7 +12,7 @@ al., "Quest: Query-Aware Sparsity for Efficient Long-Context LLM Inference",
 the page's score for a query q is sum_d max(q_d * min_d, q_d * max_d), an
 upper bound of q . k over the page's keys.
 
-Readings (listed in DESIGN.md):
+Readings of what the page leaves open:
 
 * the min / max run over the page's valid tokens (those inside the context);
 * a key/value head selects one set of pages for all G query heads sharing

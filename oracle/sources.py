@@ -8,7 +8,7 @@ Q K^T, online softmax, P V) that serves either a single source (the
 sliding-window pool) or two sources, whose pages together form one logical
 sparse set normalised by one softmax denominator.
 
-Readings (listed in DESIGN.md):
+Readings of what the page leaves open:
 
 * a source is a paged cache in the layouts of ``paged.py`` with its own block
   table and context lengths; it contributes every valid token of the
