@@ -149,6 +149,28 @@ def stored_traffic(kernel: str, workload: str):
         return None
 
 
+def stored_clock(kernel: str, workload: str):
+    """Engine clock (GHz) measured during the kernel, from a committed
+    rocprofv3 GRBM summary (profiles/clock_fwd_bwd_<workload>.txt), or None
+    when absent or when the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"clock_fwd_bwd_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if "=" in line:
+                a, b = line.split("=", 1)
+                kv[a.strip()] = b.strip()
+    if kv.get(f"{kernel}_hash") != sources_hash(kernel):
+        return None
+    try:
+        return float(kv[f"{kernel}_ghz"])
+    except (KeyError, ValueError):
+        return None
+
+
 # ------------------------------------------------------------------ CPU baseline
 def _oracle_heads(args):
     """Worker: fp64 oracle forward + backward over a list of (q, k, v, do) problems."""
@@ -370,6 +392,7 @@ def run(args):
     value = 3.5 * ff / (ms_step * 1e-3) / 1e12
     work = kernel_work(w, o.element_size())
     ratio = executed_over_counted(w)
+    n_cu = fa.device_info(D)[0]
     kern = {}
     for name in KERNELS:
         bound, amount, unit = work[name]
@@ -379,6 +402,12 @@ def run(args):
             kern[name] = {"ms": round(avg[name], 4), "bound": "mfma", "TFLOP/s": round(ach, 1),
                           "frac": round(ach / PEAK_MFMA_F16_TFLOPS, 4), "executed_over_counted": ratio[name],
                           "executed_TFLOP/s": round(ach * ratio[name], 1)}
+            clk = stored_clock(name, w.name)
+            if clk is not None:
+                # the dense fp16 rate at the clock the kernel actually ran at: CUs x clock x 4096
+                peak_clk = n_cu * clk * 4096 / 1e3
+                kern[name].update({"observed_clock_GHz": clk, "peak_at_observed_clock_TFLOP/s": round(peak_clk, 1),
+                                   "frac_at_observed_clock": round(ach / peak_clk, 4)})
         else:
             ach = amount / t / 1e9
             kern[name] = {"ms": round(avg[name], 4), "bound": "hbm", "GB/s": round(ach, 1),
