@@ -88,6 +88,54 @@ def test_small_shapes_all_heads(shape, dtype, causal):
     _compare(w, cpu, outs, heads, f"{shape} {dtype} causal={causal}")
 
 
+# Error levels these workloads reach (fp32 O max-abs, worst of the dQ / dK / dV
+# normwise errors, on the sampled heads).  A result inside the tolerances but
+# ten times worse than these points to a lost precision (a dropped fp32
+# accumulation, a wrong rounding), so the check below also holds it to
+# 10 x these levels.
+EXPECTED = {
+    "tiny": (1.6e-4, 3.0e-4),
+    "d64": (8.0e-5, 3.0e-4),
+    "d128_causal": (2.9e-4, 3.3e-4),
+    "d256_bf16": (4.1e-4, 2.4e-3),
+    "long_causal_bf16": (3.3e-3, 3.2e-3),
+}
+
+
+def _full_size_invariants(w, gpu, outs, label):
+    """Checks over every head, without the oracle, with bounds from the
+    arithmetic (u = unit roundoff of the input type: 2^-11 fp16, 2^-8 bf16):
+
+    * sum_j dV_j = sum_i dO_i per head (the rows of P sum to 1): P is rounded
+      to the input type before the product and dV on output, so per channel
+      |sum dV - sum dO| <= u (sum |dO| + sum |dV|); twice that is allowed;
+    * every O row is a convex combination of the value rows it sees (all of
+      them, or rows 0..i when causal): per channel between their minimum and
+      maximum, up to 2 u max|v| (the rounded P's weights sum to 1 + O(u)).
+    A skipped key unit, query tile or head breaks one of them."""
+    import torch
+
+    q, k, v, do = gpu
+    o32, _, _, _, _, _, dv = outs
+    u = 2.0 ** -8 if w.dtype == "bf16" else 2.0 ** -11
+    dv64, do64 = dv.double(), do.double()
+    defect = (dv64.sum(dim=2) - do64.sum(dim=2)).abs()
+    bound = 2 * u * (do64.abs().sum(dim=2) + dv64.abs().sum(dim=2)) + 1e-6
+    ratio = float((defect / bound).max())
+    del dv64, do64
+    vf = v.float()
+    if w.causal:
+        hi, lo = torch.cummax(vf, dim=2).values, torch.cummin(vf, dim=2).values
+    else:
+        hi, lo = vf.amax(dim=2, keepdim=True), vf.amin(dim=2, keepdim=True)
+    slack = 2 * u * vf.abs().amax(dim=(2, 3), keepdim=True)
+    outside = float(torch.clamp(torch.maximum(o32 - hi, lo - o32) - slack, min=0).max())
+    log(f"{label}: full-size sum(dV) - sum(dO) at {ratio:.3f} of its bound | O outside the V hull by {outside:.2e}")
+    assert ratio <= 1.0, f"{label}: sum_j dV_j != sum_i dO_i beyond the rounding bound ({ratio})"
+    assert outside == 0.0, f"{label}: an O row leaves the convex hull of its value rows"
+    assert bool(torch.isfinite(o32).all()), f"{label}: non-finite O"
+
+
 @pytest.mark.parametrize("name", ["tiny", "d64", "d128_causal", "d256_bf16", "long_causal_bf16"])
 def test_workload_parity(name):
     import torch
@@ -97,7 +145,11 @@ def test_workload_parity(name):
     cpu, gpu = device_inputs(w)
     outs = _run(w, gpu)
     heads = sample_heads(w, 2 if w.N > 4096 else 3)
-    _compare(w, cpu, outs, heads, name)
+    err_o, grads = _compare(w, cpu, outs, heads, name)
+    lvl_o, lvl_g = EXPECTED[name]
+    assert err_o <= 10 * lvl_o, f"{name}: O error {err_o:.2e} is over 10x its usual {lvl_o:.1e}"
+    assert max(grads.values()) <= 10 * lvl_g, f"{name}: gradient error {grads} over 10x its usual {lvl_g:.1e}"
+    _full_size_invariants(w, gpu, outs, name)
     # determinism: a second backward is bitwise identical
     fa = _fa()
     q, k, v, do = gpu
