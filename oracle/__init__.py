@@ -35,4 +35,4 @@ from .attention import (  # noqa: F401
 )
 from .paged import gather_context, paged_decode, reshape_and_cache  # noqa: F401
 from .quest import quest_page_minmax, quest_scores, quest_select, quest_sparse_decode  # noqa: F401
-from .sources import decode_over_sources, source_tokens  # noqa: F401
+from .sources import attention_over_sources, decode_over_sources, source_tokens  # noqa: F401

@@ -18,7 +18,11 @@ Readings of what the page leaves open:
   token sets (entries of different sources are different entries, even when
   they hold the same key), and the output is the plain softmax of
   [FA-Ascend] section 一 over that set: one maximum, one denominator;
-* a query head with no token in any source gets O = 0 and lse = -inf.
+* a query head with no token in any source gets O = 0 and lse = -inf;
+* several query rows per sequence (section 7.5: prefill and decode share the
+  kernel because the causal constraint is expanded into per-row lengths): row
+  t of sequence b sees, in each source, the first row_lens[b][t] tokens of
+  that source's token set (all of them when the source gives no row lengths).
 """
 from __future__ import annotations
 
@@ -26,7 +30,7 @@ import numpy as np
 
 from .paged import gather_context
 
-__all__ = ["source_tokens", "decode_over_sources"]
+__all__ = ["source_tokens", "decode_over_sources", "attention_over_sources"]
 
 
 def source_tokens(src, b, kv_head):
@@ -78,4 +82,42 @@ def decode_over_sources(q, sources, scale):
                 l = np.sum(e)
                 O[b, h] = (e @ V) / l
                 lse[b, h] = m + np.log(l)
+    return O, lse
+
+
+def attention_over_sources(q, sources, scale):
+    """(O, lse) of attention of several query rows per sequence over the
+    sources: q (B, T, H, D); a source may carry row_lens (B, T), the number of
+    its tokens (in the order ``source_tokens`` lists them) that each row sees.
+    O is (B, T, H, D) and lse (B, T, H); a row with no visible token gets
+    O = 0 and lse = -inf."""
+    q = np.asarray(q, dtype=np.float64)
+    B, T, H, D = q.shape
+    n_kv = sources[0]["k_cache"].shape[1]
+    if any(s["k_cache"].shape[1] != n_kv for s in sources) or n_kv <= 0 or H % n_kv != 0:
+        raise ValueError("every source must have the same key/value heads, dividing the query heads")
+    G = H // n_kv
+    O = np.zeros((B, T, H, D))
+    lse = np.full((B, T, H), -np.inf)
+    for b in range(B):
+        for hk in range(n_kv):
+            parts = [source_tokens(s, b, hk) for s in sources]
+            for t in range(T):
+                Ks, Vs = [], []
+                for s, (K, V) in zip(sources, parts):
+                    n = K.shape[0]
+                    if s.get("row_lens") is not None:
+                        n = max(0, min(n, int(s["row_lens"][b][t])))
+                    Ks.append(K[:n])
+                    Vs.append(V[:n])
+                K, V = np.concatenate(Ks, axis=0), np.concatenate(Vs, axis=0)
+                if K.shape[0] == 0:
+                    continue
+                for h in range(hk * G, (hk + 1) * G):
+                    sc = (K @ q[b, t, h]) * scale
+                    m = np.max(sc)
+                    e = np.exp(sc - m)
+                    l = np.sum(e)
+                    O[b, t, h] = (e @ V) / l
+                    lse[b, t, h] = m + np.log(l)
     return O, lse

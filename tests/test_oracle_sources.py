@@ -115,3 +115,64 @@ def test_source_order_and_grouped_heads():
 
 def test_exported():
     assert oracle.decode_over_sources is decode_over_sources
+
+
+def test_several_rows_one_row_is_decode():
+    """One query row per sequence without row lengths is the decode above."""
+    rng = np.random.default_rng(211)
+    a = _cache(rng, [40, 0, 70], 2, 16, 16)
+    b = _cache(rng, [33, 5, 64], 2, 16, 32)
+    b["selected"] = [[[0, 1], [1]], [[0], []], [[1], [0, 1]]]
+    q = rng.standard_normal((3, 4, 16))
+    O1, l1 = decode_over_sources(q, [a, b], 0.4)
+    O2, l2 = oracle.attention_over_sources(q[:, None], [a, b], 0.4)
+    assert np.array_equal(O2[:, 0], O1) and np.array_equal(l2[:, 0], l1)
+
+
+def test_causal_prefill_chunk_is_causal_attention():
+    """A chunk of the last T tokens of each sequence, each row seeing the
+    cached tokens up to its own position (row lengths n - T + t + 1), is the
+    last T rows of causal attention over the whole sequence
+    (oracle.attention_forward, pinned by finite differences and closed forms)."""
+    rng = np.random.default_rng(213)
+    D, n_kv, H, T = 16, 2, 4, 5
+    lens = [37, 5, 64]
+    src = _cache(rng, lens, n_kv, D, 16)
+    q = rng.standard_normal((3, T, H, D))
+    src["row_lens"] = [[n - T + t + 1 for t in range(T)] for n in lens]
+    O, lse = oracle.attention_over_sources(q, [src], 0.35)
+    G = H // n_kv
+    for b, n in enumerate(lens):
+        for h in range(H):
+            K, V = oracle.gather_context(src["k_cache"], src["v_cache"], src["block_tables"][b], n, h // G)
+            Q = np.zeros((n, D))
+            Q[n - T:] = q[b, :, h]  # the chunk's rows at their positions (earlier rows unused)
+            Of, lf = oracle.attention_forward(Q, K, V, 0.35, causal=True)
+            assert np.allclose(O[b, :, h], Of[n - T:], rtol=0, atol=1e-13)
+            assert np.allclose(lse[b, :, h], lf[n - T:], rtol=0, atol=1e-13)
+
+
+def test_row_lengths_clamp_and_empty_rows():
+    """Row lengths beyond a source's set are clamped to it; a row that sees
+    nothing in any source gets O = 0, lse = -inf; per-source lengths apply to
+    each source's own token order (a sparse source's kept tokens)."""
+    rng = np.random.default_rng(215)
+    a = _cache(rng, [20], 1, 8, 16)
+    b = _cache(rng, [48], 1, 8, 16)
+    b["selected"] = [[[0, 2]]]  # kept pages (ascending): tokens 0..15, then 32..47
+    q = rng.standard_normal((1, 3, 2, 8))
+    a["row_lens"] = [[0, 100, 3]]
+    b["row_lens"] = [[0, 0, 20]]
+    O, lse = oracle.attention_over_sources(q, [a, b], 1.0)
+    assert np.all(O[0, 0] == 0) and np.all(np.isneginf(lse[0, 0]))
+    a2, b2 = dict(a, row_lens=None), dict(b, row_lens=None)
+    O1, _ = oracle.attention_over_sources(q[:, 1:2], [a2], 1.0)
+    assert np.array_equal(O[0, 1], O1[0, 0])  # 100 clamps to the 20 tokens of a; b sees nothing
+    Kb, Vb = oracle.source_tokens(b2, 0, 0)
+    Ka, Va = oracle.source_tokens(a2, 0, 0)
+    K = np.concatenate([Ka[:3], Kb[:20]])
+    V = np.concatenate([Va[:3], Vb[:20]])
+    for h in range(2):
+        s = K @ q[0, 2, h]
+        e = np.exp(s - s.max())
+        assert np.allclose(O[0, 2, h], e @ V / e.sum(), rtol=0, atol=1e-13)
