@@ -30,6 +30,7 @@ from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32, FAError, check, la
 
 __all__ = ["attention", "forward", "backward", "forward_varlen", "backward_varlen", "reshape_and_cache", "paged_decode",
            "quest_page_minmax", "quest_select", "paged_decode_sparse", "paged_decode_sources",
+           "paged_attention_sources",
            "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_dq_and_stats", "workspace_bytes",
            "device_info", "dkdv_schedule", "fwd_tile_pairs", "FAError", "lib"]
 
@@ -295,7 +296,9 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_le
     return o, lse
 
 
-def _check_paged(q, k_cache, v_cache, block_tables, context_lens):
+def _check_paged(q, k_cache, v_cache, block_tables, context_lens, q_view=False):
+    """Shapes of a paged call; q_view: q is a (B, H, D) view of a larger query
+    tensor whose layout the caller checks (only its device and dtype here)."""
     torch = _torch()
     B, H, D = q.shape
     if k_cache.dim() != 5:
@@ -304,7 +307,8 @@ def _check_paged(q, k_cache, v_cache, block_tables, context_lens):
     if k_cache.shape != (nb, Hkv, D // 8, bs, 8) or (v_cache is not None and v_cache.shape != (nb, Hkv, D, bs)):
         raise ValueError("caches must be (num_blocks, Hkv, D/8, block_size, 8) and (num_blocks, Hkv, D, block_size)")
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
-        if t is not None and (not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device):
+        contiguous = t is None or t.is_contiguous() or (q_view and t is q)
+        if t is not None and (not t.is_cuda or not contiguous or t.dtype != q.dtype or t.device != q.device):
             raise ValueError(f"{n} must be a contiguous GPU tensor of q's dtype and device")
     for t, n in ((block_tables, "block_tables"), (context_lens, "context_lens")):
         if not t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
@@ -368,6 +372,48 @@ def paged_decode_sparse(q, k_cache, v_cache, block_tables, context_lens, selecte
     return o, lse
 
 
+def _source_records(q3, sources, Tq=1):
+    """fa_kv_source records of one or two source dicts for a query of shape
+    (B, H, D) (one row per sequence) with Tq rows per sequence; returns
+    (ctypes array, Hkv)."""
+    from . import _lib
+
+    torch = _torch()
+    if not 1 <= len(sources) <= 2:
+        raise ValueError("one or two sources")
+    B = q3.shape[0]
+    recs, Hkv0 = [], None
+    for src in sources:
+        kc, vc, bt, cl = src["k_cache"], src["v_cache"], src["block_tables"], src["context_lens"]
+        _, _, Hkv, _, bs, nb, mxb = _check_paged(q3, kc, vc, bt, cl, q_view=Tq != 1)
+        if Hkv0 is not None and Hkv != Hkv0:
+            raise ValueError("every source must have the same number of key/value heads")
+        Hkv0 = Hkv
+        sel, nsel, rows = src.get("selected"), src.get("n_selected"), src.get("row_lens")
+        topk = 0
+        if nsel is not None:
+            if sel is None or sel.dim() != 3:
+                raise ValueError("a sparse source needs selected (B, Hkv, topk) with n_selected")
+            topk = sel.shape[2]
+            if sel.shape != (B, Hkv, topk) or nsel.shape != (B, Hkv) or sel.dtype != torch.int32 \
+                    or nsel.dtype != torch.int32 or not sel.is_cuda or not nsel.is_cuda \
+                    or not sel.is_contiguous() or not nsel.is_contiguous():
+                raise ValueError("selected must be int32 (B, Hkv, topk) and n_selected int32 (B, Hkv), on the GPU")
+        elif sel is not None:
+            raise ValueError("selected given without n_selected")
+        if rows is not None and (rows.shape != (B, Tq) or rows.dtype != torch.int32 or not rows.is_cuda
+                                 or not rows.is_contiguous()):
+            raise ValueError("row_lens must be a contiguous int32 (B, Tq) GPU tensor")
+        mcl = src.get("max_context_len")
+        if mcl is None:
+            mcl = int(cl.max().item()) if (B > 0 and nsel is None) else 0
+        recs.append(_lib.KvSource(_ptr(kc), _ptr(vc), _ptr(bt), _ptr(cl), bs, nb, mxb, int(mcl),
+                                  _ptr(sel) if (nsel is not None and topk > 0) else None,
+                                  _ptr(nsel) if nsel is not None else None, topk,
+                                  _ptr(rows) if rows is not None else None))
+    return (_lib.KvSource * len(recs))(*recs), Hkv0
+
+
 def paged_decode_sources(q, sources, scale=None, out_dtype=None):
     """Decode attention over one or two KV sources under one softmax:
     (O (B, H, D), lse (B, H)).
@@ -380,48 +426,47 @@ def paged_decode_sources(q, sources, scale=None, out_dtype=None):
     read from context_lens when omitted).  The sources' tokens form one set:
     one maximum and one denominator per query head.
     """
-    from . import _lib
-
     torch = _torch()
-    if not 1 <= len(sources) <= 2:
-        raise ValueError("one or two sources")
     B, H, D = q.shape
-    recs = []
-    for i, src in enumerate(sources):
-        kc, vc, bt, cl = src["k_cache"], src["v_cache"], src["block_tables"], src["context_lens"]
-        _, _, Hkv, _, bs, nb, mxb = _check_paged(q, kc, vc, bt, cl)
-        if i and Hkv != recs[0][1]:
-            raise ValueError("every source must have the same number of key/value heads")
-        sel, nsel = src.get("selected"), src.get("n_selected")
-        topk = 0
-        if nsel is not None:
-            if sel is None or sel.dim() != 3:
-                raise ValueError("a sparse source needs selected (B, Hkv, topk) with n_selected")
-            topk = sel.shape[2]
-            if sel.shape != (B, Hkv, topk) or nsel.shape != (B, Hkv) or sel.dtype != torch.int32 \
-                    or nsel.dtype != torch.int32 or not sel.is_cuda or not nsel.is_cuda \
-                    or not sel.is_contiguous() or not nsel.is_contiguous():
-                raise ValueError("selected must be int32 (B, Hkv, topk) and n_selected int32 (B, Hkv), on the GPU")
-        elif sel is not None:
-            raise ValueError("selected given without n_selected")
-        mcl = src.get("max_context_len")
-        if mcl is None:
-            mcl = int(cl.max().item()) if (B > 0 and nsel is None) else 0
-        rec = _lib.KvSource(_ptr(kc), _ptr(vc), _ptr(bt), _ptr(cl), bs, nb, mxb, int(mcl),
-                            _ptr(sel) if (nsel is not None and topk > 0) else None,
-                            _ptr(nsel) if nsel is not None else None, topk)
-        recs.append((rec, Hkv))
-    arr = (_lib.KvSource * len(recs))(*[r for r, _ in recs])
-    Hkv = recs[0][1]
+    arr, Hkv = _source_records(q, sources)
     odt = q.dtype if out_dtype is None else out_dtype
     with torch.cuda.device(q.device):
         o = torch.empty((B, H, D), dtype=odt, device=q.device)
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-        nbytes = lib().fa_paged_decode_sources_workspace_bytes(B, H, Hkv, D, len(recs), arr)
+        nbytes = lib().fa_paged_decode_sources_workspace_bytes(B, H, Hkv, D, len(arr), arr)
         ws = torch.empty((max(1, nbytes // 4),), dtype=torch.float32, device=q.device)
-        st = lib().fa_paged_decode_sources(B, H, Hkv, D, _dtype_code(q), _dtype_code(o), _ptr(q), len(recs), arr,
+        st = lib().fa_paged_decode_sources(B, H, Hkv, D, _dtype_code(q), _dtype_code(o), _ptr(q), len(arr), arr,
                                            _ptr(o), _ptr(lse), _scale(scale, D), _ptr(ws), nbytes, _stream(q))
     check(st, "fa_paged_decode_sources")
+    return o, lse
+
+
+def paged_attention_sources(q, sources, scale=None, out_dtype=None):
+    """Attention of Tq query tokens per sequence over one or two KV sources
+    under one softmax: (O (B, Tq, H, D), lse (B, Tq, H)).
+
+    q: (B, Tq, H, D).  Sources as for ``paged_decode_sources``, each with an
+    optional row_lens (int32 (B, Tq)): how many of the source's tokens query
+    token t sees (n - Tq + t + 1 for a causal chunk at the end of a context of
+    n cached tokens); all of them when omitted.
+    """
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be (B, Tq, H, D)")
+    B, Tq, H, D = q.shape
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    arr, Hkv = _source_records(q[:, 0], sources, Tq)
+    odt = q.dtype if out_dtype is None else out_dtype
+    with torch.cuda.device(q.device):
+        o = torch.empty((B, Tq, H, D), dtype=odt, device=q.device)
+        lse = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device)
+        nbytes = lib().fa_paged_attention_sources_workspace_bytes(B, Tq, H, Hkv, D, len(arr), arr)
+        ws = torch.empty((max(1, nbytes // 4),), dtype=torch.float32, device=q.device)
+        st = lib().fa_paged_attention_sources(B, Tq, H, Hkv, D, _dtype_code(q), _dtype_code(o), _ptr(q), len(arr),
+                                              arr, _ptr(o), _ptr(lse), _scale(scale, D), _ptr(ws), nbytes,
+                                              _stream(q))
+    check(st, "fa_paged_attention_sources")
     return o, lse
 
 

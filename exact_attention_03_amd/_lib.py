@@ -25,7 +25,8 @@ class KvSource(ctypes.Structure):
     """fa_kv_source of include/fa.h (field for field)."""
     _fields_ = [("k_cache", _vp), ("v_cache", _vp), ("block_tables", _vp), ("context_lens", _vp),
                 ("block_size", _i64), ("num_blocks", _i64), ("max_blocks_per_seq", _i64),
-                ("max_context_len", _i64), ("selected", _vp), ("n_selected", _vp), ("topk", _i64)]
+                ("max_context_len", _i64), ("selected", _vp), ("n_selected", _vp), ("topk", _i64),
+                ("row_lens", _vp)]
 
 
 _srcp = ctypes.POINTER(KvSource)
@@ -72,6 +73,9 @@ SIGNATURES = {
     "fa_paged_decode_sources_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _int, _srcp]),
     "fa_paged_decode_sources": (_int, [_i64, _i64, _i64, _i64, _int, _int, _vp, _int, _srcp, _vp, _vp, _f32, _vp,
                                        _sz, _vp]),
+    "fa_paged_attention_sources_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _int, _srcp]),
+    "fa_paged_attention_sources": (_int, [_i64, _i64, _i64, _i64, _i64, _int, _int, _vp, _int, _srcp, _vp, _vp,
+                                          _f32, _vp, _sz, _vp]),
     "fa_device_info": (_int, [_i64, _int, _intp, _intp]),
     "fa_dkdv_schedule": (_int, [_i64, _i64, _i64, _i64, _int, _int, _i64p, _i64p, _i64p]),
     "fa_fwd_tile_pairs": (_int, [_i64, _i64, _int, _i64p, _i64p]),

@@ -534,6 +534,8 @@ int check_source(const fa_kv_source& x, int idx, int64_t B, int64_t Hkv, bool ch
   if (!sparse && x.selected != nullptr)
     return fail(FA_ERR_INVALID_ARGUMENT, "source %d: selected given without n_selected", idx);
   if (!check_pointers) return FA_OK;
+  if (reinterpret_cast<uintptr_t>(x.row_lens) % 4 != 0)
+    return fail(FA_ERR_INVALID_ARGUMENT, "source %d: row_lens not 4-byte aligned", idx);
   if (x.k_cache == nullptr || x.v_cache == nullptr || reinterpret_cast<uintptr_t>(x.k_cache) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(x.v_cache) % 16 != 0)
     return fail(FA_ERR_INVALID_ARGUMENT, "source %d: k_cache / v_cache NULL or not 16-byte aligned", idx);
@@ -558,15 +560,17 @@ int check_source(const fa_kv_source& x, int idx, int64_t B, int64_t Hkv, bool ch
   out->topk = sparse ? x.topk : 0;
   out->n_splits = split.n_splits;
   out->chunk = split.chunk;
+  out->row_lens = x.row_lens;
   return FA_OK;
 }
 
-// Paged decode over one or two sources.
-int paged_decode_impl(int64_t B, int64_t H, int64_t Hkv, int64_t D, int dtype, int o_dtype, const void* q,
-                      int n_sources, const fa_kv_source* sources, void* o, float* lse, float scale, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+// Paged attention of Tq query tokens per sequence over one or two sources
+// (Tq = 1: decode).
+int paged_decode_impl(int64_t B, int64_t Tq, int64_t H, int64_t Hkv, int64_t D, int dtype, int o_dtype,
+                      const void* q, int n_sources, const fa_kv_source* sources, void* o, float* lse, float scale,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   g_last_error.clear();
-  if (B < 0 || H < 0 || Hkv < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative size");
+  if (B < 0 || Tq < 0 || H < 0 || Hkv < 0) return fail(FA_ERR_INVALID_ARGUMENT, "negative size");
   if (n_sources < 1 || n_sources > 2 || sources == nullptr)
     return fail(FA_ERR_INVALID_ARGUMENT, "n_sources=%d must be 1 or 2 with a sources array", n_sources);
   if (D != 64 && D != 128 && D != 256)
@@ -577,19 +581,20 @@ int paged_decode_impl(int64_t B, int64_t H, int64_t Hkv, int64_t D, int dtype, i
     return fail(FA_ERR_INVALID_ARGUMENT, "H=%lld query heads must be a whole multiple of Hkv=%lld", (long long)H,
                 (long long)Hkv);
   fa::DecodeArgs a{};
-  const bool empty = B == 0 || H == 0;
+  const bool empty = B == 0 || H == 0 || Tq == 0;
   for (int i = 0; i < n_sources; ++i) FA_TRY(check_source(sources[i], i, B, Hkv, !empty, &a.src[i]));
   if (empty) return FA_OK;
   const int64_t n_splits = a.src[0].n_splits + (n_sources > 1 ? a.src[1].n_splits : 0);
-  if (B * Hkv * ((H / Hkv + 15) / 16) * n_splits > kMaxI32 || B * H * n_splits * (D + 1) > ((int64_t)1 << 40))
-    return fail(FA_ERR_UNSUPPORTED, "grid too large (B=%lld Hkv=%lld H/Hkv=%lld)", (long long)B, (long long)Hkv,
-                (long long)(H / Hkv));
-  if (B * H > kMaxI32) return fail(FA_ERR_UNSUPPORTED, "problem too large");
+  if (Tq > kMaxI32 / H || B * Hkv * ((Tq * (H / Hkv) + 15) / 16) * n_splits > kMaxI32 ||
+      B * Tq * H * n_splits * (D + 1) > ((int64_t)1 << 40))
+    return fail(FA_ERR_UNSUPPORTED, "grid too large (B=%lld Tq=%lld Hkv=%lld H/Hkv=%lld)", (long long)B,
+                (long long)Tq, (long long)Hkv, (long long)(H / Hkv));
+  if (B * Tq * H > kMaxI32) return fail(FA_ERR_UNSUPPORTED, "problem too large");
   FA_TRY(check_ptr(q, "q"));
   FA_TRY(check_ptr(o, "o"));
   if (lse != nullptr && reinterpret_cast<uintptr_t>(lse) % 4 != 0)
     return fail(FA_ERR_INVALID_ARGUMENT, "lse is not 4-byte aligned");
-  const size_t need = n_splits > 1 ? (size_t)(B * H * n_splits * (D + 1)) * sizeof(float) : 0;
+  const size_t need = n_splits > 1 ? (size_t)(B * Tq * H * n_splits * (D + 1)) * sizeof(float) : 0;
   if (need > 0) {
     if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
       return fail(FA_ERR_INVALID_ARGUMENT, "workspace is NULL or not 16-byte aligned");
@@ -597,7 +602,7 @@ int paged_decode_impl(int64_t B, int64_t H, int64_t Hkv, int64_t D, int dtype, i
       return fail(FA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu bytes needed",
                   workspace_bytes, need);
   }
-  a.B = B; a.H = H; a.Hkv = Hkv; a.D = D; a.dtype = dtype; a.o_dtype = o_dtype; a.q = q;
+  a.B = B; a.Tq = Tq; a.H = H; a.Hkv = Hkv; a.D = D; a.dtype = dtype; a.o_dtype = o_dtype; a.q = q;
   a.n_sources = n_sources; a.o = o; a.lse = lse; a.scale = scale; a.workspace = static_cast<float*>(workspace);
   a.stream = stream;
   return finish(fa::launch_paged_decode(a), stream, "fa_paged_decode launch");
@@ -634,7 +639,7 @@ int fa_paged_decode(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t block_
                     size_t workspace_bytes, hipStream_t stream) {
   const fa_kv_source x = one_source(block_size, num_blocks, max_blocks_per_seq, max_context_len, k_cache, v_cache,
                                     block_tables, context_lens, nullptr, nullptr, 0);
-  return paged_decode_impl(B, H, Hkv, D, dtype, o_dtype, q, 1, &x, o, lse, scale, workspace, workspace_bytes,
+  return paged_decode_impl(B, 1, H, Hkv, D, dtype, o_dtype, q, 1, &x, o, lse, scale, workspace, workspace_bytes,
                            stream);
 }
 
@@ -713,22 +718,35 @@ int fa_paged_decode_sparse(int64_t B, int64_t H, int64_t Hkv, int64_t D, int64_t
     return fail(FA_ERR_INVALID_ARGUMENT, "selected / n_selected NULL or not 4-byte aligned");
   const fa_kv_source x = one_source(block_size, num_blocks, max_blocks_per_seq, 0, k_cache, v_cache, block_tables,
                                     context_lens, selected, n_selected, topk);
-  return paged_decode_impl(B, H, Hkv, D, dtype, o_dtype, q, 1, &x, o, lse, scale, workspace, workspace_bytes,
+  return paged_decode_impl(B, 1, H, Hkv, D, dtype, o_dtype, q, 1, &x, o, lse, scale, workspace, workspace_bytes,
                            stream);
+}
+
+size_t fa_paged_attention_sources_workspace_bytes(int64_t B, int64_t Tq, int64_t H, int64_t Hkv, int64_t D,
+                                                  int n_sources, const fa_kv_source* sources) {
+  if (B <= 0 || Tq <= 0 || H <= 0 || Hkv <= 0 || D <= 0 || n_sources < 1 || n_sources > 2 || sources == nullptr)
+    return 0;
+  int64_t s = 0;
+  for (int i = 0; i < n_sources; ++i) s += source_split(sources[i], B, Hkv).n_splits;
+  return s > 1 ? (size_t)(B * Tq * H * s * (D + 1)) * sizeof(float) : 0;
+}
+
+int fa_paged_attention_sources(int64_t B, int64_t Tq, int64_t H, int64_t Hkv, int64_t D, int dtype, int o_dtype,
+                               const void* q, int n_sources, const fa_kv_source* sources, void* o, float* lse,
+                               float scale, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return paged_decode_impl(B, Tq, H, Hkv, D, dtype, o_dtype, q, n_sources, sources, o, lse, scale, workspace,
+                           workspace_bytes, stream);
 }
 
 size_t fa_paged_decode_sources_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t D, int n_sources,
                                                const fa_kv_source* sources) {
-  if (B <= 0 || H <= 0 || Hkv <= 0 || D <= 0 || n_sources < 1 || n_sources > 2 || sources == nullptr) return 0;
-  int64_t s = 0;
-  for (int i = 0; i < n_sources; ++i) s += source_split(sources[i], B, Hkv).n_splits;
-  return s > 1 ? (size_t)(B * H * s * (D + 1)) * sizeof(float) : 0;
+  return fa_paged_attention_sources_workspace_bytes(B, 1, H, Hkv, D, n_sources, sources);
 }
 
 int fa_paged_decode_sources(int64_t B, int64_t H, int64_t Hkv, int64_t D, int dtype, int o_dtype, const void* q,
                             int n_sources, const fa_kv_source* sources, void* o, float* lse, float scale,
                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return paged_decode_impl(B, H, Hkv, D, dtype, o_dtype, q, n_sources, sources, o, lse, scale, workspace,
+  return paged_decode_impl(B, 1, H, Hkv, D, dtype, o_dtype, q, n_sources, sources, o, lse, scale, workspace,
                            workspace_bytes, stream);
 }
 

@@ -69,6 +69,7 @@ struct DecodeSource {
   const int* selected = nullptr;
   const int* n_selected = nullptr;
   int64_t topk = 0;
+  const int* row_lens = nullptr;  // (B, Tq): tokens of this source each query row sees; nullptr = all
   int n_splits = 1;   // context splits of this source per (sequence, key/value head)
   int64_t chunk = 64;  // context tokens per split (a multiple of 64; the last split takes the rest)
 };
@@ -77,6 +78,7 @@ struct DecodeSource {
 // sources whose tokens share one softmax.
 struct DecodeArgs {
   int64_t B, H, Hkv, D;
+  int64_t Tq = 1;  // query tokens per sequence
   int dtype, o_dtype;
   const void* q;
   DecodeSource src[2];
@@ -84,8 +86,8 @@ struct DecodeArgs {
   void* o;
   float* lse;  // may be nullptr
   float scale;
-  // With more than one split over all sources: (B, H, S, D) partial outputs,
-  // then (B, H, S) partial lse, S = the sources' splits together.
+  // With more than one split over all sources: (B, Tq, H, S, D) partial
+  // outputs, then (B, Tq, H, S) partial lse, S = the sources' splits together.
   float* workspace;
   hipStream_t stream;
 };

@@ -90,6 +90,7 @@ struct KvSrc {
   const int* lens;
   const int* sel;   // kept pages (B, Hkv, topk), or nullptr for the whole context
   const int* nsel;  // their count (B, Hkv)
+  const int* rows;  // (B, Tq): tokens of this source each query row sees, or nullptr for all
   int64_t num_blocks;
   int64_t chunk;  // tokens per split
   int bs, max_blocks, topk, n_splits;
@@ -99,7 +100,7 @@ template <int D, typename T, typename OT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DecodeTile<D>::OCC, DecodeTile<D>::OCC)))
 void fa_paged_decode_kernel(const uint16_t* __restrict__ q, KvSrc src0, KvSrc src1, void* __restrict__ o,
                             float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse, int H,
-                            int Hkv, int G, float c2) {
+                            int Hkv, int G, int Tq, float c2) {
   using C = DecodeTile<D>;
   __shared__ float sm_m[C::NW][16];
   __shared__ float sm_l[C::NW][16];
@@ -108,15 +109,17 @@ void fa_paged_decode_kernel(const uint16_t* __restrict__ q, KvSrc src0, KvSrc sr
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = wave_id();
-  const int col = lane & 15;  // head column of the score / output tiles
+  const int col = lane & 15;  // query-row column of the score / output tiles
   const int grp = lane >> 4;  // k group: tokens 4 grp .. 4 grp + 3 of a tile
 
-  // Workgroup = (sequence b, key/value head hk, block hb of 16 of its G query
-  // heads, split s_all); the splits of the first source come first, then
-  // those of the second (src1.n_splits = 0 with one source).  Every split's
-  // partial result joins the same combine, so the tokens of both sources
-  // share one softmax.
-  const int n_hb = (G + 15) / 16;
+  // Workgroup = (sequence b, key/value head hk, block hb of 16 of the
+  // group's Tq * G query rows, split s_all); row r of the group is query
+  // token r / G of head hk * G + r % G.  The splits of the first source come
+  // first, then those of the second (src1.n_splits = 0 with one source).
+  // Every split's partial result joins the same combine, so the tokens of
+  // both sources share one softmax.
+  const int R = Tq * G;  // query rows of one (sequence, key/value head)
+  const int n_hb = (R + 15) / 16;
   const int n_splits = src0.n_splits + src1.n_splits;  // over all sources
   const int s_all = blockIdx.x % n_splits;
   const bool second = s_all >= src0.n_splits;
@@ -128,8 +131,8 @@ void fa_paged_decode_kernel(const uint16_t* __restrict__ q, KvSrc src0, KvSrc sr
   const int bh = rest / n_hb;
   const int hk = bh % Hkv;
   const int b = bh / Hkv;
-  const int g0 = 16 * hb;                          // first query head of the block (in the group)
-  const int gn = G - g0 < 16 ? G - g0 : 16;        // query heads in the block
+  const int g0 = 16 * hb;                          // first query row of the block (in the group)
+  const int gn = R - g0 < 16 ? R - g0 : 16;        // query rows in the block
   const int64_t max_tokens = (int64_t)src.max_blocks * bs;
   const int ctx = src.lens[b];
   const int64_t n_real = ctx < 0 ? 0 : (ctx > max_tokens ? max_tokens : ctx);
@@ -157,14 +160,38 @@ void fa_paged_decode_kernel(const uint16_t* __restrict__ q, KvSrc src0, KvSrc sr
   // the rest of a context longer than the split was sized for.
   const int64_t chunk = src.chunk;
   const int64_t t_begin = s * chunk < n_ctx ? s * chunk : n_ctx;
-  const int64_t t_end = (s + 1 < src.n_splits && (s + 1) * chunk < n_ctx) ? (s + 1) * chunk : n_ctx;
+  int64_t t_end = (s + 1 < src.n_splits && (s + 1) * chunk < n_ctx) ? (s + 1) * chunk : n_ctx;
 
-  // Q^T as the B operand of the score product: lane supplies head col of the
+  // This lane's query row (column col of the block) and how many of the
+  // source's tokens it sees (all n_ctx without row lengths).  The tile loop
+  // stops at the block's largest count; tiles past the smallest are masked
+  // per column.
+  const int r_col = g0 + (col < gn ? col : 0);
+  const int t_col = r_col / G;  // query token of the column
+  const int n_ctx32 = (int)n_ctx;  // at most max_blocks * block_size < 2^31 (checked by the host)
+  int lim = n_ctx32;
+  if (src.rows != nullptr) {
+    const int x = src.rows[(int64_t)b * Tq + t_col];
+    lim = x < 0 ? 0 : (x < n_ctx32 ? x : n_ctx32);
+  }
+  if (col >= gn) lim = src.rows != nullptr ? 0 : n_ctx32;  // padding columns decide nothing
+  int lim_hi = lim, lim_lo = col < gn ? lim : n_ctx32;
+#pragma unroll
+  for (int x = 1; x < 16; x <<= 1) {
+    lim_hi = max(lim_hi, __shfl_xor(lim_hi, x, 64));
+    lim_lo = min(lim_lo, __shfl_xor(lim_lo, x, 64));
+  }
+  lim_hi = __builtin_amdgcn_readfirstlane(lim_hi);  // the same in every 16-lane group
+  lim_lo = __builtin_amdgcn_readfirstlane(lim_lo);
+  if (t_end > lim_hi) t_end = lim_hi < t_begin ? t_begin : lim_hi;
+  const int64_t t_mask = t_end < lim_lo ? t_end : lim_lo;  // tiles reaching past it need masks
+
+  // Q^T as the B operand of the score product: lane supplies row col of the
   // block, channels 32 ks + 8 grp .. +7; columns past the block are zero.
   u32x4 qf[C::KSTEPS];
   {
-    const int h = hk * G + g0 + (col < gn ? col : 0);
-    const auto rq = make_rsrc(q + ((int64_t)b * H + h) * D, D * 2);
+    const int h = hk * G + r_col % G;
+    const auto rq = make_rsrc(q + (((int64_t)b * Tq + t_col) * H + h) * D, D * 2);
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
       const u32x4 x = gload16(rq, (uint32_t)((32 * ks + 8 * grp) * 2));
@@ -229,20 +256,23 @@ void fa_paged_decode_kernel(const uint16_t* __restrict__ q, KvSrc src0, KvSrc sr
       float sc[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[i] = sacc[i] * c2;
-      if (t0 + 16 > t_end) {  // the split's last tile: mask tokens past its end
+      if (t0 + 16 > t_mask) {  // the split's last tile, or a column's last visible token
         keep_branch();
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (t0 + 4 * grp + i >= t_end) sc[i] = -INFINITY;
+          if (t0 + 4 * grp + i >= t_end || t0 + 4 * grp + i >= lim) sc[i] = -INFINITY;
       }
       float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);  // finite: the tile has a token
-      const float alpha = fast_exp2(m_run - m_new);
+      const float m_new = fmaxf(m_run, mx);
+      // -inf while a column has seen no visible token: exponentiate against 0
+      // then (every weight is 0) instead of forming -inf - (-inf)
+      const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_ref);
       float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - m_new);
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(sc[i] - m_ref);
       l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
       if (wave_any(m_new > m_run)) {
 #pragma unroll
@@ -290,8 +320,8 @@ void fa_paged_decode_kernel(const uint16_t* __restrict__ q, KvSrc src0, KvSrc sr
     }
     const float val = m != -INFINITY ? acc / l : 0.f;
     const float lse_n = m != -INFINITY ? (m + __log2f(l)) * kLn2 : -INFINITY;
-    const int h = hk * G + g0 + c;
-    const int64_t row = (int64_t)b * H + h;
+    const int r = g0 + c;  // query row: token r / G of head hk * G + r % G
+    const int64_t row = ((int64_t)b * Tq + r / G) * H + hk * G + r % G;
     if (n_splits == 1) {
       if constexpr (sizeof(OT) == 4) {
         reinterpret_cast<float*>(o)[row * D + d] = val;
@@ -368,6 +398,7 @@ static KvSrc kv_src(const DecodeSource& d) {
   k.max_blocks = (int)d.max_blocks;
   k.topk = (int)d.topk;
   k.n_splits = d.n_splits;
+  k.rows = d.row_lens;
   return k;
 }
 
@@ -378,16 +409,16 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   KvSrc s1 = a.n_sources > 1 ? kv_src(a.src[1]) : s0;
   if (a.n_sources < 2) s1.n_splits = 0;  // no workgroup takes the second source
   const int n_splits = s0.n_splits + s1.n_splits;
-  const int64_t grid = a.B * a.Hkv * ((G + 15) / 16) * n_splits;
+  const int64_t grid = a.B * a.Hkv * ((a.Tq * G + 15) / 16) * n_splits;
   float* part_o = a.workspace;
-  float* part_lse = a.workspace + a.B * a.H * n_splits * a.D;
+  float* part_lse = a.workspace + a.B * a.Tq * a.H * n_splits * a.D;
   hipLaunchKernelGGL((fa_paged_decode_kernel<D, T, OT>), dim3((unsigned)grid), dim3(256), 0, a.stream,
-                     (const uint16_t*)a.q, s0, s1, a.o, a.lse, part_o, part_lse, (int)a.H, (int)a.Hkv, G,
+                     (const uint16_t*)a.q, s0, s1, a.o, a.lse, part_o, part_lse, (int)a.H, (int)a.Hkv, G, (int)a.Tq,
                      a.scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_splits == 1) return e;
-  hipLaunchKernelGGL((fa_paged_decode_combine_kernel<D, T, OT>), dim3((unsigned)(a.B * a.H)), dim3(D), 0, a.stream,
-                     part_o, part_lse, a.o, a.lse, n_splits);
+  hipLaunchKernelGGL((fa_paged_decode_combine_kernel<D, T, OT>), dim3((unsigned)(a.B * a.Tq * a.H)), dim3(D), 0,
+                     a.stream, part_o, part_lse, a.o, a.lse, n_splits);
   return hipGetLastError();
 }
 template <int D, typename T>

@@ -402,6 +402,7 @@ typedef struct fa_kv_source {
   const int32_t* selected;      /* DEVICE (B, Hkv, topk) or NULL */
   const int32_t* n_selected;    /* DEVICE (B, Hkv), or NULL for a dense source */
   int64_t topk;
+  const int32_t* row_lens;      /* DEVICE (B, Tq): tokens each query row sees, or NULL (all) */
 } fa_kv_source;
 size_t fa_paged_decode_sources_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t D,
                                                int n_sources, const fa_kv_source* sources);
@@ -409,6 +410,28 @@ int fa_paged_decode_sources(int64_t B, int64_t H, int64_t Hkv, int64_t D, int dt
                             int o_dtype, const void* q, int n_sources,
                             const fa_kv_source* sources, void* o, float* lse, float scale,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Several query tokens per sequence over the same sources (section 7.5 of the
+ * page above: prefill and decode share the kernel because the causal
+ * constraint is expanded into per-row lengths).  q is (B, Tq, H, D); o is
+ * (B, Tq, H, D) o_dtype and lse (B, Tq, H) float32 or NULL.  A source's
+ * row_lens (DEVICE int32 (B, Tq), or NULL) gives how many of its tokens --
+ * the first ones of its context, or of its kept pages' tokens in page order --
+ * query token t of sequence b sees (clamped to [0, what the source holds]);
+ * NULL: all of them.  For a chunk of the last Tq tokens of a context of n
+ * cached tokens, row_lens[b][t] = n - Tq + t + 1 is causal attention.  A
+ * query row that sees no token gets O = 0 and lse = -inf.  Tq = 1 is
+ * fa_paged_decode_sources.  workspace: fa_paged_attention_sources_workspace_bytes
+ * of the same arguments.
+ */
+size_t fa_paged_attention_sources_workspace_bytes(int64_t B, int64_t Tq, int64_t H, int64_t Hkv,
+                                                  int64_t D, int n_sources,
+                                                  const fa_kv_source* sources);
+int fa_paged_attention_sources(int64_t B, int64_t Tq, int64_t H, int64_t Hkv, int64_t D,
+                               int dtype, int o_dtype, const void* q, int n_sources,
+                               const fa_kv_source* sources, void* o, float* lse, float scale,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Device facts used for launch sizing, for the current device: compute

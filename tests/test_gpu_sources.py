@@ -203,3 +203,90 @@ def test_window_and_quest_selection_end_to_end():
     eo, el = max_abs(to_f64(o), O), max_abs(to_f64(lse), L)
     log(f"window + selection: O32 max-abs {eo:.3e} | lse {el:.3e}")
     assert eo <= O_MAX_ABS and el <= LSE_MAX_ABS
+
+
+def _rows_tensor(x):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.int32))).cuda()
+
+
+@pytest.mark.parametrize("B,Tq,H,Hkv,D,dtype,bs", [
+    (3, 7, 8, 2, 128, "bf16", 16),    # 28 query rows per key/value head: two column blocks
+    (2, 33, 4, 4, 64, "f16", 32),     # a longer chunk, one query head per key/value head
+    (2, 5, 16, 1, 256, "bf16", 16),   # 80 rows on one key/value head
+])
+def test_causal_prefill_chunk_over_paged_cache(B, Tq, H, Hkv, D, dtype, bs):
+    """The last Tq tokens of each context as queries, each seeing the cache up
+    to its own position (row lengths n - Tq + t + 1): against the oracle, and
+    the stored O is RNE of the fp32 O."""
+    import torch
+
+    fa = _fa()
+    w = workloads.DecodeWorkload("prefill", 950 + Tq + D, B, H, Hkv, D, bs, Tq, 3000, dtype)
+    log(f"case prefill chunk {w} Tq={Tq}")
+    cpu = workloads.make_decode_inputs(w)
+    lens = cpu[4].numpy()
+    rng = np.random.default_rng(Tq)
+    qd = torch.from_numpy((rng.integers(-32, 32, size=(B, Tq, H, D)) / 16).astype(np.float32)).to(cpu[0].dtype)
+    rows = [[int(n) - Tq + t + 1 for t in range(Tq)] for n in lens]
+    src = _gpu_src(cpu)
+    src["row_lens"] = _rows_tensor(rows)
+    q = qd.cuda()
+    o32, lse = fa.paged_attention_sources(q, [src], scale=w.scale, out_dtype=torch.float32)
+    o16, _ = fa.paged_attention_sources(q, [src], scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o16.view(torch.int16), o32.to(o16.dtype).view(torch.int16)), "O16 != RNE(O32)"
+    O, L = oracle.attention_over_sources(to_f64(qd), [dict(_oracle_src(cpu), row_lens=rows)], w.scale)
+    eo, el = max_abs(to_f64(o32), O), max_abs(to_f64(lse), L)
+    log(f"  O32 max-abs {eo:.3e} | lse {el:.3e}")
+    assert eo <= O_MAX_ABS and el <= LSE_MAX_ABS
+
+
+def test_two_sources_with_row_lengths():
+    """A window pool and a sparse pool, each with its own per-row lengths
+    (zero, partial, past the end), rows that see nothing anywhere included."""
+    import torch
+
+    fa = _fa()
+    B, Tq, H, Hkv, D = 3, 6, 8, 2, 128
+    wa = workloads.DecodeWorkload("rows_a", 960, B, H, Hkv, D, 16, 1, 200, "bf16")
+    wb = workloads.DecodeWorkload("rows_b", 961, B, H, Hkv, D, 32, 100, 2000, "bf16")
+    ca, cb = workloads.make_decode_inputs(wa), workloads.make_decode_inputs(wb)
+    rng = np.random.default_rng(962)
+    sel, nsel, lists = _random_selection(rng, cb[4].numpy(), Hkv, 32, 9)
+    ra = rng.integers(-3, 260, size=(B, Tq)).astype(np.int32)
+    rb = rng.integers(0, 400, size=(B, Tq)).astype(np.int32)
+    ra[0, 0] = 0
+    rb[0, 0] = 0  # row 0 of sequence 0 sees nothing
+    qd = torch.from_numpy((rng.integers(-32, 32, size=(B, Tq, H, D)) / 16).astype(np.float32)).to(torch.bfloat16)
+    ga, gb = _gpu_src(ca), _gpu_src(cb, sel, nsel)
+    ga["row_lens"], gb["row_lens"] = _rows_tensor(ra), _rows_tensor(rb)
+    o, lse = fa.paged_attention_sources(qd.cuda(), [ga, gb], scale=wa.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    oa = dict(_oracle_src(ca), row_lens=ra.tolist())
+    ob = dict(_oracle_src(cb, lists), row_lens=rb.tolist())
+    O, L = oracle.attention_over_sources(to_f64(qd), [oa, ob], wa.scale)
+    fin = np.isfinite(L)
+    assert np.array_equal(np.isfinite(to_f64(lse)), fin) and not fin[0, 0].any()
+    assert np.all(to_f64(o)[0, 0] == 0)
+    eo, el = max_abs(to_f64(o), O), max_abs(to_f64(lse)[fin], L[fin])
+    log(f"two sources with row lengths: O32 max-abs {eo:.3e} | lse {el:.3e}")
+    assert eo <= O_MAX_ABS and el <= LSE_MAX_ABS
+
+
+def test_one_query_row_is_the_decode_call():
+    """Tq = 1 without row lengths runs what fa_paged_decode_sources runs, bit for bit."""
+    import torch
+
+    fa = _fa()
+    w = workloads.DecodeWorkload("rows_one", 963, 4, 8, 2, 128, 16, 1, 5000, "f16")
+    cpu = workloads.make_decode_inputs(w)
+    rng = np.random.default_rng(7)
+    sel, nsel, _ = _random_selection(rng, cpu[4].numpy(), 2, 16, 20)
+    srcs = [_gpu_src(cpu), _gpu_src(cpu, sel, nsel)]
+    q = cpu[0].cuda()
+    o1, l1 = fa.paged_decode_sources(q, srcs, scale=w.scale, out_dtype=torch.float32)
+    o2, l2 = fa.paged_attention_sources(q[:, None].contiguous(), srcs, scale=w.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2[:, 0]) and torch.equal(l1, l2[:, 0])

@@ -290,3 +290,29 @@ def test_two_source_decode_argument_errors(fa):
     small = (KvSource * 2)(src(mctx=64), src(sel=I4, nsel=I4, topk=2))
     assert lib.fa_paged_decode_sources_workspace_bytes(1, 8, 1, 128, 2, small) == 8 * 2 * 129 * 4
     assert call([src(mctx=64), src(sel=I4, nsel=I4, topk=2)], B=1, Hkv=1) == 1 and "workspace" in fa.last_error()
+
+
+@_NO_GPU
+def test_several_query_rows_argument_errors(fa):
+    """fa_paged_attention_sources: Tq rules, row_lens alignment, workspace for
+    Tq rows; every call fails validation (or is empty) before any HIP call."""
+    from exact_attention_03_amd._lib import KvSource
+
+    lib = fa.lib()
+    I4 = ctypes.c_void_p(0x30000)
+
+    def src(rows=None, mctx=800):
+        return KvSource(P, P, I4, I4, 16, 100, 50, mctx, None, None, 0, rows)
+
+    def call(srcs, Tq=3, B=2, ws=None, wsb=0):
+        arr = (KvSource * len(srcs))(*srcs)
+        return lib.fa_paged_attention_sources(B, Tq, 8, 2, 128, 0, 0, P, len(srcs), arr, P, P, 0.1, ws, wsb, None)
+
+    assert call([src()], Tq=-1) == 1
+    assert call([src()], Tq=0) == 0                                      # empty
+    assert call([src(rows=ctypes.c_void_p(0x30002))]) == 1 and "row_lens" in fa.last_error()
+    one = lib.fa_paged_attention_sources_workspace_bytes(1, 1, 8, 2, 128, 1, (KvSource * 1)(src(mctx=10000)))
+    five = lib.fa_paged_attention_sources_workspace_bytes(1, 5, 8, 2, 128, 1, (KvSource * 1)(src(mctx=10000)))
+    assert one > 0 and five == 5 * one
+    assert one == lib.fa_paged_decode_sources_workspace_bytes(1, 8, 2, 128, 1, (KvSource * 1)(src(mctx=10000)))
+    assert call([src(mctx=10000)], Tq=5, B=1, ws=P, wsb=five - 4) == 1 and "workspace" in fa.last_error()
