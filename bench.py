@@ -48,6 +48,7 @@ KERNEL_SOURCES = {
     "fa_paged_decode": ("fa_paged.hip", "fa_device.h", "fa_kernels.h"),
     "fa_paged_decode_sparse": ("fa_paged.hip", "fa_device.h", "fa_kernels.h"),
     "fa_paged_decode_sources": ("fa_paged.hip", "fa_device.h", "fa_kernels.h"),
+    "fa_paged_attention_sources": ("fa_paged.hip", "fa_device.h", "fa_kernels.h"),
     "fa_quest_select": ("fa_quest.hip", "fa_device.h", "fa_kernels.h"),
 }
 
@@ -466,17 +467,20 @@ def run(args):
 # ------------------------------------------------------------------ paged decode
 def decode_bytes(w, lens) -> float:
     """Algorithmic HBM bytes of one decode step: the new tokens' K / V rows
-    read and written into the cache, every cached K and V element of the
-    contexts read once, q read, O (16-bit) and lse written, the block-table
-    entries of the contexts and the context lengths read."""
+    read and written into the cache (q_len per sequence), every cached K and
+    V element of the contexts read once, q read, O (16-bit) and lse written
+    (q_len rows per sequence), the block-table entries of the contexts, the
+    context lengths and (q_len > 1) the per-row visible lengths read."""
     import numpy as np
 
     lens = np.asarray(lens, dtype=np.int64)
     e = 2  # bytes per 16-bit element
+    n = len(lens)
+    T = w.q_len
     ctx = float(lens.sum()) * w.Hkv * w.D * 2 * e
-    new = float(w.B) * w.Hkv * w.D * 2 * e * 2
-    qo = float(w.B) * w.H * w.D * e * 2 + w.B * w.H * 4
-    tables = float((-(-lens // w.block_size)).sum()) * 4 + w.B * 4
+    new = float(n) * T * w.Hkv * w.D * 2 * e * 2
+    qo = float(n) * T * (w.H * w.D * e * 2 + w.H * 4)
+    tables = float((-(-lens // w.block_size)).sum()) * 4 + n * 4 + (n * T * 4 if T > 1 else 0)
     return ctx + new + qo + tables
 
 
@@ -484,6 +488,12 @@ def _oracle_decode(args):
     import oracle
 
     q, kc, vc, tables, lens, scale, topk, win = args
+    if q.ndim == 4:  # several query tokens per sequence: the last ones of each context, each causal
+        T = q.shape[1]
+        rows = [[int(n) - T + t + 1 for t in range(T)] for n in lens]
+        src = {"k_cache": kc, "v_cache": vc, "block_tables": tables, "context_lens": lens, "row_lens": rows}
+        oracle.attention_over_sources(q, [src], scale)
+        return len(lens)
     if not topk:
         oracle.paged_decode(q, kc, vc, tables, lens, scale)
         return len(lens)
@@ -556,6 +566,8 @@ def decode_cpu_baseline(w, cpu, n_seq: int, workers: int, window=None):
     nbytes = sum(quest_bytes(w, sub)) if w.topk else decode_bytes(w, sub)
     what = ("query-aware oracle (page min / max, scores, Top-K, attention over the kept pages)" if w.topk
             else "paged-decode oracle (token-by-token gather through the block table, plain softmax)")
+    if w.q_len > 1:
+        what = f"paged oracle with {w.q_len} causal query rows per sequence (per-row visible lengths)"
     if window is not None:
         what = ("query-aware oracle (page min / max, scores, Top-K) and the two-source oracle (window pool and kept "
                 "pages under one softmax)")
@@ -722,33 +734,46 @@ def run_quest(args):
 
 
 def run_decode(args):
-    """One step = fa_reshape_and_cache of one new token per sequence (at the
-    last position of its context) + fa_paged_decode over the whole context."""
+    """One step = fa_reshape_and_cache of the new tokens (the last q_len
+    positions of each context) + attention of those tokens over the whole
+    context: fa_paged_decode for one token, fa_paged_attention_sources with
+    per-row visible lengths (each token causal) for several."""
     import numpy as np
     import torch
 
     import exact_attention_03_amd as fa
+    from exact_attention_03_amd._lib import KvSource
 
     w = workloads.DECODE_WORKLOADS[args.workload]
+    T = w.q_len
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cpu = workloads.make_decode_inputs(w)
     q, kc, vc, tables, lens = (t.to(dev) for t in cpu)
     lens_np = cpu[4].numpy().astype(np.int64)
     tab_np = cpu[3].numpy()
-    slots = torch.tensor([int(tab_np[b, (n - 1) // w.block_size]) * w.block_size + (n - 1) % w.block_size
-                          for b, n in enumerate(lens_np)], dtype=torch.int64, device=dev)
+    pos = [(b, int(n) - T + t) for b, n in enumerate(lens_np) for t in range(T)]
+    slots = torch.tensor([int(tab_np[b, p // w.block_size]) * w.block_size + p % w.block_size for b, p in pos],
+                         dtype=torch.int64, device=dev)
     gen = torch.Generator().manual_seed(w.seed)
-    new_k = torch.randn((w.B, w.Hkv, w.D), generator=gen).to(q.dtype).to(dev)
-    new_v = torch.randn((w.B, w.Hkv, w.D), generator=gen).to(q.dtype).to(dev)
-    o = torch.empty((w.B, w.H, w.D), dtype=q.dtype, device=dev)
-    lse = torch.empty((w.B, w.H), dtype=torch.float32, device=dev)
+    new_k = torch.randn((w.B * T, w.Hkv, w.D), generator=gen).to(q.dtype).to(dev)
+    new_v = torch.randn((w.B * T, w.Hkv, w.D), generator=gen).to(q.dtype).to(dev)
+    o = torch.empty(tuple(q.shape), dtype=q.dtype, device=dev)
+    lse = torch.empty(tuple(q.shape[:-1]), dtype=torch.float32, device=dev)
     L = fa.lib()
     code = fa._dtype_code(q)
     nb, mxb = kc.shape[0], tables.shape[1]
-    ws_bytes = L.fa_paged_decode_workspace_bytes(w.B, w.H, w.Hkv, w.D, w.hi)
-    ws = torch.empty((max(1, ws_bytes // 4),), dtype=torch.float32, device=dev)
     P = lambda t: t.data_ptr()  # noqa: E731
+    if T > 1:
+        rows = torch.tensor([[int(n) - T + t + 1 for t in range(T)] for n in lens_np], dtype=torch.int32, device=dev)
+        srcs = (KvSource * 1)(KvSource(P(kc), P(vc), P(tables), P(lens), w.block_size, nb, mxb, w.hi, None, None, 0,
+                                       P(rows)))
+        ws_bytes = L.fa_paged_attention_sources_workspace_bytes(w.B, T, w.H, w.Hkv, w.D, 1, srcs)
+        dec_name = "fa_paged_attention_sources"
+    else:
+        ws_bytes = L.fa_paged_decode_workspace_bytes(w.B, w.H, w.Hkv, w.D, w.hi)
+        dec_name = "fa_paged_decode"
+    ws = torch.empty((max(1, ws_bytes // 4),), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
 
@@ -769,12 +794,16 @@ def run_decode(args):
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        call(L.fa_reshape_and_cache(w.B, w.Hkv, w.D, w.block_size, nb, code, P(new_k), P(new_v), P(slots), P(kc),
-                                    P(vc), sp), "fa_reshape_and_cache")
+        call(L.fa_reshape_and_cache(w.B * T, w.Hkv, w.D, w.block_size, nb, code, P(new_k), P(new_v), P(slots),
+                                    P(kc), P(vc), sp), "fa_reshape_and_cache")
         if ev is not None:
             ev[1].record(stream)
-        call(L.fa_paged_decode(w.B, w.H, w.Hkv, w.D, w.block_size, nb, mxb, w.hi, code, code, P(q), P(kc), P(vc),
-                               P(tables), P(lens), P(o), P(lse), w.scale, P(ws), ws_bytes, sp), "fa_paged_decode")
+        if T > 1:
+            call(L.fa_paged_attention_sources(w.B, T, w.H, w.Hkv, w.D, code, code, P(q), 1, srcs, P(o), P(lse),
+                                              w.scale, P(ws), ws_bytes, sp), dec_name)
+        else:
+            call(L.fa_paged_decode(w.B, w.H, w.Hkv, w.D, w.block_size, nb, mxb, w.hi, code, code, P(q), P(kc),
+                                   P(vc), P(tables), P(lens), P(o), P(lse), w.scale, P(ws), ws_bytes, sp), dec_name)
         if ev is not None:
             ev[2].record(stream)
 
@@ -793,11 +822,14 @@ def run_decode(args):
     cache_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     nbytes = decode_bytes(w, lens_np)
-    dec_bytes = nbytes - float(w.B) * w.Hkv * w.D * 2 * 2 * 2  # the cache write's bytes are the other kernel's
-    splits = max(1, ws_bytes // (4 * w.B * w.H * (w.D + 1))) if ws_bytes else 1
+    dec_bytes = nbytes - float(w.B) * T * w.Hkv * w.D * 2 * 2 * 2  # the cache write's bytes are the other kernel's
+    splits = max(1, ws_bytes // (4 * w.B * T * w.H * (w.D + 1))) if ws_bytes else 1
     ach = dec_bytes / (dec_ms * 1e-3) / 1e9
+    metric = ("paged decode attention (cache write + decode) HBM GB/s on 1 MI355X" if T == 1 else
+              f"speculative verification over a paged cache (cache write of {T} tokens + attention of {T} causal "
+              f"query tokens per sequence) HBM GB/s on 1 MI355X")
     out = {
-        "metric": "paged decode attention (cache write + decode) HBM GB/s on 1 MI355X",
+        "metric": metric,
         "value": round(nbytes / (ms_step * 1e-3) / 1e9, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -811,13 +843,15 @@ def run_decode(args):
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B={w.B} sequences, contexts {int(lens_np.min())}..{int(lens_np.max())} "
                                f"tokens ({int(lens_np.sum())} total), H={w.H} Hkv={w.Hkv} D={w.D} pages of "
-                               f"{w.block_size} tokens, {w.dtype}, {splits} context splits",
-                   "B": w.B, "H": w.H, "Hkv": w.Hkv, "D": w.D, "block_size": w.block_size, "seed": w.seed},
+                               f"{w.block_size} tokens, {w.dtype}, {splits} context splits"
+                               + (f", {T} query tokens per sequence" if T > 1 else ""),
+                   "B": w.B, "H": w.H, "Hkv": w.Hkv, "D": w.D, "block_size": w.block_size, "q_len": T,
+                   "seed": w.seed},
         "breakdown": {"reshape_and_cache_ms": round(cache_ms, 4), "paged_decode_ms": round(dec_ms, 4),
                       "splits": splits},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": stored_traffic("fa_paged_decode", w.name),
-                     "kernel": "fa_paged_decode (decode kernel and, with splits, its combine kernel)",
+                     "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": stored_traffic(dec_name, w.name),
+                     "kernel": f"{dec_name} (decode kernel and, with splits, its combine kernel)",
                      "algorithmic": {"amount": dec_bytes, "unit": "byte", "per_launch": True}},
         "cpu_baseline": None,
     }

@@ -290,3 +290,34 @@ def test_one_query_row_is_the_decode_call():
     o2, l2 = fa.paged_attention_sources(q[:, None].contiguous(), srcs, scale=w.scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2[:, 0]) and torch.equal(l1, l2[:, 0])
+
+
+def test_verify_workload():
+    """The speculative verification workload (64 sequences of 512..16000
+    tokens, 4 causal query tokens each) on its shortest, longest and one
+    middle sequence."""
+    import torch
+
+    fa = _fa()
+    w = workloads.DECODE_WORKLOADS["verify_gqa_bf16"]
+    cpu = workloads.make_decode_inputs(w)
+    q, kc, vc, tables, lens = cpu
+    n = lens.numpy()
+    T = w.q_len
+    rows = np.array([[int(x) - T + t + 1 for t in range(T)] for x in n], dtype=np.int32)
+    src = _gpu_src(cpu)
+    src["row_lens"] = _rows_tensor(rows)
+    o, lse = fa.paged_attention_sources(q.cuda(), [src], scale=w.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    seqs = sorted({int(np.argmin(n)), int(np.argmax(n)), 7})
+    t = tables[seqs].numpy()
+    used = sorted({int(x) for x in t.flatten() if x >= 0})
+    remap = np.full(kc.shape[0], -1, dtype=np.int32)
+    remap[used] = np.arange(len(used), dtype=np.int32)
+    sub = {"k_cache": to_f64(kc[used]), "v_cache": to_f64(vc[used]),
+           "block_tables": np.where(t >= 0, remap[np.clip(t, 0, None)], -1), "context_lens": n[seqs],
+           "row_lens": rows[seqs].tolist()}
+    O, L = oracle.attention_over_sources(to_f64(q[seqs]), [sub], w.scale)
+    eo, el = max_abs(to_f64(o[seqs]), O), max_abs(to_f64(lse[seqs]), L)
+    log(f"verify_gqa_bf16 sequences {seqs}: O32 max-abs {eo:.3e} | lse {el:.3e}")
+    assert eo <= O_MAX_ABS and el <= LSE_MAX_ABS

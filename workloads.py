@@ -186,6 +186,7 @@ class DecodeWorkload:
     dtype: str
     topk: int = 0      # pages kept per (sequence, key/value head) by the query-aware selection; 0 = all
     window: int = 0    # tokens per sequence of a second, sliding-window pool attended whole; 0 = none
+    q_len: int = 1     # query tokens per sequence: the last q_len positions of each context, each causal
 
     @property
     def scale(self) -> float:
@@ -222,6 +223,9 @@ DECODE_WORKLOADS = {
     # 64 sequences of 512..16000 tokens (about 8K on average), 32 query heads over 8
     # key/value heads, D = 128, pages of 16 tokens
     "decode_gqa_bf16": DecodeWorkload("decode_gqa_bf16", 11, 64, 32, 8, 128, 16, 512, 16000, "bf16"),
+    # speculative verification on the same batch and cache: the last 4 tokens of every context
+    # are written to the cache and attend, each causally, to the context up to themselves
+    "verify_gqa_bf16": DecodeWorkload("verify_gqa_bf16", 11, 64, 32, 8, 128, 16, 512, 16000, "bf16", 0, 0, 4),
     # the same batch and cache with 64 pages (1024 tokens) kept per context by the query-aware selection
     "quest_gqa_bf16": DecodeWorkload("quest_gqa_bf16", 11, 64, 32, 8, 128, 16, 512, 16000, "bf16", 64),
     # two sources under one softmax: the same 64 kept pages plus a sliding-window pool of the
@@ -245,7 +249,7 @@ def make_decode_inputs(w: DecodeWorkload):
         x = torch.from_numpy(rng.integers(-32, 32, size=shape, dtype=np.int8))
         return x.to(tdt) * 0.0625  # exact: a power-of-two scale of small integers
 
-    q = draw((w.B, w.H, w.D))
+    q = draw((w.B, w.H, w.D) if w.q_len == 1 else (w.B, w.q_len, w.H, w.D))
     kc = draw((num_blocks, w.Hkv, w.D // 8, w.block_size, 8))
     vc = draw((num_blocks, w.Hkv, w.D, w.block_size))
     return q, kc, vc, torch.from_numpy(tables), torch.from_numpy(lens)
