@@ -115,11 +115,21 @@ def executed_over_counted(w) -> dict:
             "fa_bwd_dkdv": round(dkdv, 4)}
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace runs collapsed, so
+    that an edit of comments alone does not count as a change of the kernel."""
+    import re
+
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def sources_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "exact_attention_03_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "exact_attention_03_amd", "csrc", name), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -20,18 +20,28 @@
 // per lane, 16 tokens x 4 chunks = 1 KiB per load; and 8-byte runs of four
 // consecutive tokens of one value channel, 512 bytes per load.
 //
-// Decode (one query token per sequence).  A workgroup owns (sequence b,
-// key/value head hk, split s) and a contiguous range of the context; its 4
-// waves take 16-token tiles in turn.  Per tile a wave computes, for the G
-// query heads of hk padded to 16,
-//     S^T (16 tokens x 16 heads) = K Q^T      4 or 8 or 16 x v_mfma 16x16x32
-//     online softmax per head column (exp2 units)
-//     O^T (D x 16 heads) += V^T P^T           D/16 x v_mfma 16x16x16
+// Decode.  A workgroup owns (sequence b, key/value head hk, a block of 16 of
+// the query rows that use hk, split s) and a contiguous range of the
+// context; its 4 waves take 16-token tiles in turn.  The query rows are the G
+// query heads of hk (one query token per sequence), or the Tq x G (token,
+// head) rows of several query tokens, each with its own count of visible
+// tokens; blocks are padded to 16.  Per tile a wave computes
+//     S^T (16 tokens x 16 rows) = K Q^T       4 or 8 or 16 x v_mfma 16x16x32
+//     online softmax per row column (exp2 units)
+//     O^T (D x 16 rows) += V^T P^T            D/16 x v_mfma 16x16x16
 // where the score result is already the B operand of the output product.
 // The waves' states are merged through LDS; with several splits per
 // sequence the merged (O, lse) pairs go to a workspace and a second kernel
 // combines them: O = sum_s exp(lse_s - lse) O_s, lse = ln sum_s exp(lse_s).
-// HBM-bound: every cached key and value of the context is read once.
+// The splits may come from two sources (two caches, or a whole context and
+// a set of kept pages, [V4-A100] below), which the combine then normalises
+// together.  HBM-bound: every cached key and value a block needs is read
+// once.
+//
+// [V4-A100] = the page "在 4 张 A100 上部署 DeepSeek-V4-Flash-0731" (BiumBiu),
+// section 7.5: one sparse attention kernel for one source or two sources
+// under a single softmax denominator; prefill and decode share it because
+// the causal constraint becomes per-row lengths.
 #include "fa_device.h"
 #include "fa_kernels.h"
 

@@ -42,3 +42,11 @@ def test_two_source_bytes_add_the_window():
     sel_b, dec_b = bench.quest_bytes(wq, lens)
     per_seq = 1024 * w.Hkv * w.D * 2 * 2 + (1024 // 16) * w.Hkv * 4
     assert sel_a == sel_b and dec_a - dec_b == len(lens) * per_seq
+
+
+def test_source_hash_ignores_comments_only():
+    """A stored measurement stays valid across comment edits, not across code edits."""
+    a = "int f(int x) {  // twice\n  return 2 * x; /* scaled */\n}\n"
+    b = "// a new header line\nint f(int x) {\n  return 2 * x;\n}\n"
+    c = "int f(int x) {\n  return 3 * x;\n}\n"
+    assert bench._code_only(a) == bench._code_only(b) != bench._code_only(c)
