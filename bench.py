@@ -870,6 +870,19 @@ def run_decode(args):
     return out
 
 
+def device_record() -> dict:
+    """What the numbers were measured on: device name and CU count, ROCm/HIP,
+    torch and numpy versions."""
+    import numpy as np
+    import torch
+
+    import exact_attention_03_amd as fa
+
+    return {"name": torch.cuda.get_device_name(0), "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", ""),
+            "compute_units": fa.device_info(128)[0], "hip": torch.version.hip, "torch": torch.__version__,
+            "numpy": np.__version__}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -895,6 +908,7 @@ def main(argv=None):
         out = run_quest(args) if workloads.DECODE_WORKLOADS[args.workload].topk else run_decode(args)
     else:
         out = run(args)
+    out["device"] = device_record()
     print(json.dumps(out), flush=True)
     return 0
 
