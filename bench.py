@@ -264,12 +264,17 @@ def cpu_baseline(w, cpu_inputs, n_heads: int, workers: int):
 
 
 # ------------------------------------------------------------------ GPU timing
-def run(args):
+def run(args, workload=None, steps=None, warmup=None, side=False):
+    """One JSON record of the step on a workload (args.workload by default).
+    side=True: a secondary configuration of the default run (no CPU baseline,
+    no calibration copy, no standalone Delta pass)."""
     import torch
 
     import exact_attention_03_amd as fa
 
-    w = workloads.by_name(args.workload)
+    w = workloads.by_name(workload or args.workload)
+    n_steps = args.steps if steps is None else steps
+    n_warm = args.warmup if warmup is None else warmup
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cpu_inputs = workloads.make_inputs(w)
@@ -341,7 +346,7 @@ def run(args):
         if ev is not None:
             ev[3].record(stream)
 
-    if args.calib_copy_mib > 0:
+    if args.calib_copy_mib > 0 and not side:
         # A plain device copy of known size, for scaling HBM counters.
         n = args.calib_copy_mib * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -351,21 +356,21 @@ def run(args):
         torch.cuda.synchronize()
         del a, b
 
-    for _ in range(args.warmup):
+    for _ in range(n_warm):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(n_steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
-    for s in range(args.steps):
+    for s in range(n_steps):
         step(evs[s])
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
+    ms_step = total_ms / n_steps
     per = {name: [] for name in KERNELS}
     for e in evs:
         for i, name in enumerate(KERNELS):
@@ -378,7 +383,7 @@ def run(args):
     # The standalone Delta pass (fa_bwd_preprocess), outside the step (the
     # step's dQ pass computes the same statistics): its HBM rate.
     delta = None
-    if not w.varlen and Hkv == H:
+    if not w.varlen and Hkv == H and not side:
         stats2 = torch.empty_like(stats)
         pre = lambda: call(L.fa_bwd_preprocess(Z, H, N, D, code, code, P(o), P(do), P(lse), P(stats2), sp),  # noqa
                            "fa_bwd_preprocess")
@@ -442,8 +447,8 @@ def run(args):
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": n_steps,
+        "warmup": n_warm,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -469,9 +474,32 @@ def run(args):
         "roofline": roof,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not side:
         out["cpu_baseline"] = cpu_baseline(w, cpu_inputs, args.cpu_heads, args.cpu_workers)
     return out
+
+
+SIDE_CONFIGS = ("d64", "d256_bf16", "long_causal_bf16")
+
+
+def side_configs(args) -> dict:
+    """fwd, bwd and fwd+bwd throughput of the other full-size workloads (the
+    same step, at most 20 timed steps each), for the default run's line."""
+    import torch
+
+    res = {}
+    for name in SIDE_CONFIGS:
+        r = run(args, workload=name, steps=min(args.steps, 20), warmup=min(args.warmup, 5), side=True)
+        b = r["breakdown"]
+        res[name] = {"workload": r["config"]["workload"], "steps": r["steps"], "ms_per_step": r["ms_per_step"],
+                     "fwd_ms": b["fwd_ms"], "bwd_ms": b["bwd_ms"],
+                     "fwd_TFLOP/s": b["fwd_TFLOP/s"], "bwd_TFLOP/s": b["bwd_TFLOP/s"],
+                     "fwd_bwd_TFLOP/s": r["value"], "fwd_frac": b["fwd_frac"], "bwd_frac": b["bwd_frac"],
+                     "fwd_bwd_frac": r["frac_of_peak"],
+                     "kernels_ms": {n: k["ms"] for n, k in b["kernels"].items()}}
+        print(f"bench: {name} {r['value']} TFLOP/s", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    return res
 
 
 # ------------------------------------------------------------------ paged decode
@@ -661,7 +689,7 @@ def run_quest(args):
         if st != 0:
             raise fa.FAError(st, name, fa.last_error())
 
-    if args.calib_copy_mib > 0:
+    if args.calib_copy_mib > 0 and not side:
         # A plain device copy of known size, for scaling HBM counters.
         n = args.calib_copy_mib * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -791,7 +819,7 @@ def run_decode(args):
         if st != 0:
             raise fa.FAError(st, name, fa.last_error())
 
-    if args.calib_copy_mib > 0:
+    if args.calib_copy_mib > 0 and not side:
         # A plain device copy of known size, for scaling HBM counters.
         n = args.calib_copy_mib * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -891,7 +919,9 @@ def main(argv=None):
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     choices=sorted(workloads.WORKLOADS) + sorted(workloads.DECODE_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--cpu-heads", type=int, default=384, help="heads in the oracle timing sample")
+    ap.add_argument("--cpu-heads", type=int, default=1024, help="heads in the oracle timing sample")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="default workload only: skip the other full-size workloads in the 'configs' object")
     ap.add_argument("--cpu-workers", type=int, default=min(16, len(os.sched_getaffinity(0))))
     ap.add_argument("--cpu-decode-seqs", type=int, default=64, help="sequences in the decode oracle timing sample")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -908,6 +938,8 @@ def main(argv=None):
         out = run_quest(args) if workloads.DECODE_WORKLOADS[args.workload].topk else run_decode(args)
     else:
         out = run(args)
+        if args.workload == DEFAULT_WORKLOAD and not args.no_configs:
+            out["configs"] = side_configs(args)
     out["device"] = device_record()
     print(json.dumps(out), flush=True)
     return 0

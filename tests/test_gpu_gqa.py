@@ -95,6 +95,11 @@ def test_gqa_workload_parity_and_determinism():
     outs = _run(w, gpu)
     _compare(w, cpu, outs, [(0, 0), (w.Z - 1, w.kv_heads - 1)], w.name)
     q, k, v, do = gpu
+    from invariants import backward_ratios
+
+    ratios = backward_ratios(q, k, outs[2], do, outs[4], outs[5], outs[6], w.scale, w.dtype)
+    log(f"{w.name}: full-size identities at {ratios} of their bounds")
+    assert max(ratios.values()) <= 1.0, ratios
     dq2, dk2, dv2 = fa.backward(q, k, v, outs[2], do, outs[3], causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()
     for a, b, n in ((outs[4], dq2, "dq"), (outs[5], dk2, "dk"), (outs[6], dv2, "dv")):

@@ -104,25 +104,24 @@ EXPECTED = {
 
 def _full_size_invariants(w, gpu, outs, label):
     """Checks over every head, without the oracle, with bounds from the
-    arithmetic (u = unit roundoff of the input type: 2^-11 fp16, 2^-8 bf16):
+    arithmetic (see tests/invariants.py; u = unit roundoff of the input type):
 
-    * sum_j dV_j = sum_i dO_i per head (the rows of P sum to 1): P is rounded
-      to the input type before the product and dV on output, so per channel
-      |sum dV - sum dO| <= u (sum |dO| + sum |dV|); twice that is allowed;
+    * sum_j dV_j = sum_i dO_i, sum_j dK_j = 0 (per channel) and
+      Q^T dQ = dK^T K (per head, a D x D matrix), each within twice its
+      rounding bound;
     * every O row is a convex combination of the value rows it sees (all of
       them, or rows 0..i when causal): per channel between their minimum and
       maximum, up to 2 u max|v| (the rounded P's weights sum to 1 + O(u)).
     A skipped key unit, query tile or head breaks one of them."""
     import torch
 
+    from invariants import backward_ratios, unit_roundoff
+
     q, k, v, do = gpu
-    o32, _, _, _, _, _, dv = outs
-    u = 2.0 ** -8 if w.dtype == "bf16" else 2.0 ** -11
-    dv64, do64 = dv.double(), do.double()
-    defect = (dv64.sum(dim=2) - do64.sum(dim=2)).abs()
-    bound = 2 * u * (do64.abs().sum(dim=2) + dv64.abs().sum(dim=2)) + 1e-6
-    ratio = float((defect / bound).max())
-    del dv64, do64
+    o32, _, o16, _, dq, dk, dv = outs
+    ratios = backward_ratios(q, k, o16, do, dq, dk, dv, w.scale, w.dtype)
+    torch.cuda.empty_cache()
+    u = unit_roundoff(w.dtype)
     vf = v.float()
     if w.causal:
         hi, lo = torch.cummax(vf, dim=2).values, torch.cummin(vf, dim=2).values
@@ -130,8 +129,10 @@ def _full_size_invariants(w, gpu, outs, label):
         hi, lo = vf.amax(dim=2, keepdim=True), vf.amin(dim=2, keepdim=True)
     slack = 2 * u * vf.abs().amax(dim=(2, 3), keepdim=True)
     outside = float(torch.clamp(torch.maximum(o32 - hi, lo - o32) - slack, min=0).max())
-    log(f"{label}: full-size sum(dV) - sum(dO) at {ratio:.3f} of its bound | O outside the V hull by {outside:.2e}")
-    assert ratio <= 1.0, f"{label}: sum_j dV_j != sum_i dO_i beyond the rounding bound ({ratio})"
+    log(f"{label}: full-size identities at " + ", ".join(f"{n} {r:.3f}" for n, r in ratios.items()) +
+        f" of their bounds | O outside the V hull by {outside:.2e}")
+    for n, r in ratios.items():
+        assert r <= 1.0, f"{label}: {n} identity broken beyond its rounding bound ({r})"
     assert outside == 0.0, f"{label}: an O row leaves the convex hull of its value rows"
     assert bool(torch.isfinite(o32).all()), f"{label}: non-finite O"
 

@@ -123,6 +123,11 @@ def test_varlen_workload_parity_and_determinism():
     for name in ("dq", "dk", "dv"):
         assert acc[name].value <= GRAD_NORMWISE, (name, acc[name].value)
     q, k, v, do = gpu
+    from invariants import backward_ratios_varlen
+
+    ratios = backward_ratios_varlen(q, k, o16, do, dq, dk, dv, w.cu_seqlens, w.scale, w.dtype)
+    log(f"{w.name}: identities over every sequence at {ratios} of their bounds")
+    assert max(ratios.values()) <= 1.0, ratios
     dq2, dk2, dv2 = fa.backward_varlen(q, k, v, o16, do, lse16, cu, w.N, causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()
     for a, b_, n in ((dq, dq2, "dq"), (dk, dk2, "dk"), (dv, dv2, "dv")):
