@@ -28,7 +28,7 @@ import math
 from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32, FAError, check, last_error, lib,  # noqa: F401
                    status_name)
 
-__all__ = ["attention", "forward", "backward", "forward_varlen", "backward_varlen", "reshape_and_cache", "paged_decode",
+__all__ = ["attention", "forward", "backward", "backward_noalloc", "forward_varlen", "backward_varlen", "reshape_and_cache", "paged_decode",
            "quest_page_minmax", "quest_select", "paged_decode_sparse", "paged_decode_sources",
            "paged_attention_sources",
            "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_dq_and_stats", "workspace_bytes",
@@ -162,6 +162,26 @@ def backward(q, k, v, o, do, lse, causal=False, scale=None, workspace=None):
         else:
             st = lib().fa_bwd_gqa(Z, H, Hkv, N, D, *common)
     check(st, "fa_bwd" if Hkv == H else "fa_bwd_gqa")
+    return dq, dk, dv
+
+
+def backward_noalloc(q, k, v, o, do, lse, causal=False, scale=None):
+    """``backward`` through fa_bwd_noalloc: the row statistics live in the
+    library's fixed device array instead of a workspace (plain heads only;
+    Z*H*N <= 2^22).  Only the outputs dq, dk, dv are allocated here."""
+    torch = _torch()
+    _check_qkv(q, k, v, do, o, names=("q", "k", "v", "do", "o"))
+    if k.dtype != q.dtype or v.dtype != q.dtype or do.dtype != q.dtype:
+        raise TypeError("q, k, v, do must share one dtype")
+    Z, H, N, D = q.shape
+    if lse.shape != (Z, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 (Z, H, N) tensor on q's device")
+    with torch.cuda.device(q.device):
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        st = lib().fa_bwd_noalloc(Z, H, N, D, _dtype_code(q), _dtype_code(o), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                  _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _scale(scale, D),
+                                  int(bool(causal)), _stream(q))
+    check(st, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

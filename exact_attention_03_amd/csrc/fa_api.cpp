@@ -403,6 +403,19 @@ int bwd_impl(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int dtype,
 
 }  // namespace
 
+namespace fa {
+
+int api_error(int status, const char* message) { return fail(status, "%s", message); }
+
+int api_bwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, const void* q, const void* k,
+            const void* v, const void* o, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+            float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(Z, H, H, N, D, dtype, o_dtype, q, k, v, o, dout, lse, dq, dk, dv, scale, causal, workspace,
+                  workspace_bytes, stream);
+}
+
+}  // namespace fa
+
 extern "C" {
 
 int fa_bwd_dq_and_stats(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, const void* q,

@@ -149,6 +149,14 @@ hipError_t launch_bwd_dq(const BwdArgs& a);
 // Resident dK/dV workgroups per CU for (D, dtype), from the occupancy API.
 hipError_t dkdv_blocks_per_cu(int D, int dtype, int* out);
 
+// Entry points of the C ABI layer for other translation units: record an
+// error message (returns status), and fa_bwd itself (argument checks, both
+// stages) with the caller's workspace.
+int api_error(int status, const char* message);
+int api_bwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype, const void* q, const void* k,
+            const void* v, const void* o, const void* dout, const float* lse, void* dq, void* dk, void* dv,
+            float scale, int causal, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 // Queries per forward workgroup and keys per forward K/V tile.
 constexpr int kFwdQueries = 128;
 constexpr int fwd_keys(int D) { return D == 64 ? 64 : 32; }

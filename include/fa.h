@@ -114,6 +114,26 @@ int fa_bwd(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype,
            hipStream_t stream);
 
 /*
+ * fa_bwd without the workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The row statistics live in a fixed array of the
+ * library's own device memory (2 * FA_BWD_NOALLOC_MAX_ROWS float32 = 32 MiB on
+ * every GPU the library runs on, held until the process ends), so the call
+ * allocates and frees nothing.
+ *   Limit: Z*H*N <= FA_BWD_NOALLOC_MAX_ROWS query rows; larger problems return
+ *   FA_ERR_UNSUPPORTED before any work is enqueued.
+ * Arguments, results (bitwise) and other errors are those of fa_bwd.  All
+ * calls on one GPU share that GPU's array, which keeps the last call's
+ * statistics: calls that overlap on one GPU (on other streams or from other
+ * threads) race, and the caller must serialise them.
+ */
+#define FA_BWD_NOALLOC_MAX_ROWS ((int64_t)1 << 22)
+int fa_bwd_noalloc(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, int o_dtype,
+                   const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   float scale, int causal, hipStream_t stream);
+
+/*
  * Stage 1 of the backward: the per-row statistics of the gradient stages.
  *   o     : (Z,H,N,D) o_dtype;  dout : (Z,H,N,D) dtype;
  *   lse   : (Z,H,N) float32 from fa_fwd (read);

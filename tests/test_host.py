@@ -106,6 +106,17 @@ def test_bwd_workspace_rules(fa):
 
 
 @_NO_GPU
+def test_noalloc_backward_refuses_rows_past_its_array(fa):
+    """fa_bwd_noalloc refuses a problem whose row statistics would not fit its
+    fixed array before touching the device."""
+    lib = fa.lib()
+    limit = 1 << 22
+    assert lib.fa_bwd_noalloc(1, 1, limit + 1, 64, 0, 0, *([P] * 9), 0.125, 0, None) == 2
+    assert "FA_BWD_NOALLOC_MAX_ROWS" in fa.last_error()
+    assert lib.fa_bwd_noalloc(4, 1 << 10, 1025, 64, 0, 0, *([P] * 9), 0.125, 0, None) == 2
+
+
+@_NO_GPU
 def test_stage_argument_errors(fa):
     lib = fa.lib()
     assert lib.fa_bwd_preprocess(1, 1, 64, 64, 0, 1, P, P, P, P, None) == 1    # o_dtype bf16 with f16
