@@ -38,6 +38,8 @@ PEAK_MFMA_F16_TFLOPS = 2516.6   # fp16 / bf16 dense MFMA
 PEAK_HBM_GBS = 8000.0           # HBM3E
 DEFAULT_WORKLOAD = "d128_causal"
 KERNELS = ("fa_fwd", "fa_bwd_dq", "fa_bwd_dkdv")  # the step, in launch order
+# The step with the fused per-head backward: statistics pass, then one pass for dQ, dK, dV.
+KERNELS_FUSED = ("fa_fwd", "fa_bwd_pre", "fa_bwd_fused")
 # Source files each kernel is built from; a stored traffic measurement is only
 # reported while these are unchanged.
 KERNEL_SOURCES = {
@@ -45,6 +47,7 @@ KERNEL_SOURCES = {
     "fa_bwd_pre": ("fa_bwd.hip", "fa_device.h", "fa_kernels.h"),
     "fa_bwd_dkdv": ("fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_schedule.h"),
     "fa_bwd_dq": ("fa_bwd.hip", "fa_device.h", "fa_kernels.h", "fa_schedule.h"),
+    "fa_bwd_fused": ("fa_bwd_fused.hip", "fa_device.h", "fa_kernels.h", "fa_schedule.h"),
     "fa_paged_decode": ("fa_paged.hip", "fa_device.h", "fa_kernels.h"),
     "fa_paged_decode_sparse": ("fa_paged.hip", "fa_device.h", "fa_kernels.h"),
     "fa_paged_decode_sources": ("fa_paged.hip", "fa_device.h", "fa_kernels.h"),
@@ -79,6 +82,7 @@ def kernel_work(w, o_bytes: int):
     rows = w.H * w.T if w.varlen else w.Z * w.H * w.N
     return {
         "fa_fwd": ("mfma", hf, "flop"),
+        "fa_bwd_fused": ("mfma", 2.5 * hf, "flop"),
         "fa_bwd_dkdv": ("mfma", 2.0 * hf, "flop"),
         "fa_bwd_dq": ("mfma", 0.5 * hf, "flop"),
         "fa_bwd_pre": ("hbm", float(rows * (w.D * o_bytes + w.D * 2 + 12)), "byte"),
@@ -112,7 +116,7 @@ def executed_over_counted(w) -> dict:
     fwd = sum(_computed_pairs(n, 32, bk, w.causal) for n in lengths) / counted
     dkdv = sum(_computed_pairs(n, 32, 32, w.causal) for n in lengths) / counted
     return {"fa_fwd": round(fwd * (1.5 if w.D == 256 else 1.0), 4), "fa_bwd_dq": round(3 * fwd, 4),
-            "fa_bwd_dkdv": round(dkdv, 4)}
+            "fa_bwd_dkdv": round(dkdv, 4), "fa_bwd_fused": round(dkdv, 4)}
 
 
 def _code_only(text: str) -> str:
@@ -156,6 +160,30 @@ def stored_traffic(kernel: str, workload: str):
         return None
     try:
         return float(kv["fetch_bytes"]) + float(kv["write_bytes"])
+    except (KeyError, ValueError):
+        return None
+
+
+def stored_mfma_busy(kernel: str, workload: str):
+    """Share of the dispatch's SIMD cycles in which the matrix unit was busy,
+    from a committed rocprofv3 counter summary
+    (profiles/mfma_<kernel>_<workload>.txt: SQ_VALU_MFMA_BUSY_CYCLES over
+    GRBM_GUI_ACTIVE per XCD x CUs x 4), or None when absent or when the
+    kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"mfma_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if "=" in line:
+                a, b = line.split("=", 1)
+                kv[a.strip()] = b.strip()
+    if kv.get("source_hash") != sources_hash(kernel):
+        return None
+    try:
+        return float(kv["mfma_busy"])
     except (KeyError, ValueError):
         return None
 
@@ -264,10 +292,12 @@ def cpu_baseline(w, cpu_inputs, n_heads: int, workers: int):
 
 
 # ------------------------------------------------------------------ GPU timing
-def run(args, workload=None, steps=None, warmup=None, side=False):
+def run(args, workload=None, steps=None, warmup=None, side=False, bwd=None):
     """One JSON record of the step on a workload (args.workload by default).
     side=True: a secondary configuration of the default run (no CPU baseline,
-    no calibration copy, no standalone Delta pass)."""
+    no calibration copy, no standalone Delta pass).  bwd: "split" (dQ pass
+    with the statistics, then the dK/dV pass) or "fused" (statistics pass,
+    then the fused per-head pass); args.bwd by default."""
     import torch
 
     import exact_attention_03_amd as fa
@@ -275,6 +305,8 @@ def run(args, workload=None, steps=None, warmup=None, side=False):
     w = workloads.by_name(workload or args.workload)
     n_steps = args.steps if steps is None else steps
     n_warm = args.warmup if warmup is None else warmup
+    variant = bwd or args.bwd
+    kernels = KERNELS_FUSED if variant == "fused" else KERNELS
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cpu_inputs = workloads.make_inputs(w)
@@ -315,9 +347,31 @@ def run(args, workload=None, steps=None, warmup=None, side=False):
         if ev is not None:
             ev[3].record(stream)
 
+    part = None
+    if variant == "fused":
+        if w.varlen or Hkv != H:
+            raise SystemExit("bench.py: the fused backward takes plain heads and dense batches only")
+        part = torch.empty((L.fa_bwd_fused_workspace_bytes(Z, H, N, D) // 4,), dtype=torch.float32, device=dev)
+
+    def step_fused(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        call(L.fa_fwd(Z, H, N, D, code, code, P(q), P(k), P(v), P(o), P(lse), scale, causal, sp), "fa_fwd")
+        if ev is not None:
+            ev[1].record(stream)
+        call(L.fa_bwd_preprocess(Z, H, N, D, code, code, P(o), P(do), P(lse), P(stats), sp), "fa_bwd_preprocess")
+        if ev is not None:
+            ev[2].record(stream)
+        call(L.fa_bwd_fused(Z, H, N, D, code, P(q), P(k), P(v), P(do), P(stats), P(dq), P(dk), P(dv), scale, causal,
+                            0, P(part), part.numel() * 4, sp), "fa_bwd_fused")
+        if ev is not None:
+            ev[3].record(stream)
+
     def step(ev=None):
         # Grouped key/value heads go through the *_gqa forms of the same calls,
         # variable-length batches through the *_varlen forms.
+        if variant == "fused":
+            return step_fused(ev)
         if w.varlen:
             return step_varlen(ev)
         if ev is not None:
@@ -360,7 +414,7 @@ def run(args, workload=None, steps=None, warmup=None, side=False):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(n_steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)] for _ in range(n_steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -371,9 +425,9 @@ def run(args, workload=None, steps=None, warmup=None, side=False):
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / n_steps
-    per = {name: [] for name in KERNELS}
+    per = {name: [] for name in kernels}
     for e in evs:
-        for i, name in enumerate(KERNELS):
+        for i, name in enumerate(kernels):
             per[name].append(e[i].elapsed_time(e[i + 1]))
     avg = {n: sum(x) / len(x) for n, x in per.items()}
     step_times = sorted(e[0].elapsed_time(e[-1]) for e in evs)  # first launch to last completion
@@ -404,13 +458,13 @@ def run(args, workload=None, steps=None, warmup=None, side=False):
 
     ff = fwd_flops(w)
     fwd_ms = avg["fa_fwd"]
-    bwd_ms = avg["fa_bwd_dq"] + avg["fa_bwd_dkdv"]
+    bwd_ms = sum(avg[n] for n in kernels[1:])
     value = 3.5 * ff / (ms_step * 1e-3) / 1e12
     work = kernel_work(w, o.element_size())
     ratio = executed_over_counted(w)
     n_cu = fa.device_info(D)[0]
     kern = {}
-    for name in KERNELS:
+    for name in kernels:
         bound, amount, unit = work[name]
         t = avg[name] * 1e-3
         if bound == "mfma":
@@ -418,6 +472,9 @@ def run(args, workload=None, steps=None, warmup=None, side=False):
             kern[name] = {"ms": round(avg[name], 4), "bound": "mfma", "TFLOP/s": round(ach, 1),
                           "frac": round(ach / PEAK_MFMA_F16_TFLOPS, 4), "executed_over_counted": ratio[name],
                           "executed_TFLOP/s": round(ach * ratio[name], 1)}
+            busy = stored_mfma_busy(name, w.name)
+            if busy is not None:
+                kern[name]["mfma_busy"] = busy
             clk = stored_clock(name, w.name)
             if clk is not None:
                 # the dense fp16 rate at the clock the kernel actually ran at: CUs x clock x 4096
@@ -428,7 +485,7 @@ def run(args, workload=None, steps=None, warmup=None, side=False):
             ach = amount / t / 1e9
             kern[name] = {"ms": round(avg[name], 4), "bound": "hbm", "GB/s": round(ach, 1),
                           "frac": round(ach / PEAK_HBM_GBS, 4)}
-    dom = max(KERNELS, key=lambda n: avg[n])
+    dom = max(kernels, key=lambda n: avg[n])
     bound, amount, unit = work[dom]
     t = avg[dom] * 1e-3
     traffic = stored_traffic(dom, w.name)
@@ -462,6 +519,7 @@ def run(args, workload=None, steps=None, warmup=None, side=False):
                    "Z": Z, "H": H, "Hkv": Hkv, "N": N, "D": D, "causal": bool(w.causal), "seed": w.seed},
         "frac_of_peak": round(value / PEAK_MFMA_F16_TFLOPS, 4),
         "breakdown": {
+            "bwd_variant": variant,
             "step_ms": spread,
             "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
             "fwd_TFLOP/s": round(ff / (fwd_ms * 1e-3) / 1e12, 1),
@@ -480,6 +538,34 @@ def run(args, workload=None, steps=None, warmup=None, side=False):
 
 
 SIDE_CONFIGS = ("d64", "d256_bf16", "long_causal_bf16")
+AB_CONFIGS = ("d128_causal", "long_causal_bf16")
+
+
+def backward_ab(args, main) -> dict:
+    """The whole backward both ways on the A/B workloads: the two-pass form
+    (dQ pass with the statistics, then dK/dV) against the fused per-head form
+    (statistics pass, then dQ/dK/dV in one pass), at most 20 timed steps
+    each; the main line's own variant is taken from it."""
+    import torch
+
+    res = {}
+    for name in AB_CONFIGS:
+        row = {}
+        for variant in ("split", "fused"):
+            if name == main["config"]["workload"].split(":")[0] and variant == main["breakdown"]["bwd_variant"]:
+                r = main
+            else:
+                r = run(args, workload=name, steps=min(args.steps, 20), warmup=min(args.warmup, 5), side=True,
+                        bwd=variant)
+            b = r["breakdown"]
+            row[variant] = {"bwd_ms": b["bwd_ms"], "bwd_TFLOP/s": b["bwd_TFLOP/s"], "bwd_frac": b["bwd_frac"],
+                            "kernels_ms": {n: k["ms"] for n, k in b["kernels"].items() if n != "fa_fwd"}}
+            torch.cuda.empty_cache()
+        row["faster"] = min(("split", "fused"), key=lambda v: row[v]["bwd_ms"])
+        res[name] = row
+        print(f"bench: backward A/B {name}: split {row['split']['bwd_ms']} ms, fused {row['fused']['bwd_ms']} ms",
+              file=sys.stderr, flush=True)
+    return res
 
 
 def side_configs(args) -> dict:
@@ -864,7 +950,7 @@ def run_decode(args):
     splits = max(1, ws_bytes // (4 * w.B * T * w.H * (w.D + 1))) if ws_bytes else 1
     ach = dec_bytes / (dec_ms * 1e-3) / 1e9
     metric = ("paged decode attention (cache write + decode) HBM GB/s on 1 MI355X" if T == 1 else
-              f"speculative verification over a paged cache (cache write of {T} tokens + attention of {T} causal "
+              f"causal chunk over a paged cache (cache write of {T} tokens + attention of {T} causal "
               f"query tokens per sequence) HBM GB/s on 1 MI355X")
     out = {
         "metric": metric,
@@ -920,6 +1006,8 @@ def main(argv=None):
                     choices=sorted(workloads.WORKLOADS) + sorted(workloads.DECODE_WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-heads", type=int, default=1024, help="heads in the oracle timing sample")
+    ap.add_argument("--bwd", choices=("split", "fused"), default="split",
+                    help="backward form of the step: dQ pass + dK/dV pass, or statistics + fused per-head pass")
     ap.add_argument("--no-configs", action="store_true",
                     help="default workload only: skip the other full-size workloads in the 'configs' object")
     ap.add_argument("--cpu-workers", type=int, default=min(16, len(os.sched_getaffinity(0))))
@@ -940,6 +1028,7 @@ def main(argv=None):
         out = run(args)
         if args.workload == DEFAULT_WORKLOAD and not args.no_configs:
             out["configs"] = side_configs(args)
+            out["bwd_ab"] = backward_ab(args, out)
     out["device"] = device_record()
     print(json.dumps(out), flush=True)
     return 0

@@ -31,7 +31,7 @@ from ._lib import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_F32, FAError, check, la
 __all__ = ["attention", "forward", "backward", "backward_noalloc", "forward_varlen", "backward_varlen", "reshape_and_cache", "paged_decode",
            "quest_page_minmax", "quest_select", "paged_decode_sparse", "paged_decode_sources",
            "paged_attention_sources",
-           "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_dq_and_stats", "workspace_bytes",
+           "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_dq_and_stats", "bwd_fused", "workspace_bytes",
            "device_info", "dkdv_schedule", "fwd_tile_pairs", "FAError", "lib"]
 
 
@@ -267,10 +267,14 @@ def reshape_and_cache(key, value, slot_mapping, k_cache, v_cache):
     nb, bs = k_cache.shape[0], k_cache.shape[3]
     for t, n, shp in ((key, "key", (T, Hkv, D)), (value, "value", (T, Hkv, D)),
                       (k_cache, "k_cache", (nb, Hkv, D // 8, bs, 8)), (v_cache, "v_cache", (nb, Hkv, D, bs))):
-        if not t.is_cuda or tuple(t.shape) != shp or not t.is_contiguous() or t.dtype != key.dtype:
-            raise ValueError(f"{n} must be a contiguous GPU tensor of shape {shp} and dtype {key.dtype}")
-    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,) or not slot_mapping.is_cuda:
-        raise ValueError("slot_mapping must be an int64 GPU tensor of shape (num_tokens,)")
+        if (not t.is_cuda or tuple(t.shape) != shp or not t.is_contiguous() or t.dtype != key.dtype
+                or t.device != key.device):
+            raise ValueError(f"{n} must be a contiguous GPU tensor of shape {shp}, dtype {key.dtype} and on "
+                             f"{key.device}")
+    # The kernel reads slot i at element i: a strided view would map tokens to the wrong slots.
+    if (slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,) or not slot_mapping.is_cuda
+            or not slot_mapping.is_contiguous() or slot_mapping.device != key.device):
+        raise ValueError(f"slot_mapping must be a contiguous int64 GPU tensor of shape (num_tokens,) on {key.device}")
     with torch.cuda.device(key.device):
         st = lib().fa_reshape_and_cache(T, Hkv, D, bs, nb, _dtype_code(key), _ptr(key), _ptr(value),
                                         _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), _stream(key))
@@ -520,6 +524,29 @@ def bwd_dkdv(q, k, v, do, stats, causal=False, scale=None, num_programs=0):
                                _stream(q))
     check(st, "fa_bwd_dkdv")
     return dk, dv
+
+
+def bwd_fused(q, k, v, do, stats, causal=False, scale=None, num_programs=0, workspace=None):
+    """dQ, dK, dV from the fused per-head pass (fa_bwd_fused); stats from
+    ``bwd_preprocess``.  workspace: optional float32 GPU tensor of at least
+    fa_bwd_fused_workspace_bytes / 4 elements (the heads' dQ partials)."""
+    torch = _torch()
+    _check_qkv(q, k, v, do, names=("q", "k", "v", "do"))
+    Z, H, N, D = q.shape
+    with torch.cuda.device(q.device):
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        _check_stats(stats, Z, H, N)
+        nbytes = int(lib().fa_bwd_fused_workspace_bytes(Z, H, N, D))
+        if workspace is None:
+            workspace = torch.empty((max(1, nbytes // 4),), dtype=torch.float32, device=q.device)
+        if (workspace.dtype != torch.float32 or not workspace.is_cuda or not workspace.is_contiguous()
+                or workspace.device != q.device):
+            raise ValueError("workspace must be a contiguous float32 GPU tensor on q's device")
+        st = lib().fa_bwd_fused(Z, H, N, D, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(stats),
+                                _ptr(dq), _ptr(dk), _ptr(dv), _scale(scale, D), int(bool(causal)), int(num_programs),
+                                _ptr(workspace), workspace.numel() * 4, _stream(q))
+    check(st, "fa_bwd_fused")
+    return dq, dk, dv
 
 
 def bwd_dq(q, k, v, do, stats, causal=False, scale=None):

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_paged.hip", "fa_quest.hip", "fa_noalloc.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_paged.hip", "fa_quest.hip", "fa_noalloc.hip", "fa_bwd_fused.hip"]
 ARCH = "gfx950"
 
 COMMON = [

@@ -45,6 +45,9 @@ SIGNATURES = {
     "fa_bwd_preprocess": (_int, [_i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp]),
     "fa_bwd_dkdv": (_int, [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                            _f32, _int, _int, _vp]),
+    "fa_bwd_fused_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "fa_bwd_fused": (_int, [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _int, _int,
+                            _vp, _sz, _vp]),
     "fa_bwd_dq": (_int, [_i64, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _int, _vp]),
     "fa_bwd_dq_and_stats": (_int, [_i64, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    _f32, _int, _vp]),

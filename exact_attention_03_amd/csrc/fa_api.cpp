@@ -148,7 +148,8 @@ struct DeviceFacts {
   std::once_flag once;
   hipError_t err = hipSuccess;
   int cus = 0;
-  int dkdv_per_cu[3][2] = {};  // [D index][dtype]
+  int dkdv_per_cu[3][2] = {};   // [D index][dtype]
+  int fused_per_cu[3][2] = {};  // [D index][dtype]
 };
 constexpr int kMaxDevices = 64;
 DeviceFacts g_facts[kMaxDevices];
@@ -170,6 +171,8 @@ int device_facts(DeviceFacts** out) {
     for (int di = 0; di < 3; ++di)
       for (int dt = 0; dt < 2; ++dt) {
         f.err = fa::dkdv_blocks_per_cu(Ds[di], dt, &f.dkdv_per_cu[di][dt]);
+        if (f.err != hipSuccess) return;
+        f.err = fa::fused_blocks_per_cu(Ds[di], dt, &f.fused_per_cu[di][dt]);
         if (f.err != hipSuccess) return;
       }
   });
@@ -317,6 +320,40 @@ int fa_bwd_dkdv(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, const voi
                 const void* v, const void* dout, const float* stats, void* dk, void* dv, float scale,
                 int causal, int num_programs, hipStream_t stream) {
   return dkdv_impl(Z, H, H, N, D, dtype, q, k, v, dout, stats, dk, dv, scale, causal, num_programs, stream);
+}
+
+size_t fa_bwd_fused_workspace_bytes(int64_t Z, int64_t H, int64_t N, int64_t D) {
+  if (Z <= 0 || H <= 0 || N <= 0 || D <= 0) return 0;
+  return (size_t)(Z * H) * (size_t)((N + 31) / 32 * 32) * (size_t)D * sizeof(float);
+}
+
+int fa_bwd_fused(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, const void* q, const void* k,
+                 const void* v, const void* dout, const float* stats, void* dq, void* dk, void* dv, float scale,
+                 int causal, int num_programs, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error.clear();
+  const Shape s{Z, H, N, D};
+  FA_TRY(validate_bwd_common(s, dtype, q, k, v, dout, stats, scale, causal));
+  if (num_programs < 0) return fail(FA_ERR_INVALID_ARGUMENT, "num_programs must be >= 0 (got %d)", num_programs);
+  if (s.empty()) return FA_OK;
+  FA_TRY(check_ptr(dq, "dq"));
+  FA_TRY(check_ptr(dk, "dk"));
+  FA_TRY(check_ptr(dv, "dv"));
+  FA_TRY(check_ptr(workspace, "workspace"));
+  const size_t need = fa_bwd_fused_workspace_bytes(Z, H, N, D);
+  if (workspace_bytes < need)
+    return fail(FA_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu bytes needed",
+                workspace_bytes, need);
+  if (num_programs == 0) {
+    DeviceFacts* f = nullptr;
+    FA_TRY(device_facts(&f));
+    num_programs = f->cus * f->fused_per_cu[d_index(D)][dtype];
+  }
+  fa::BwdArgs a{};
+  a.Z = Z; a.H = H; a.Hkv = H; a.N = N; a.D = D; a.dtype = dtype;
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.stats = const_cast<float*>(stats);
+  a.dq = dq; a.dk = dk; a.dv = dv; a.scale = scale; a.causal = causal; a.num_programs = num_programs;
+  a.partial = static_cast<float*>(workspace); a.stream = stream;
+  return finish(fa::launch_bwd_fused(a), stream, "fa_bwd_fused launch");
 }
 
 int fa_bwd_dq(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype, const void* q, const void* k,

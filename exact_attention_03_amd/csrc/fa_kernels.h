@@ -42,6 +42,8 @@ struct BwdArgs {
   hipStream_t stream;
   const int* cu_seqlens = nullptr;  // as in FwdArgs
   int64_t T = 0;
+  // Fused per-head backward: the heads' fp32 dQ partials, Z*H*ceil(N/32)*32*D floats.
+  float* partial = nullptr;
   // Query rows of every head and problem together: Z*H*N dense, H*T packed
   // (the offset of the second plane of stats).
   int64_t rows() const { return cu_seqlens ? H * T : Z * H * N; }
@@ -148,6 +150,11 @@ hipError_t launch_bwd_dq(const BwdArgs& a);
 
 // Resident dK/dV workgroups per CU for (D, dtype), from the occupancy API.
 hipError_t dkdv_blocks_per_cu(int D, int dtype, int* out);
+
+// The fused per-head backward (dQ, dK, dV in one pass, persistent programs
+// over heads) and its resident workgroups per CU.
+hipError_t launch_bwd_fused(const BwdArgs& a);
+hipError_t fused_blocks_per_cu(int D, int dtype, int* out);
 
 // Entry points of the C ABI layer for other translation units: record an
 // error message (returns status), and fa_bwd itself (argument checks, both

@@ -171,6 +171,35 @@ int fa_bwd_dq(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype,
               hipStream_t stream);
 
 /*
+ * dQ, dK and dV in one pass: the persistent-program form of [FA-Ascend] §五.
+ * A grid of `num_programs` workgroups (0 = one per resident slot on the
+ * device) claims heads with a fixed stride; a program computes everything of
+ * its heads, walking the key tiles in order with dK/dV of the key tile in
+ * registers and adding each query tile's dQ contribution to an fp32 partial
+ * of the head kept in `workspace`; the key tile holding a query tile's last
+ * visible key writes its finished dQ rows instead.  Five matrix products per
+ * (query tile, key tile), against seven for fa_bwd_dkdv + fa_bwd_dq.  Each
+ * dQ, dK and dV element has one writer; no atomics; the scratch is O(N*D) per
+ * head, never N*N ([FA-Ascend] §二).
+ *   q, k, v, dout   : (Z,H,N,D) dtype (read);  stats : (2,Z,H,N) float32
+ *                     from fa_bwd_preprocess (read);
+ *   dq, dk, dv      : (Z,H,N,D) dtype (written once);
+ *   workspace       : device buffer of at least
+ *                     fa_bwd_fused_workspace_bytes(Z, H, N, D) bytes
+ *                     (Z*H*ceil(N/32)*32*D float32: the heads' dQ partials;
+ *                     contents on return are unspecified).
+ * The result does not depend on num_programs (bitwise) and equals the
+ * two-pass result to rounding (dQ's fp32 summation order differs).
+ * Plain heads and dense batches only.  Errors as for fa_bwd_dkdv.
+ */
+size_t fa_bwd_fused_workspace_bytes(int64_t Z, int64_t H, int64_t N, int64_t D);
+int fa_bwd_fused(int64_t Z, int64_t H, int64_t N, int64_t D, int dtype,
+                 const void* q, const void* k, const void* v, const void* dout,
+                 const float* stats, void* dq, void* dk, void* dv, float scale,
+                 int causal, int num_programs, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+/*
  * dQ together with the row statistics ([FA-Ascend] §二): the dQ pass computes
  * Delta for its own query rows from o and dout (with the summation order of
  * fa_bwd_preprocess, so the values are bitwise the same) and lse * log2(e)

@@ -31,7 +31,7 @@ def test_executed_ratios():
     assert r["fa_fwd"] == round(528 / 512, 4) and r["fa_bwd_dkdv"] == round(528 / 512, 4)
     assert r["fa_bwd_dq"] == round(3 * 528 / 512, 4)
     r = bench.executed_over_counted(workloads.WORKLOADS["d256_bf16"])
-    assert r == {"fa_fwd": 1.5, "fa_bwd_dq": 3.0, "fa_bwd_dkdv": 1.0}
+    assert r == {"fa_fwd": 1.5, "fa_bwd_dq": 3.0, "fa_bwd_dkdv": 1.0, "fa_bwd_fused": 1.0}
 
 
 def test_two_source_bytes_add_the_window():
