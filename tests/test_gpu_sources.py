@@ -293,7 +293,7 @@ def test_one_query_row_is_the_decode_call():
 
 
 def test_verify_workload():
-    """The speculative verification workload (64 sequences of 512..16000
+    """The causal-chunk workload (64 sequences of 512..16000
     tokens, 4 causal query tokens each) on its shortest, longest and one
     middle sequence."""
     import torch

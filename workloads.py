@@ -223,7 +223,7 @@ DECODE_WORKLOADS = {
     # 64 sequences of 512..16000 tokens (about 8K on average), 32 query heads over 8
     # key/value heads, D = 128, pages of 16 tokens
     "decode_gqa_bf16": DecodeWorkload("decode_gqa_bf16", 11, 64, 32, 8, 128, 16, 512, 16000, "bf16"),
-    # speculative verification on the same batch and cache: the last 4 tokens of every context
+    # a causal chunk on the same batch and cache: the last 4 tokens of every context
     # are written to the cache and attend, each causally, to the context up to themselves
     "verify_gqa_bf16": DecodeWorkload("verify_gqa_bf16", 11, 64, 32, 8, 128, 16, 512, 16000, "bf16", 0, 0, 4),
     # the same batch and cache with 64 pages (1024 tokens) kept per context by the query-aware selection
