@@ -208,27 +208,9 @@ void fa_bwd_fused_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
         }
       };
 
-      // Query tile i0 + f from stage cs (the copy of the next goes to ns); its
-      // dS^T goes to dsw, after the previous tile's dQ is taken from dsp.
-      int cf = 0;
-      auto item = [&](const char* cs, char* ns, char* dsw, const char* dsp) {
-        // The tile has landed for every wave; every wave is done with the last
-        // one, including its reads of the dS^T buffer written below, and has
-        // written the previous tile's dS^T rows.
-        wait_vmem();
-        __syncthreads();
-        const int f = cf++;
-        if (f + 1 < nq) issue_item(i0 + f + 1, ns);
-        if (f > 0) {
-          if constexpr (!C::PREFETCH) dq_load(i0 + f - 1);
-          dq_finish(i0 + f - 1, dsp);
-        }
-        if constexpr (C::PREFETCH) dq_load(i0 + f);
-        const int qb0 = (i0 + f) * BQ;
-        // Causal: a tile whose last query precedes the wave's first key is
-        // empty for this wave (its dS^T rows are never read: the dQ product
-        // skips that key block).
-        if (CAUSAL && qb0 + 31 < kw0) return;
+      // This wave's products for the query tile in stage cs: S, dP, P, dS,
+      // dV and dK, with its dS^T rows written to dsw.
+      auto products = [&](const char* cs, char* dsw, int qb0) {
         const char* qt = cs;
         const char* dot = qt + C::QT_BYTES;
         const float* stats = reinterpret_cast<const float*>(qt + C::STAT_OFF);
@@ -282,6 +264,35 @@ void fa_bwd_fused_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
             dka[db] = mfma32<T>(lds_read_tr_operand<BQ>(qt, trd, 16 * t2, db), dsf, dka[db]);
           }
         }
+      };
+
+      // Query tile i0 + f from stage cs (the copy of the next goes to ns); its
+      // dS^T goes to dsw; the previous tile's dQ is taken from dsp.
+      int cf = 0;
+      auto item = [&](const char* cs, char* ns, char* dsw, const char* dsp) {
+        // The tile has landed for every wave; every wave is done with the last
+        // one, including its reads of the dS^T buffer written below, and has
+        // written the previous tile's dS^T rows.
+        wait_vmem();
+        __syncthreads();
+        const int f = cf++;
+        if (f + 1 < nq) issue_item(i0 + f + 1, ns);
+        // The previous tile's dQ, then this tile's partial on its way (its
+        // latency hidden by this tile's products).  Putting the previous dQ
+        // after the products on half of the waves (so that the two waves of a
+        // SIMD start a tile in different phases) measured slower: 1.35 ->
+        // 1.45 ms on the 128 x 8 x 1024 x 128 causal workload, as its partial
+        // stores then sit just before the next barrier's wait.
+        if (f > 0) {
+          if constexpr (!C::PREFETCH) dq_load(i0 + f - 1);
+          dq_finish(i0 + f - 1, dsp);
+        }
+        if constexpr (C::PREFETCH) dq_load(i0 + f);
+        const int qb0 = (i0 + f) * BQ;
+        // Causal: a tile whose last query precedes the wave's first key is
+        // empty for this wave (its dS^T rows are never read: the dQ product
+        // skips that key block).
+        if (!(CAUSAL && qb0 + 31 < kw0)) products(cs, dsw, qb0);
       };
       for (int f = 0; f < nq; f += 2) {
         item(st0, st1, ds0, ds1);

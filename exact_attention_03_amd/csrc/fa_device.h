@@ -310,32 +310,32 @@ FA_DEV u32x4 lds_read_tr_operand(const char* tile, const TrRead<R>& b, int k0, i
 
 // Transposed operand of a 16x16x32 product with the contraction index along
 // tile rows: lane l (g = l / 16) receives T[k0 + 8g + i][c0 + l % 16] for
-// i = 0..7 (k0 a multiple of 16, c0 a multiple of 16), the A layout
-// A[m = l % 16][k = 8g + i] (or the B layout B[k = 8g + i][n = l % 16]) with
-// m (n) = column c0 + l % 16.  Two transposing reads: fetching lane
-// 16g + 4r + c takes the 8 bytes at row k0 + 8g + r (then 8g + 4 + r),
-// columns c0 + 4c .. c0 + 4c + 3.  The lane-dependent part of an address
-// only depends on the parity of c0 / 16 and on which of the two reads it is,
-// so a lane keeps four bases and every read is a base plus a compile-time
-// offset.
+// i = 0..7 (k0, c0 multiples of 16), the A layout A[m = l % 16][k = 8g + i]
+// (or the B layout B[k = 8g + i][n = l % 16]) with m (n) = column
+// c0 + l % 16.  Two transposing reads: fetching lane 16g + 4r + c takes the 8
+// bytes at row k0 + 8g + r (then 8g + 4 + r), columns c0 + 4c .. c0 + 4c + 3;
+// lanes 0-31 (and 32-63) then cover rows of two swizzle classes, each bank
+// once.  The lane-dependent part of an address only depends on the parity of
+// c0 / 16 and on which of the two reads it is, so a lane keeps four bases (in
+// named registers: an indexed array would be placed in LDS) and every read is
+// a base plus a compile-time offset.
 template <int R>
 struct TrRead16 {
-  int b[2][2];  // [parity of c0 / 16][first / second read]
-  FA_HD explicit TrRead16(int lane) {
+  int b00, b01, b10, b11;  // b<parity of c0 / 16><first / second read>
+  FA_HD static int base(int lane, int e, int x) {
     const int g = lane >> 4, r = (lane >> 2) & 3, c = lane & 3;
-    for (int e = 0; e < 2; ++e)
-      for (int x = 0; x < 2; ++x) {
-        // column 16 e + 4 c of a 32-column group lies in chunk 2 e + c / 2
-        b[e][x] = CmTile<R>::off(8 * g + 4 * x + r, 2 * e + (c >> 1)) + 8 * (c & 1);
-      }
+    // column 16 e + 4 c of a 32-column group lies in chunk 2 e + c / 2
+    return CmTile<R>::off(8 * g + 4 * x + r, 2 * e + (c >> 1)) + 8 * (c & 1);
   }
+  FA_HD explicit TrRead16(int lane)
+      : b00(base(lane, 0, 0)), b01(base(lane, 0, 1)), b10(base(lane, 1, 0)), b11(base(lane, 1, 1)) {}
 };
 template <int R>
 FA_DEV u32x4 lds_read_tr16(const char* tile, const TrRead16<R>& t, int k0, int c0) {
-  const int e = (c0 >> 4) & 1;
+  const bool odd = (c0 >> 4) & 1;
   const int o = k0 * 64 + (c0 >> 5) * CmTile<R>::GB;
-  const u32x2 lo = lds_read_tr(tile, t.b[e][0] + o);
-  const u32x2 hi = lds_read_tr(tile, t.b[e][1] + o);
+  const u32x2 lo = lds_read_tr(tile, (odd ? t.b10 : t.b00) + o);
+  const u32x2 hi = lds_read_tr(tile, (odd ? t.b11 : t.b01) + o);
   return u32x4{lo.x, lo.y, hi.x, hi.y};
 }
 
