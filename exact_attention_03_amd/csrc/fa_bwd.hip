@@ -207,7 +207,7 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
         dma16(rv, vsm + blk * 1024, (uint32_t)(((k0 + row) * D + 8 * chunk) * 2));
       }
     }
-    issue_qtile(0, i0, st0);
+    issue_qtile(0, n_qtiles - 1, st0);
 
     // K (and V) rows of this wave's keys, B-operand layout (lane = key, k = d).
     u32x4 kf[C::KSTEPS];
@@ -232,8 +232,12 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     const char* vbase = vsm + kRowBlockBytes * w;
     const TrRead<C::BQ> trd(lane);
 
-    // Item (member cm, query tile i0 + cit), read from stage cs; the copy of
-    // the next item goes to ns.
+    // Item (member cm, query tile n_qtiles - 1 - cit), read from stage cs; the
+    // copy of the next item goes to ns.  Query tiles are taken from the last
+    // down: the units of one head (which run at the same time on one XCD)
+    // then read the same query tiles at about the same time and share them
+    // through L2 (with the causal mask they start on different first tiles
+    // when walking up).  0.746 -> 0.728 ms on the causal D128 workload.
     int cm = 0, cit = 0;
     auto qtile = [&](const char* cs, char* ns) {
       // The item has landed for every wave; every wave is done with the last.
@@ -243,9 +247,9 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
       const bool wrap = cit + 1 == nq;
       const int nm = wrap ? cm + 1 : cm;
       cit = wrap ? 0 : cit + 1;
-      if (nm < G) issue_qtile(nm, i0 + cit, ns);
+      if (nm < G) issue_qtile(nm, n_qtiles - 1 - cit, ns);
       cm = nm;
-      const int qb0 = (i0 + it) * C::BQ;  // first query of the tile
+      const int qb0 = (n_qtiles - 1 - it) * C::BQ;  // first query of the tile
       // Causal: a tile whose last query precedes the wave's first key is empty.
       if (CAUSAL && qb0 + 31 < kw0) return;
       const char* qt = cs;
