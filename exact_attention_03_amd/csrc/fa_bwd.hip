@@ -256,17 +256,19 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
       const char* dot = qt + C::QT_BYTES;
       const float* stats = reinterpret_cast<const float*>(qt + C::STAT_OFF);
       f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int t = 0; t < C::KSTEPS; ++t) {
-        const int off = qrd.at(t);
-        s = mfma32<T>(lds_read16(qt, off), kf[t], s);
-        u32x4 vb;
-        if constexpr (C::V_LDS)
-          vb = lds_read16(vbase, vrd.at(t));
-        else
-          vb = vf[t];
-        dp = mfma32<T>(lds_read16(dot, off), vb, dp);
-      }
+      read_ahead<C::KSTEPS>(
+          [&](int t) {
+            u32x4 vb;
+            if constexpr (C::V_LDS)
+              vb = lds_read16(vbase, vrd.at(t));
+            else
+              vb = vf[t];
+            return U4x3{lds_read16(qt, qrd.at(t)), lds_read16(dot, qrd.at(t)), vb};
+          },
+          [&](int t, const U4x3& x) {
+            s = mfma32<T>(x.a, kf[t], s);
+            dp = mfma32<T>(x.b, x.c, dp);
+          });
       // Register jj holds query qb0 + 16(jj/8) + 8h + jj%8 for key kw0 + l32.
       // Each half (t2) of the registers is finished and fed to the dV / dK
       // products before the next, which keeps fewer values live.
@@ -304,11 +306,15 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
         }
         const u32x4 pf = pack8<T>(s, 8 * t2);
         const u32x4 dsf = pack8<T>(dp, 8 * t2);
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          dva[db] = mfma32<T>(lds_read_tr_operand<C::BQ>(dot, trd, 16 * t2, db), pf, dva[db]);
-          dka[db] = mfma32<T>(lds_read_tr_operand<C::BQ>(qt, trd, 16 * t2, db), dsf, dka[db]);
-        }
+        read_ahead<C::DB>(
+            [&](int db) {
+              return U4x2{lds_read_tr_operand<C::BQ>(dot, trd, 16 * t2, db),
+                          lds_read_tr_operand<C::BQ>(qt, trd, 16 * t2, db)};
+            },
+            [&](int db, const U4x2& x) {
+              dva[db] = mfma32<T>(x.a, pf, dva[db]);
+              dka[db] = mfma32<T>(x.b, dsf, dka[db]);
+            });
       }
     };
     if constexpr (C::PAIRS) {
