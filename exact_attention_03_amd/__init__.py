@@ -217,7 +217,9 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen=None, causal=False, scale=Non
     q: (H, T, D); k, v: (Hkv, T, D) (H a multiple of Hkv); sequence b is
     tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of every head and attends only
     within itself.  max_seqlen: at least the longest sequence (read from
-    cu_seqlens when omitted).  Returns O (H, T, D) and lse (H, T).
+    cu_seqlens when omitted; a smaller value leaves some tiles of the longer
+    sequences uncomputed, with unspecified results).  Returns O (H, T, D) and
+    lse (H, T).
     """
     torch = _torch()
     B, H, Hkv, T, D, mx = _check_varlen(q, k, v, cu_seqlens, max_seqlen)

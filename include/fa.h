@@ -268,9 +268,13 @@ int fa_bwd_dkdv_gqa(int64_t Z, int64_t H, int64_t Hkv, int64_t N, int64_t D, int
  *                    cu_seqlens[b] .. cu_seqlens[b+1]-1 of every head
  *                    (0 = cu_seqlens[0] <= ... <= cu_seqlens[B] = T; empty
  *                    sequences allowed); read by the kernels, never written;
- *   max_seqlen     : at least the longest sequence (it sizes the grids; the
- *                    tiles of a longer sequence past max_seqlen are not
- *                    computed and their outputs are left unwritten);
+ *   max_seqlen     : at least the longest sequence: it sizes the grids.
+ *                    With a smaller value some tiles of a longer sequence
+ *                    get no workgroup (not only its last ones: with the
+ *                    causal mask query tiles are dealt in pairs from both
+ *                    ends, so interior tiles are the ones left out); their
+ *                    outputs are left unwritten and the results of such a
+ *                    call are unspecified;
  *   workspace      : fa_bwd_workspace_bytes(1, H, T, D) bytes (stats are
  *                    (2, H, T) for the stage forms).
  * Each sequence is its own attention problem (causal within itself when
