@@ -603,14 +603,24 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
           s[kb] = f32x16{};
           dp[kb] = f32x16{};
         }
+        read_ahead<C::KSTEPS * C::KB>(
+            [&](int n) {
+              const int off = krd.at(n / C::KB) + kRowBlockBytes * (n % C::KB);
+              return U4x2{lds_read16(kt, off), lds_read16(vt, off)};
+            },
+            [&](int n, const U4x2& x) {
+              const int t = n / C::KB, kb = n % C::KB;
+              s[kb] = mfma32<T>(x.a, qf[t], s[kb]);
+              dp[kb] = mfma32<T>(x.b, dof[t], dp[kb]);
+            });
+        // Keep that order: the reads of step n + 1, then the products of step n.
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-        for (int t = 0; t < C::KSTEPS; ++t)
-#pragma unroll
-          for (int kb = 0; kb < C::KB; ++kb) {
-            const int off = krd.at(t) + kRowBlockBytes * kb;
-            s[kb] = mfma32<T>(lds_read16(kt, off), qf[t], s[kb]);
-            dp[kb] = mfma32<T>(lds_read16(vt, off), dof[t], dp[kb]);
-          }
+        for (int n = 0; n + 1 < C::KSTEPS * C::KB; ++n) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
       // This item's rows are not needed any more: load the next item's.
       const float l2c = l2, dlc = dl;
