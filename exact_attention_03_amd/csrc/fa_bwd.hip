@@ -23,6 +23,30 @@
 
 namespace fa {
 
+// Straight-line sequence of N steps whose operands come from LDS:
+// read(n) returns step n's operands and use(n, ops) issues its products.  The
+// reads of step n + 1 are issued before the products of step n, so that one
+// step's LDS latency overlaps the previous step's matrix instructions (without
+// this the compiler, short of registers, waits for each read right before its
+// product).  Costs one extra set of operand registers.
+struct U4x2 {
+  u32x4 a, b;
+};
+struct U4x3 {
+  u32x4 a, b, c;
+};
+template <int N, typename Read, typename Use>
+FA_DEV void read_ahead(Read read, Use use) {
+  auto cur = read(0);
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    auto nxt = cur;
+    if (n + 1 < N) nxt = read(n + 1);
+    use(n, cur);
+    cur = nxt;
+  }
+}
+
 // ============================================================ Delta pass
 // delta[row] = sum_d O[row, d] * dO[row, d] in fp32, and lse2[row] =
 // lse[row] * log2(e), the row statistic in the exp2 units the gradient passes

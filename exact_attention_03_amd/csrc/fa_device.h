@@ -339,30 +339,6 @@ FA_DEV u32x4 lds_read_tr16(const char* tile, const TrRead16<R>& t, int k0, int c
   return u32x4{lo.x, lo.y, hi.x, hi.y};
 }
 
-// Straight-line sequence of N steps whose operands come from LDS:
-// read(n) returns step n's operands and use(n, ops) issues its products.  The
-// reads of step n + 1 are issued before the products of step n, so that one
-// step's LDS latency overlaps the previous step's matrix instructions (without
-// this the compiler, short of registers, waits for each read right before its
-// product).  Costs one extra set of operand registers.
-struct U4x2 {
-  u32x4 a, b;
-};
-struct U4x3 {
-  u32x4 a, b, c;
-};
-template <int N, typename Read, typename Use>
-FA_DEV void read_ahead(Read read, Use use) {
-  auto cur = read(0);
-#pragma unroll
-  for (int n = 0; n < N; ++n) {
-    auto nxt = cur;
-    if (n + 1 < N) nxt = read(n + 1);
-    use(n, cur);
-    cur = nxt;
-  }
-}
-
 FA_DEV void gstore8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
 }
