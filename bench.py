@@ -775,7 +775,7 @@ def run_quest(args):
         if st != 0:
             raise fa.FAError(st, name, fa.last_error())
 
-    if args.calib_copy_mib > 0 and not side:
+    if args.calib_copy_mib > 0:
         # A plain device copy of known size, for scaling HBM counters.
         n = args.calib_copy_mib * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -905,7 +905,7 @@ def run_decode(args):
         if st != 0:
             raise fa.FAError(st, name, fa.last_error())
 
-    if args.calib_copy_mib > 0 and not side:
+    if args.calib_copy_mib > 0:
         # A plain device copy of known size, for scaling HBM counters.
         n = args.calib_copy_mib * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)

@@ -1,5 +1,7 @@
 """Host checks of bench.py's bookkeeping: the executed-work ratios and the
-decode byte models (no GPU)."""
+decode byte models, and a static check of its names (no GPU)."""
+import os
+
 import numpy as np
 
 import bench
@@ -50,3 +52,43 @@ def test_source_hash_ignores_comments_only():
     b = "// a new header line\nint f(int x) {\n  return 2 * x;\n}\n"
     c = "int f(int x) {\n  return 3 * x;\n}\n"
     assert bench._code_only(a) == bench._code_only(b) != bench._code_only(c)
+
+
+def test_bench_functions_use_only_defined_names():
+    """Every name a top-level function of bench.py reads is bound in that
+    function (or a function nested in it), at module level or in builtins:
+    a static guard for the paths only a GPU run executes."""
+    import ast
+    import builtins
+
+    src = open(bench.__file__, encoding="utf-8").read()
+    tree = ast.parse(src)
+    module_names = set(dir(builtins))
+    for node in tree.body:
+        if isinstance(node, (ast.FunctionDef, ast.ClassDef)):
+            module_names.add(node.name)
+        elif isinstance(node, (ast.Import, ast.ImportFrom)):
+            module_names.update((a.asname or a.name).split(".")[0] for a in node.names)
+        elif isinstance(node, (ast.Assign, ast.AnnAssign, ast.AugAssign)):
+            for t in (node.targets if isinstance(node, ast.Assign) else [node.target]):
+                module_names.update(n.id for n in ast.walk(t) if isinstance(n, ast.Name))
+    missing = {}
+    for fn in (n for n in tree.body if isinstance(n, ast.FunctionDef)):
+        bound, loads = set(), set()
+        for n in ast.walk(fn):
+            if isinstance(n, (ast.FunctionDef, ast.Lambda)):
+                a = n.args
+                bound.update(x.arg for x in a.args + a.kwonlyargs + a.posonlyargs)
+                bound.update(x.arg for x in (a.vararg, a.kwarg) if x is not None)
+                if isinstance(n, ast.FunctionDef):
+                    bound.add(n.name)
+            elif isinstance(n, ast.Name):
+                (bound if isinstance(n.ctx, (ast.Store, ast.Del)) else loads).add(n.id)
+            elif isinstance(n, (ast.Import, ast.ImportFrom)):
+                bound.update((a.asname or a.name).split(".")[0] for a in n.names)
+            elif isinstance(n, ast.ExceptHandler) and n.name:
+                bound.add(n.name)
+        undefined = loads - bound - module_names
+        if undefined:
+            missing[fn.name] = sorted(undefined)
+    assert not missing, missing
