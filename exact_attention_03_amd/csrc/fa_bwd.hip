@@ -134,7 +134,10 @@ struct DkdvTile {
   // registers the accumulators need.
   static constexpr int COPY_UNROLL = D == 256 ? 1 : 16;
   static_assert(BK == NW * 32, "one 32-key block per wave");
-  static constexpr int OCC = D == 256 ? 1 : 2;    // waves per SIMD the registers are sized for
+  // Waves per SIMD the registers are sized for.  At D = 64 (dK, dV, K and V
+  // rows of a wave in 168 registers) three fit: 0.708 -> 0.643 ms on the
+  // 128 x 8 x 1024 x 64 workload against two.
+  static constexpr int OCC = D == 256 ? 1 : (D == 64 ? 3 : 2);
   // Query tiles handled in pairs with compile-time ring stages (see the LDS
   // declarations).  At D = 256 the doubled loop body costs more registers
   // than the stage-aliasing waits it removes.
