@@ -640,7 +640,9 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
               s[kb] = mfma32<T>(x.a, qf[t], s[kb]);
               dp[kb] = mfma32<T>(x.b, dof[t], dp[kb]);
             });
-        // Keep that order: the reads of step n + 1, then the products of step n.
+        // Keep that order: the reads of step n + 1, then the products of step n
+        // (scheduling groups in sequence: mask 0x100 = LDS reads, 0x008 =
+        // matrix instructions, two of each per step).
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
         for (int n = 0; n + 1 < C::KSTEPS * C::KB; ++n) {
