@@ -160,17 +160,18 @@ def test_workload_parity(name):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{name}: {n} not deterministic"
 
 
-def test_dkdv_bitwise_independent_of_grid_size():
+@pytest.mark.parametrize("Z,H,N,D,dtype", [(2, 4, 1000, 128, "f16"), (1, 4, 600, 256, "bf16")])
+def test_dkdv_bitwise_independent_of_grid_size(Z, H, N, D, dtype):
     """No atomics and a fixed accumulation order: any persistent grid size gives the same bits."""
     import torch
 
     fa = _fa()
-    w = workloads.Workload("grid", 77, 2, 4, 1000, 128, "f16", True)
+    w = workloads.Workload("grid", 77, Z, H, N, D, dtype, True)
     cpu, gpu = device_inputs(w)
     q, k, v, do = gpu
     o, lse = fa.forward(q, k, v, causal=True, scale=w.scale)
     stats = fa.bwd_preprocess(o, do, lse)
-    cus, default = fa.device_info(128, fa.FA_DTYPE_F16)
+    cus, default = fa.device_info(D, fa.FA_DTYPE_BF16 if dtype == "bf16" else fa.FA_DTYPE_F16)
     log(f"device: {cus} CUs, default dK/dV grid {default}")
     ref = fa.bwd_dkdv(q, k, v, do, stats, causal=True, scale=w.scale, num_programs=0)
     for P in (1, 7, cus, 3 * cus + 1):
