@@ -359,7 +359,11 @@ void fa_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restri
     const auto rdv = make_rsrc(dv + kvoff, head_bytes);
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
-      const f32x16 ks = dka[db] * scale;
+      // Element by element: the vector-times-scalar form kept a register per
+      // element for the (uniform) scale.
+      f32x16 ks;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ks[i] = dka[db][i] * scale;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const uint32_t off = (uint32_t)((key * D + 32 * db + 16 * half + 8 * h) * 2);
@@ -700,7 +704,9 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
-      const f32x16 y = dqa[db] * scale;
+      f32x16 y;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) y[i] = dqa[db][i] * scale;
 #pragma unroll
       for (int half = 0; half < 2; ++half)
         gstore16(rdq, (uint32_t)((query * D + 32 * db + 16 * half + 8 * h) * 2), pack8<T>(y, 8 * half));
