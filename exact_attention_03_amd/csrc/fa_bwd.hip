@@ -400,6 +400,11 @@ struct DqTile {
   static constexpr int DMA = TILE_BYTES / (NW * 1024);
   static_assert(DMA * NW * 1024 == TILE_BYTES, "tile must split into 1 KiB copies per wave");
   static constexpr int OCC = D == 256 ? 1 : (D == 128 ? 2 : 3);  // waves per SIMD (registers)
+  // The causal kernel at D = 64 needs 176-188 registers (masks, the second
+  // tile of each pair): at three waves per SIMD (168) it spilled in the key
+  // tile loop; two measured faster (dQ 0.357 -> 0.352 ms on the causal
+  // 128 x 8 x 1024 x 64 workload).
+  static constexpr int occ(bool causal) { return (D == 64 && causal) ? 2 : OCC; }
   // Key tiles in pairs with compile-time ring stages (as in the dK/dV pass).
   static constexpr bool PAIRS = D <= 128;
 };
@@ -411,7 +416,8 @@ struct DqTile {
 enum DqStats { kStatsIn = 0, kStatsO16 = 1, kStatsO32 = 2 };
 
 template <int D, typename T, bool CAUSAL, int STATS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DqTile<D>::OCC, DqTile<D>::OCC)))
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(DqTile<D>::occ(CAUSAL), DqTile<D>::occ(CAUSAL))))
 void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                       const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                       const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dq,
