@@ -206,13 +206,17 @@ void fa_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
       // ---- masks: causal diagonal tile and ragged last tile only
       const bool need_mask = (CAUSAL && kv0 + C::BN - 1 > wq0) || (kv0 + C::BN > N);
       if (need_mask) {
-        const int query = wq0 + l32;
+        // Key kv0 + 8h + c (c = 32kb + 16(jj/8) + jj%8, a constant per
+        // register) is dropped when it lies past the query (causal) or past
+        // the sequence, i.e. when c exceeds one per-lane limit.
+        const int last = CAUSAL ? min(wq0 + l32, N - 1) : N - 1;  // last key kept
+        const int lim = last - kv0 - 8 * h;
 #pragma unroll
         for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
           for (int jj = 0; jj < 16; ++jj) {
-            const int key = kv0 + 32 * kb + 16 * (jj >> 3) + 8 * h + (jj & 7);
-            s[kb][jj] = ((CAUSAL && key > query) || key >= N) ? -INFINITY : s[kb][jj];
+            const int c = 32 * kb + 16 * (jj >> 3) + (jj & 7);
+            s[kb][jj] = c > lim ? -INFINITY : s[kb][jj];
           }
       }
       // ---- online softmax, exp2 units
