@@ -411,6 +411,12 @@ struct DqTile {
   // tile loop; two measured faster (dQ 0.357 -> 0.352 ms on the causal
   // 128 x 8 x 1024 x 64 workload).
   static constexpr int occ(bool causal) { return (D == 64 && causal) ? 2 : OCC; }
+  // Causal: a wave whose queries all precede a key tile skips it, except at
+  // D = 256, where the masked products run instead (P = 0, dQ unchanged):
+  // the branch cost 50 registers there and the causal pass 1.49 -> 1.31 ms
+  // on a 128 x 8 x 1024 x 256 bf16 problem without it; at D = 64 and 128 the
+  // skip measured faster.
+  static constexpr bool SKIP_IDLE = D <= 128;
   // Key tiles in pairs with compile-time ring stages (as in the dK/dV pass).
   static constexpr bool PAIRS = D <= 128;
 };
@@ -638,7 +644,7 @@ void fa_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
         if (j == 1 && more) issue_o(qt_b);
       }
       const int kv0 = j * C::BN;
-      const bool active = !CAUSAL || kv0 <= wq0 + 31;
+      const bool active = !CAUSAL || !C::SKIP_IDLE || kv0 <= wq0 + 31;
       f32x16 s[C::KB], dp[C::KB];
       if (active) {
 #pragma unroll
