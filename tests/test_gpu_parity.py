@@ -73,6 +73,11 @@ SMALL = [
     ((1, 1, n, 64), "bf16", True) for n in (2, 200)
 ] + [
     ((1, 1, n, 256), "f16", causal) for n in (33, 160) for causal in (False, True)
+] + [
+    # D = 256 with the mask over eight key tiles: every dK/dV unit and dQ item
+    # crosses the diagonal, where at this width the waves run their wholly
+    # masked tiles instead of skipping them.
+    ((2, 4, 1024, 256), "bf16", True),
 ]
 
 
