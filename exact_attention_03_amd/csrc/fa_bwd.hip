@@ -144,9 +144,10 @@ struct DkdvTile {
   static constexpr bool PAIRS = D <= 128;
   // Causal: a wave whose keys all follow a query tile skips it.  At D = 256
   // the branch around the tile's products made the compiler keep the K rows
-  // in scratch and reload them for every query tile (4.04 ms for the causal
-  // pass against 2.66 ms without the mask); there the wave runs the products
-  // on its masked tile instead (P = 0, so dS = 0 and dK, dV do not change).
+  // in scratch and reload them for every query tile: the causal pass of a
+  // 128 x 8 x 1024 x 256 bf16 problem took 4.04 ms, more than the non-causal
+  // one (2.66 ms).  There the wave runs the products on its masked tile
+  // instead (P = 0, so dS = 0 and dK, dV do not change): 1.66 ms.
   // At D = 64 and 128 the skip measured faster (0.695 against 0.726 ms on
   // the causal D = 128 workload).
   static constexpr bool SKIP_IDLE = D <= 128;
