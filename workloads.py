@@ -98,13 +98,14 @@ def f32_scale(D: int) -> float:
 
 # The five workloads: a tiny parity case, three Z=128 x H=8 x N=1024 cases at
 # head dims 64/128/256, and a long-sequence causal case with a peaked softmax;
-# then a grouped key/value head case: Z=4, 32 query heads over 8 key/value
+# then the D = 256 case with the causal mask, a grouped key/value head case: Z=4, 32 query heads over 8 key/value
 # heads (4 query heads per key/value head), N=4096, D=128, causal.
 WORKLOADS = {
     "tiny": Workload("tiny", 1, 1, 1, 128, 64, "f16", False),
     "d64": Workload("d64", 2, 128, 8, 1024, 64, "f16", False),
     "d128_causal": Workload("d128_causal", 3, 128, 8, 1024, 128, "f16", True),
     "d256_bf16": Workload("d256_bf16", 4, 128, 8, 1024, 256, "bf16", False),
+    "d256_causal_bf16": Workload("d256_causal_bf16", 8, 128, 8, 1024, 256, "bf16", True),
     "long_causal_bf16": Workload("long_causal_bf16", 5, 16, 16, 8192, 128, "bf16", True, 2.0),
     "gqa_causal_bf16": Workload("gqa_causal_bf16", 6, 4, 32, 4096, 128, "bf16", True, 1.0, 8),
 }
